@@ -1,0 +1,217 @@
+/*
+ * bgg.h -- C ABI of libbgg.so: the linear-layer product y = W.x of a ternary
+ * LLM whose weights are trits {-1, 0, +1} with one fp16 scale per 128 weights
+ * along K, stored in block-Hadamard-rotated coordinates, in one of two
+ * packings.  Built for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by address, title and paragraph or section):
+ *   [A] allhereai.com/news/1346, "27B 模型压到 5.95GB，推理能力还保住 98%":
+ *       method paragraph (trits, one FP16 scale shared by every 128 weights,
+ *       block Hadamard rotation folded into storage); runtime paragraph (the
+ *       runtime must apply the Hadamard transform to the activations; the
+ *       wrong runtime can load the file and print garbage); packing
+ *       paragraph (PTQ1_0 compact trits, PQ2_0 one trit per 2-bit slot, and
+ *       which decodes faster where).
+ *   [B] 10100.com/article/156675786, "Bonsai 2，把27B压进6个G", section
+ *       "它怎么做到的": rotation before ternary rounding; the input needs the
+ *       matching transform at inference, and skipping it fails silently.
+ *   [C] wmrh.cn/news/471187, section "关键机制": five trits per byte, about
+ *       1.6 bits per trit; FP16 group-wise scales.
+ *
+ * What the library computes (readings of the pages, fixed here):
+ *   x'[m] = blockdiag(H_128 / sqrt(128)) x[m]   (Sylvester order, no signs)
+ *   y[m][n] = sum_k S[n][k/128] * T[n][k] * x'[m][k]
+ * with x and y fp16, x' computed in fp32, sums in fp32.
+ *
+ * Conventions for every call
+ *   - The caller owns every buffer.  Pointers named *_dev are device
+ *     pointers (hipMalloc or a framework's device allocator); the others are
+ *     host pointers.  The library keeps no pointer after a call returns and
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls
+ *     only enqueue work and never synchronise; argument errors are reported
+ *     before anything is enqueued.  A failed launch returns BGG_ERR_HIP.
+ *   - Nothing aborts or prints.  Every call returns a bgg_status; a
+ *     thread-local message with details is kept for bgg_last_error().
+ *   - Device pointers must be 16-byte aligned (fp16 activation rows: K is a
+ *     multiple of 128, so every row is aligned when the base is).
+ *   - Calls are re-entrant; calls that share a workspace must not overlap.
+ */
+#ifndef BGG_H
+#define BGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Packings of the trits [A packing paragraph; C].  The two tags are checked
+ * on every call, so a buffer packed one way cannot be run the other way (the
+ * silent-garbage hazard of [A runtime paragraph]). */
+typedef enum {
+  BGG_FMT_PQ2_0 = 1,  /* one trit per 2-bit slot: code t+1 in {0,1,2}; 2.125 bits/weight */
+  BGG_FMT_PTQ1_0 = 2  /* five trits per byte, base 3 of t+1; 8/5 + 16/128 = 1.725 bits/weight */
+} bgg_format;
+
+typedef enum {
+  BGG_OK = 0,
+  BGG_ERR_NULL = 1,        /* a required pointer is NULL */
+  BGG_ERR_FORMAT = 2,      /* unknown format tag */
+  BGG_ERR_SHAPE = 3,       /* K not a positive multiple of 128, N < 1, M out of range */
+  BGG_ERR_TRIT = 4,        /* a trit outside {-1, 0, 1} */
+  BGG_ERR_PACKED_BYTE = 5, /* a PQ2_0 code of 3 or a PTQ1_0 byte >= 243 */
+  BGG_ERR_BUFFER = 6,      /* buffer too small or misaligned */
+  BGG_ERR_DESC = 7,        /* descriptor not made by bgg_describe, or it disagrees with the call */
+  BGG_ERR_HIP = 8,         /* the HIP runtime reported an error */
+  BGG_ERR_SCALE = 9        /* a scale that is not a finite fp16 */
+} bgg_status;
+
+/* Flags of bgg_ternary_gemv / bgg_ternary_gemm. */
+enum {
+  /* x is in model coordinates: the call applies the normalised block-128
+   * transform first [A runtime paragraph; B].  Without it x must already be
+   * x' (so projections that share an input can share one transform). */
+  BGG_ROTATE_INPUT = 1u
+};
+
+#define BGG_GROUP 128     /* weights per scale = Hadamard block, along K [A method paragraph] */
+#define BGG_ROW_TILE 64   /* rows per tile of the device layout (one row per lane) */
+#define BGG_CHUNK 16      /* bytes of one row that one lane loads at once */
+#define BGG_MAX_GEMV_M 16 /* largest token count of bgg_ternary_gemv */
+
+#define BGG_DESC_MAGIC 0x57474742u /* "BGGW" */
+#define BGG_DESC_VERSION 1u
+
+/*
+ * Descriptor of a packed weight matrix W [N out][K in].  Host struct, filled
+ * by bgg_describe, owned and passed back by the caller on every call.
+ *
+ * Device layout of the packed buffer (total_bytes):
+ *   trit region, at offset 0: rows in tiles of 64; the bytes of each row in
+ *     the format's canonical row stream (PQ2_0: row byte j holds trits
+ *     4j..4j+3, trit 4j+i in bits 2i..2i+1 as t+1; PTQ1_0: row byte j =
+ *     sum_i (t_{5j+i}+1) 3^i, trits past K are 0), cut into 16-byte chunks.
+ *     Chunk c of row 64*t + l sits at byte ((t*chunks + c)*64 + l)*16, so the
+ *     64 rows of a tile read chunk c with one coalesced 1 KiB load.  Rows
+ *     past N hold zero trits, bytes past the row stream hold zero trits.
+ *   scale region, at scale_offset: fp16 scale of row 64*t + l, group g at
+ *     byte scale_offset + ((t*groups + g)*64 + l)*2; rows past N hold 0.
+ */
+typedef struct bgg_weights_desc {
+  uint32_t magic;        /* BGG_DESC_MAGIC */
+  uint32_t version;      /* BGG_DESC_VERSION */
+  int32_t format;        /* bgg_format */
+  int32_t row_tile;      /* BGG_ROW_TILE */
+  int64_t N;             /* output rows */
+  int64_t K;             /* input columns, a multiple of 128 */
+  int64_t groups;        /* K / 128 */
+  int64_t row_tiles;     /* ceil(N / 64) */
+  int64_t row_bytes;     /* canonical packed bytes per row: ceil(K/4) or ceil(K/5) */
+  int64_t chunks;        /* ceil(row_bytes / 16) */
+  uint64_t trit_bytes;   /* row_tiles * chunks * 1024 */
+  uint64_t scale_offset; /* trit_bytes rounded up to 256 */
+  uint64_t scale_bytes;  /* row_tiles * groups * 128 */
+  uint64_t total_bytes;  /* scale_offset + scale_bytes */
+  uint64_t format_bytes; /* N*row_bytes + N*groups*2: the format's own size, no padding */
+} bgg_weights_desc;
+
+/* Fill *out for a format and shape.  Host only, no side effects.
+ * Errors: BGG_ERR_NULL, BGG_ERR_FORMAT, BGG_ERR_SHAPE. */
+bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* out);
+
+/* Pack trits and scales into the device layout (a0 of the path: offline,
+ * once per matrix) [A method and packing paragraphs; C].
+ *   trits   host int8 [N][K], row-major, values in {-1,0,1} (rotated coordinates)
+ *   scales  host fp16 bits [N][K/128], row-major
+ *   packed  host buffer of desc->total_bytes; every byte is written
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_TRIT, BGG_ERR_SCALE (nothing
+ * useful is left in packed after an error). */
+bgg_status bgg_pack_weights(const bgg_weights_desc* desc, const int8_t* trits,
+                            const uint16_t* scales, void* packed);
+
+/* Lay out canonical row-stream bytes (the format's file form) in the device
+ * layout without decoding them.
+ *   canonical  host uint8 [N][desc->row_bytes]
+ *   scales     host fp16 bits [N][K/128]
+ *   packed     host buffer of desc->total_bytes
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_PACKED_BYTE, BGG_ERR_SCALE. */
+bgg_status bgg_repack_canonical(const bgg_weights_desc* desc, const uint8_t* canonical,
+                                const uint16_t* scales, void* packed);
+
+/* Check a host copy of a packed buffer: every code valid, padding as laid
+ * out, every scale a finite fp16.  Errors: BGG_ERR_NULL, BGG_ERR_DESC,
+ * BGG_ERR_PACKED_BYTE, BGG_ERR_SCALE. */
+bgg_status bgg_validate_packed(const bgg_weights_desc* desc, const void* packed);
+
+/* Decode a packed device buffer back to trits and scales with the same
+ * device decoders the products use (for checking; not on the hot path).
+ *   packed_dev  device, desc->total_bytes
+ *   trits_dev   device int8 [N][K]; scales_dev device fp16 bits [N][K/128]
+ * Invalid codes decode as t = 0.  Errors: BGG_ERR_NULL, BGG_ERR_DESC,
+ * BGG_ERR_BUFFER, BGG_ERR_HIP. */
+bgg_status bgg_unpack_weights(const bgg_weights_desc* desc, const void* packed_dev,
+                              int8_t* trits_dev, uint16_t* scales_dev, void* stream);
+
+/* x' = blockdiag(H_128/sqrt(128)) x for each of M rows of K fp16 values
+ * [A runtime paragraph; B]: the butterflies run in fp32 and x' is rounded to
+ * fp16 (nearest even) once.  x_dev and xr_dev are device fp16 [M][K]; they
+ * may be the same buffer.  Errors: BGG_ERR_NULL, BGG_ERR_SHAPE (K % 128 or
+ * M < 0), BGG_ERR_BUFFER (alignment), BGG_ERR_HIP.  M == 0 is a no-op. */
+bgg_status bgg_hadamard_rotate(const void* x_dev, void* xr_dev, int64_t M, int64_t K,
+                               void* stream);
+
+/* Device workspace bytes that bgg_ternary_gemv needs for M tokens (0 on a
+ * bad descriptor or M outside 1..16). */
+size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
+
+/*
+ * Decode-time product, 1 <= M <= 16 tokens [A packing paragraph: decode].
+ *   packed_dev  device buffer made from bgg_pack_weights output
+ *   x_dev       device fp16 [M][K] (model coordinates with BGG_ROTATE_INPUT,
+ *               else already rotated)
+ *   y_dev       device fp16 [M][N]
+ *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
+ *               bytes; its contents need no initialisation and are scratch.
+ * Each 64-row tile is read once per call, all M tokens at a time.  The
+ * activations are carried as 15-bit integers with a power-of-two scale per
+ * 128-block (absolute error at most 2^-14 of the block's largest |x'|), the
+ * trit products are exact integer sums, and each group's sum is scaled and
+ * accumulated in fp32; y is rounded to fp16 once.
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER,
+ * BGG_ERR_HIP.
+ */
+bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev,
+                            const void* x_dev, void* y_dev, int64_t M, uint32_t flags,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace bytes that bgg_ternary_gemm needs for M tokens. */
+size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
+
+/*
+ * Prompt-time product for any M >= 1 (PQ2_0 only) [A packing paragraph:
+ * prompt processing].  Trit tiles are decoded to fp16 s*t (exact) in LDS and
+ * multiplied with fp16 x' on the matrix cores, fp32 accumulation, fp16 y.
+ *   workspace  device, bgg_gemm_workspace_size(desc, M) bytes (holds x' when
+ *              BGG_ROTATE_INPUT is set; may be NULL when it is not).
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (PTQ1_0), BGG_ERR_SHAPE,
+ * BGG_ERR_BUFFER, BGG_ERR_HIP.
+ */
+bgg_status bgg_ternary_gemm(const bgg_weights_desc* desc, const void* packed_dev,
+                            const void* x_dev, void* y_dev, int64_t M, uint32_t flags,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English name of a status. */
+const char* bgg_status_string(int32_t status);
+
+/* Details of the last error raised on the calling thread ("" if none). */
+const char* bgg_last_error(void);
+
+/* BGG_DESC_VERSION of the loaded library. */
+uint32_t bgg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BGG_H */

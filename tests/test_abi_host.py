@@ -1,0 +1,191 @@
+"""Host-side tests of libbgg.so: exported symbols, descriptors, packing into
+the device layout, validation and error codes.  No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_gemv_gemm_amd as bgg
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bgg.h")
+FMTS = ("PQ2_0", "PTQ1_0")
+RNG = np.random.default_rng(99)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bgg_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(bgg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bgg.h but not exported"
+    assert set(names) == set(bgg.EXPORTED), "binding and header disagree"
+
+
+def test_abi_version_and_status_strings():
+    assert bgg.bgg_abi_version() == 1
+    for s in range(10):
+        assert bgg.bgg_status_string(s)
+    assert bgg.bgg_status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(1, 128), (64, 512), (100, 640), (256, 5120), (5120, 17408), (17408, 5120)])
+def test_describe_sizes(fmt, N, K):
+    d = bgg.bgg_describe(fmt, N, K)
+    assert d.groups == K // 128
+    assert d.row_bytes == oracle.row_bytes(fmt, K)
+    assert d.format_bytes == oracle.format_bytes(fmt, N, K)
+    assert d.row_tiles == -(-N // 64)
+    assert d.chunks == -(-d.row_bytes // 16)
+    assert d.trit_bytes == d.row_tiles * d.chunks * 1024
+    assert d.scale_offset % 256 == 0 and d.scale_offset >= d.trit_bytes
+    assert d.total_bytes == d.scale_offset + d.row_tiles * d.groups * 128
+
+
+def test_describe_rejects_bad_shapes_and_formats():
+    for (f, N, K, st) in [(3, 64, 128, 2), (0, 64, 128, 2), (1, 0, 128, 3), (1, 64, 100, 3),
+                          (2, 64, 0, 3), (2, 64, 64, 3), (1, -5, 128, 3)]:
+        with pytest.raises(bgg.BggError) as e:
+            bgg.bgg_describe(f, N, K)
+        assert e.value.status == st
+
+
+def _canonical_from_layout(d, packed):
+    """Read row r's canonical byte stream back out of the tiled device layout
+    (the layout documented in bgg.h)."""
+    C, G = d.chunks, d.groups
+    tiles = packed[:d.trit_bytes].reshape(d.row_tiles, C, 64, 16)
+    rows = tiles.transpose(0, 2, 1, 3).reshape(d.row_tiles * 64, C * 16)
+    sc = packed[d.scale_offset:d.scale_offset + d.scale_bytes].view(np.uint16)
+    sc = sc.reshape(d.row_tiles, G, 64).transpose(0, 2, 1).reshape(d.row_tiles * 64, G)
+    return rows, sc
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(1, 128), (100, 640), (130, 1152), (64, 6144)])
+def test_pack_layout_matches_oracle_canonical_bytes(fmt, N, K):
+    T = synth.trits(5, 1, N, K)
+    S = synth.scales_f16(5, 1, N, K)
+    d = bgg.bgg_describe(fmt, N, K)
+    packed = bgg.bgg_pack_weights(d, T, S)
+    rows, sc = _canonical_from_layout(d, packed)
+    canon = oracle.pack(fmt, T)
+    assert np.array_equal(rows[:N, :d.row_bytes], canon)
+    zero = 0x55 if fmt == "PQ2_0" else 121
+    assert np.all(rows[:N, d.row_bytes:] == zero)       # zero trits past the row stream
+    assert np.all(rows[N:] == zero)                      # zero trits in padding rows
+    assert np.array_equal(sc[:N], S.view(np.uint16))
+    assert np.all(sc[N:] == 0)
+    bgg.bgg_validate_packed(d, packed)
+    # repacking the oracle's canonical bytes gives the same buffer
+    assert np.array_equal(bgg.bgg_repack_canonical(d, canon, S), packed)
+
+
+def test_pack_rejects_bad_trits_and_scales():
+    d = bgg.bgg_describe("PQ2_0", 4, 128)
+    T = np.zeros((4, 128), np.int8)
+    S = np.full((4, 1), 0.01, np.float16)
+    T[2, 7] = 2
+    with pytest.raises(bgg.BggError) as e:
+        bgg.bgg_pack_weights(d, T, S)
+    assert e.value.status == 4 and "row 2 col 7" in str(e.value)
+    T[2, 7] = -2
+    with pytest.raises(bgg.BggError):
+        bgg.bgg_pack_weights(d, T, S)
+    T[2, 7] = 0
+    for bad in (np.inf, -np.inf, np.nan):
+        S2 = S.copy()
+        S2[1, 0] = bad
+        with pytest.raises(bgg.BggError) as e:
+            bgg.bgg_pack_weights(d, T, S2)
+        assert e.value.status == 9
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_validate_catches_bad_bytes(fmt):
+    N, K = 70, 256
+    d = bgg.bgg_describe(fmt, N, K)
+    T = synth.trits(9, 2, N, K)
+    S = synth.scales_f16(9, 2, N, K)
+    p = bgg.bgg_pack_weights(d, T, S)
+    bgg.bgg_validate_packed(d, p)
+    bad = p.copy()
+    bad[17] = 0xFF                     # PQ2_0 code 3 / PTQ1_0 byte 255
+    with pytest.raises(bgg.BggError) as e:
+        bgg.bgg_validate_packed(d, bad)
+    assert e.value.status == 5
+    canon = oracle.pack(fmt, T)
+    canon[3, 2] = 0xC0 if fmt == "PQ2_0" else 250
+    with pytest.raises(bgg.BggError) as e:
+        bgg.bgg_repack_canonical(d, canon, S)
+    assert e.value.status == 5
+    # a padding row that holds a non-zero trit is rejected
+    rows_layout = p.copy()
+    t_last, l_last = (N // 64), (N % 64)   # first padding row
+    rows_layout[((t_last * d.chunks) * 64 + l_last) * 16] = 0 if fmt == "PQ2_0" else 0
+    with pytest.raises(bgg.BggError):
+        bgg.bgg_validate_packed(d, rows_layout)
+
+
+def test_descriptor_tampering_is_rejected():
+    d = bgg.bgg_describe("PQ2_0", 64, 256)
+    T = np.zeros((64, 256), np.int8)
+    S = np.zeros((64, 2), np.float16)
+    bgg.bgg_pack_weights(d, T, S)
+    for field, val in (("magic", 1), ("version", 2), ("format", 2), ("N", 65), ("total_bytes", 5)):
+        d2 = bgg.bgg_weights_desc.from_buffer_copy(d)
+        setattr(d2, field, val)
+        with pytest.raises(bgg.BggError) as e:
+            bgg.bgg_pack_weights(d2, np.zeros((d2.N, d2.K), np.int8), np.zeros((d2.N, d2.groups), np.float16))
+        assert e.value.status == 7
+    # a PQ2_0 descriptor relabelled PTQ1_0 is caught before any work
+    d3 = bgg.bgg_weights_desc.from_buffer_copy(d)
+    d3.format = 2
+    assert bgg.bgg_gemv_workspace_size(d3, 1) == 0
+
+
+def test_workspace_sizes():
+    d = bgg.bgg_describe("PQ2_0", 5120, 17408)
+    assert bgg.bgg_gemv_workspace_size(d, 1) > 0
+    assert bgg.bgg_gemv_workspace_size(d, 0) == 0
+    assert bgg.bgg_gemv_workspace_size(d, 17) == 0
+    assert bgg.bgg_gemv_workspace_size(d, 16) >= bgg.bgg_gemv_workspace_size(d, 4)
+    assert bgg.bgg_gemm_workspace_size(d, 4096) >= 4096 * 17408 * 2
+
+
+def test_null_pointers_are_errors_not_crashes():
+    lib = ctypes.CDLL(bgg.LIB_PATH)
+    lib.bgg_describe.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    assert lib.bgg_describe(1, 64, 128, None) == 1
+    d = bgg.bgg_describe("PQ2_0", 64, 128)
+    lib.bgg_pack_weights.argtypes = [ctypes.c_void_p] * 4
+    assert lib.bgg_pack_weights(ctypes.addressof(d), None, None, None) == 1
+    assert lib.bgg_pack_weights(None, None, None, None) == 1
+    lib.bgg_ternary_gemv.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_uint32,
+                                                             ctypes.c_void_p, ctypes.c_size_t,
+                                                             ctypes.c_void_p]
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), None, None, None, 1, 1, None, 0, None) == 1
+    lib.bgg_hadamard_rotate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    assert lib.bgg_hadamard_rotate(None, None, 1, 128, None) == 1
+    # shape errors are reported before any device work
+    assert lib.bgg_hadamard_rotate(16, 16, 1, 100, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 0, 1, 16, 1 << 20, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, 1 << 20, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 20, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
+    dp = bgg.bgg_describe("PTQ1_0", 64, 128)
+    lib.bgg_ternary_gemm.argtypes = lib.bgg_ternary_gemv.argtypes
+    assert lib.bgg_ternary_gemm(ctypes.addressof(dp), 16, 16, 16, 4, 0, None, 0, None) == 2

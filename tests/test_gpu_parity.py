@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on
+seeded synthetic inputs.  Marked gpu; run on an MI355X.
+
+Bars: unpacking bit-exact; the transform within one fp16 ulp of the rounded
+fp64 result; y within 2e-3 of the oracle, measured per token row as
+max_n |y - y_oracle| / max_n |y_oracle|.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from gpu_helpers import TOL, Dev, gen_matrix, oracle_y, relerr  # noqa: E402
+
+FMTS = ("PQ2_0", "PTQ1_0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need the GPU"
+    import bit_gemv_gemm_amd as bgg
+    return bgg, torch
+
+
+# ---------------------------------------------------------------------------
+# unpack: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(1, 128), (100, 640), (130, 1152), (256, 512), (64, 6144), (5120, 17408)])
+def test_unpack_bit_exact(env, fmt, N, K):
+    bgg, torch = env
+    say(f"unpack {fmt} N={N} K={K}")
+    T, S = gen_matrix(11, 3, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    td = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    sd = torch.empty((N, K // 128), dtype=torch.float16, device="cuda")
+    bgg.bgg_unpack_weights(d.desc, d.packed, td, sd)
+    torch.cuda.synchronize()
+    want = oracle.unpack(fmt, oracle.pack(fmt, T), K)
+    assert np.array_equal(td.cpu().numpy(), want)
+    assert np.array_equal(sd.cpu().numpy().view(np.uint16), S.view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unpack_exhaustive_codes(env, fmt):
+    """Every valid byte value appears: all 243 base-3 bytes / all 81 code
+    bytes, laid out by the oracle's canonical packer."""
+    bgg, torch = env
+    say(f"unpack exhaustive {fmt}")
+    width = 5 if fmt == "PTQ1_0" else 4
+    vals = np.array(np.meshgrid(*([[-1, 0, 1]] * width), indexing="ij")).reshape(width, -1).T
+    reps = -(-640 // (vals.shape[0] * width)) + 1
+    row = np.tile(vals.reshape(-1), reps)[:640].astype(np.int8)
+    T = np.stack([np.roll(row, 7 * i) for i in range(70)])
+    S = synth.scales_f16(1, 1, 70, 640)
+    d = Dev(bgg, torch, fmt, T, S)
+    td = torch.empty(T.shape, dtype=torch.int8, device="cuda")
+    sd = torch.empty(S.shape, dtype=torch.float16, device="cuda")
+    bgg.bgg_unpack_weights(d.desc, d.packed, td, sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(td.cpu().numpy(), T)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard transform
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 640), (17, 5120), (5, 17408), (300, 1024)])
+def test_hadamard_rotate_within_one_ulp(env, M, K):
+    bgg, torch = env
+    say(f"rotate M={M} K={K}")
+    x = synth.activations_f16(5, K, M, K)
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty_like(xd)
+    bgg.bgg_hadamard_rotate(xd, yd, M, K)
+    torch.cuda.synchronize()
+    got = yd.cpu().numpy()
+    want = oracle.rotate(x)
+    want16 = want.astype(np.float16)
+    # one fp16 ulp of the correctly rounded value
+    ulp = np.spacing(np.abs(want16)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - want16.astype(np.float64)) <= ulp)
+    assert np.mean(got == want16) > 0.95
+    # in place
+    bgg.bgg_hadamard_rotate(xd, xd, M, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(xd.cpu().numpy(), got)
+
+
+def test_hadamard_closed_forms(env):
+    bgg, torch = env
+    say("rotate closed forms")
+    K = 256
+    x = np.zeros((2, K), np.float16)
+    x[0, 0] = 1.0
+    x[1, 128:] = 1.0
+    xd = torch.from_numpy(x).cuda()
+    bgg.bgg_hadamard_rotate(xd, xd, 2, K)
+    torch.cuda.synchronize()
+    y = xd.cpu().numpy().astype(np.float64)
+    assert np.all(y[0, :128] == np.float16(1 / np.sqrt(128)))
+    assert np.all(y[0, 128:] == 0)
+    assert y[1, 128] == np.float16(np.sqrt(128)) and np.all(y[1, 129:] == 0) and np.all(y[1, :128] == 0)
+
+
+# ---------------------------------------------------------------------------
+# decode GEMV
+# ---------------------------------------------------------------------------
+GEMV_CASES = [
+    ("tiny", 256, 512, 1),
+    ("ragged", 100, 640, 1),
+    ("tail-periods", 130, 1152, 2),
+    ("one-group", 64, 128, 1),
+    ("one-row", 1, 384, 1),
+    ("q", 6144, 5120, 1),
+    ("o", 5120, 6144, 1),
+    ("kv", 1024, 5120, 3),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case,N,K,M", GEMV_CASES)
+def test_gemv_parity(env, fmt, case, N, K, M):
+    bgg, torch = env
+    say(f"gemv {fmt} {case} N={N} K={K} M={M}")
+    T, S = gen_matrix(21, 4, N, K)
+    x = synth.activations_f16(21, 100 + K, M, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    y = d.gemv(x)
+    assert not np.isnan(y).any()
+    ref = oracle_y(fmt, T, S, x)
+    e = relerr(y, ref)
+    say(f"  rel err {e}")
+    assert np.all(e <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16])
+def test_gemv_token_counts(env, fmt, M):
+    bgg, torch = env
+    N, K = 200, 1280
+    say(f"gemv {fmt} M={M} N={N} K={K}")
+    T, S = gen_matrix(31, 5, N, K)
+    x = synth.activations_f16(31, 7, M, K)
+    y = Dev(bgg, torch, fmt, T, S).gemv(x)
+    ref = oracle_y(fmt, T, S, x)
+    e = relerr(y, ref)
+    say(f"  rel err {e.max():.3g}")
+    assert np.all(e <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_gemv_projection_full_size(env, fmt, name):
+    """The single-projection workload at its full shape, every output checked."""
+    bgg, torch = env
+    w = synth.WORKLOADS["projection"]
+    mat = [m for m in w["matrices"] if m.name == name][0]
+    say(f"gemv full {fmt} {name} N={mat.n} K={mat.k}")
+    T, S = synth.workload_matrix(mat, w["seed"])
+    x = synth.workload_x(w["seed"], 1, mat.k)
+    y = Dev(bgg, torch, fmt, T, S).gemv(x)
+    ref = oracle_y(fmt, T, S, x)
+    e = relerr(y, ref)
+    say(f"  rel err {e}")
+    assert np.all(e <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_basis_vectors_bit_exact(env, fmt):
+    """Rotation off and x = e_k: y_n = S[n][k/128] * T[n][k] exactly."""
+    bgg, torch = env
+    N, K = 130, 768
+    say(f"gemv basis {fmt}")
+    T, S = gen_matrix(41, 6, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    ks = [0, 1, 127, 128, 129, 383, 640, 767]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    for i0 in range(0, len(ks), 4):
+        y = d.gemv(x[i0:i0 + 4], rotate=False)
+        for j, k in enumerate(ks[i0:i0 + 4]):
+            want = (S[:, k // 128].astype(np.float64) * T[:, k]).astype(np.float16)
+            assert np.array_equal(y[j].view(np.uint16), want.view(np.uint16)), f"k={k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_sylvester_rows(env, fmt):
+    """Trit row n = Sylvester row r of block b with scale s picks out
+    s * sqrt(128) * x[128 b + r] (closed form; no oracle involved)."""
+    import scipy.linalg
+    bgg, torch = env
+    say(f"gemv sylvester {fmt}")
+    K = 640
+    H = scipy.linalg.hadamard(128).astype(np.int8)
+    cases = [(b, r) for b in range(5) for r in (0, 1, 77, 127)]
+    T = np.zeros((len(cases), K), np.int8)
+    S = np.zeros((len(cases), K // 128), np.float16)
+    for n, (b, r) in enumerate(cases):
+        T[n, 128 * b:128 * b + 128] = H[r]
+        S[n, b] = np.float16(0.0078125 * (1 + n % 5))
+    x = synth.activations_f16(3, 3, 1, K)
+    y = Dev(bgg, torch, fmt, T, S).gemv(x)[0].astype(np.float64)
+    want = np.array([float(S[n, b]) * np.sqrt(128.0) * float(x[0, 128 * b + r]) for n, (b, r) in enumerate(cases)])
+    assert np.all(np.abs(y - want) <= 2e-3 * np.max(np.abs(want)))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_without_rotation_is_garbage(env, fmt):
+    """Skipping the activation transform must fail the tolerance by far (the
+    pages warn that the wrong runtime emits garbage silently)."""
+    bgg, torch = env
+    say(f"gemv no-rotation {fmt}")
+    N, K = 512, 2048
+    T, S = gen_matrix(51, 7, N, K)
+    x = synth.activations_f16(51, 8, 1, K)
+    y = Dev(bgg, torch, fmt, T, S).gemv(x, rotate=False)
+    ref = oracle_y(fmt, T, S, x)
+    assert relerr(y, ref).min() > 100 * TOL
+    # while the same call given x' does match
+    xr = oracle.rotate(x).astype(np.float16)
+    y2 = Dev(bgg, torch, fmt, T, S).gemv(xr, rotate=False)
+    assert np.all(relerr(y2, oracle_y(fmt, T, S, xr, rotate=False)) <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_zero_weights_and_repeat_calls(env, fmt):
+    bgg, torch = env
+    say(f"gemv zeros/repeat {fmt}")
+    N, K = 300, 5120
+    T = np.zeros((N, K), np.int8)
+    S = synth.scales_f16(1, 1, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    x = synth.activations_f16(1, 2, 2, K)
+    assert np.all(d.gemv(x) == 0)
+    # the same workspace reused across calls and shapes gives the same results
+    T2, S2 = gen_matrix(61, 8, N, K)
+    d2 = Dev(bgg, torch, fmt, T2, S2)
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d2.desc, 16))
+    y_a = d2.gemv(x, ws=ws)
+    y_b = d2.gemv(x[:1], ws=ws)
+    y_c = d2.gemv(x, ws=ws)
+    assert np.array_equal(y_a, y_c)
+    assert np.array_equal(y_a[:1], y_b)
+
+
+def test_gemv_decode_step_shapes_sampled(env):
+    """Every projection shape of the 64-layer decode step at full size
+    (first and last layer), both packings; outputs of 96 sampled rows per
+    matrix checked against the oracle, which regenerates just those rows."""
+    bgg, torch = env
+    w = synth.WORKLOADS["decode_step"]
+    rng = np.random.default_rng(0)
+    for mat in [m for m in w["matrices"] if m.name.startswith(("L0.", "L63."))]:
+        T, S = synth.workload_matrix(mat, w["seed"])
+        x = synth.workload_x(w["seed"], 1, mat.k)
+        rows = np.sort(rng.choice(mat.n, 96, replace=False))
+        for fmt in FMTS:
+            say(f"decode-step {fmt} {mat.name} N={mat.n} K={mat.k}")
+            y = Dev(bgg, torch, fmt, T, S).gemv(x)
+            ref = oracle.matvec(T[rows], S[rows], oracle.rotate(x))
+            full_scale = np.max(np.abs(y.astype(np.float64)))
+            err = np.max(np.abs(y[:, rows].astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30)
+            assert err <= TOL and full_scale > 0
+
+
+@pytest.mark.parametrize("M", [2, 4, 8, 16])
+def test_gemv_small_batch_full_shapes(env, M):
+    """Small-batch decode at the decode step's gate/up and down shapes."""
+    bgg, torch = env
+    w = synth.WORKLOADS["small_batch"]
+    for mat in [m for m in w["matrices"] if m.name in ("L0.gate", "L0.down")]:
+        T, S = synth.workload_matrix(mat, w["seed"])
+        x = synth.workload_x(w["seed"], M, mat.k)
+        rows = np.arange(0, mat.n, 37)
+        xr = oracle.rotate(x)
+        ref = oracle.matvec(T[rows], S[rows], xr)
+        for fmt in FMTS:
+            say(f"small-batch {fmt} M={M} {mat.name}")
+            y = Dev(bgg, torch, fmt, T, S).gemv(x)
+            assert np.all(relerr(y[:, rows], ref) <= TOL)
+
+
+# ---------------------------------------------------------------------------
+# prompt GEMM
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (96, 256, 512), (200, 300, 640), (129, 1000, 1152),
+                                   (257, 129, 2048)])
+def test_gemm_parity(env, M, N, K):
+    bgg, torch = env
+    say(f"gemm M={M} N={N} K={K}")
+    T, S = gen_matrix(71, 9, N, K)
+    x = synth.activations_f16(71, 10, M, K)
+    d = Dev(bgg, torch, "PQ2_0", T, S)
+    y = d.gemm(x)
+    assert not np.isnan(y).any()
+    ref = oracle_y("PQ2_0", T, S, x)
+    e = relerr(y, ref)
+    say(f"  rel err max {e.max():.3g}")
+    assert np.all(e <= TOL)
+    # without rotation, given x'
+    xr = oracle.rotate(x).astype(np.float16)
+    y2 = d.gemm(xr, rotate=False)
+    assert np.all(relerr(y2, oracle_y("PQ2_0", T, S, xr, rotate=False)) <= TOL)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_gemm_prefill_full_size_sampled(env, name):
+    """The prefill workload (4096 tokens) at full size; 24 token rows checked
+    against the oracle over all N outputs."""
+    bgg, torch = env
+    w = synth.WORKLOADS["prefill"]
+    mat = [m for m in w["matrices"] if m.name == name][0]
+    say(f"gemm full {name} M=4096 N={mat.n} K={mat.k}")
+    T, S = synth.workload_matrix(mat, w["seed"])
+    x = synth.workload_x(w["seed"], 4096, mat.k)
+    y = Dev(bgg, torch, "PQ2_0", T, S).gemm(x)
+    assert not np.isnan(y).any()
+    rows = np.array([0, 1, 2, 31, 32, 127, 128, 255, 256, 1000, 2047, 2048, 3000, 4031, 4064, 4095,
+                     511, 512, 767, 1023, 1536, 2560, 3583, 3584])
+    ref = oracle.matvec(T, S, oracle.rotate(x[rows]))
+    e = relerr(y[rows], ref)
+    say(f"  rel err max {e.max():.3g}")
+    assert np.all(e <= TOL)
