@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary linear-layer hot path on one MI355X.
+
+Workload (one step): the single-projection decode workload at batch 1 --
+gate/up (K=5120 -> N=17408) and down (K=17408 -> N=5120), each in both
+packings (PQ2_0, PTQ1_0), each call applying the block-128 Hadamard
+transform to its fp16 input and then the GEMV.  Inputs are seeded and
+synthetic (trit, scale and activation distributions of the 27B-class stack)
+and resident in HBM before timing starts; the weights rotate over several
+distinct device copies (> 512 MiB together) so the 256 MiB Infinity Cache
+cannot serve them.
+
+value = packed weight bytes of the step (format bytes: trits + fp16 scales)
+        / wall time of one step.
+
+Also printed in the same JSON line: the roofline of the dominant GEMV kernel
+(its own average duration from HIP events recorded around every launch in
+the timed region), per-kernel figures, the prefill GEMM (4096 tokens) in
+TFLOP/s with its MFMA roofline and the activation transform in GB/s, and
+the CPU oracle timed on this host on the whole step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+METRIC = "ternary GEMV packed-weight GB/s (% HBM peak) + prefill GEMM TFLOPS (% MFMA)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_gemv_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "gemv_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="distinct device copies of the weights")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the path has no multi-GPU part", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_gemv_gemm_amd as bgg
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = synth.WORKLOADS["projection"]
+    seed = w["seed"]
+    fmts = ("PQ2_0", "PTQ1_0")
+
+    # ------------------------------------------------------------------ data
+    t0 = time.time()
+    items = []  # one per (format, matrix)
+    for mat in w["matrices"]:
+        T, S = synth.workload_matrix(mat, seed)
+        x = torch.from_numpy(synth.workload_x(seed, 1, mat.k)).to(dev)
+        for fmt in fmts:
+            d = bgg.bgg_describe(fmt, mat.n, mat.k)
+            host = bgg.bgg_pack_weights(d, T, S)
+            copies = [bgg.upload(host, dev) for _ in range(args.copies)]
+            ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d, 1), dev)
+            y = torch.empty((1, mat.n), dtype=torch.float16, device=dev)
+            items.append(dict(fmt=fmt, name=mat.name, desc=d, copies=copies, ws=ws, x=x, y=y,
+                              bytes=int(d.format_bytes), n=mat.n, k=mat.k))
+        del T, S
+    resident = sum(it["desc"].total_bytes * args.copies for it in items)
+    log(f"setup {time.time() - t0:.1f}s; {resident / 2**20:.0f} MiB of packed weights resident")
+
+    def step(i, events=None):
+        c = i % args.copies
+        for j, it in enumerate(items):
+            bgg.bgg_gemv_prepare(it["desc"], it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
+            if events is not None:
+                events[j][0].record(stream)
+            bgg.bgg_gemv_run(it["desc"], it["copies"][c], it["y"], 1, it["ws"], stream)
+            if events is not None:
+                events[j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in items] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall / args.steps * 1e3
+    step_bytes = sum(it["bytes"] for it in items)
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    kernels = []
+    for j, it in enumerate(items):
+        us = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)])) * 1e3
+        kname = f"k_gemv_{'pq2' if it['fmt'] == 'PQ2_0' else 'ptq1'}"
+        kernels.append(dict(kernel=kname, format=it["fmt"], matrix=it["name"], n=it["n"], k=it["k"],
+                            bytes_per_launch=it["bytes"], avg_us=round(us, 3),
+                            gbs=round(it["bytes"] / us / 1e3, 1),
+                            frac=round(it["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)))
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    traffic = measured_traffic(f"{dom['kernel']}:{dom['format']}:{dom['matrix']}")
+    roofline = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dom["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel=f"{dom['kernel']} ({dom['format']}, {dom['matrix']} {dom['n']}x{dom['k']})",
+                    bytes_per_launch=dom["bytes_per_launch"], avg_us=dom["avg_us"])
+    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; kernels: " +
+        ", ".join(f"{k['format']}/{k['matrix']} {k['avg_us']:.2f}us {k['gbs']:.0f}GB/s" for k in kernels))
+    for it in items:
+        del it["copies"]
+
+    # --------------------------------------------------------- prefill GEMM
+    prefill = None
+    if not args.no_prefill:
+        pw = synth.WORKLOADS["prefill"]
+        M = pw["m"][0]
+        shapes, fwht = [], []
+        for mat in pw["matrices"]:
+            T, S = synth.workload_matrix(mat, pw["seed"])
+            d = bgg.bgg_describe("PQ2_0", mat.n, mat.k)
+            packed = bgg.upload(bgg.bgg_pack_weights(d, T, S), dev)
+            x = torch.from_numpy(synth.workload_x(pw["seed"], M, mat.k)).to(dev)
+            xr = torch.empty_like(x)
+            y = torch.empty((M, mat.n), dtype=torch.float16, device=dev)
+            reps = 10
+            for _ in range(3):
+                bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
+                bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+            torch.cuda.synchronize()
+            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for r in range(reps):
+                e[r][0].record(stream)
+                bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
+                e[r][1].record(stream)
+                bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+                e[r][2].record(stream)
+            torch.cuda.synchronize()
+            f_us = float(np.mean([a.elapsed_time(b) for a, b, _ in e])) * 1e3
+            g_us = float(np.mean([b.elapsed_time(c) for _, b, c in e])) * 1e3
+            flops = 2.0 * M * mat.n * mat.k
+            shapes.append(dict(matrix=mat.name, m=M, n=mat.n, k=mat.k, avg_us=round(g_us, 1),
+                               tflops=round(flops / g_us / 1e6, 1)))
+            fbytes = 2 * M * mat.k * 2
+            fwht.append(dict(m=M, k=mat.k, avg_us=round(f_us, 1), gbs=round(fbytes / f_us / 1e3, 1)))
+            del T, S, packed, x, xr, y
+        tot_flops = sum(2.0 * s["m"] * s["n"] * s["k"] for s in shapes)
+        tot_us = sum(s["avg_us"] for s in shapes)
+        tf = tot_flops / tot_us / 1e6
+        prefill = dict(
+            workload="prefill: 4096 tokens x (5120->17408, 17408->5120), PQ2_0, x' precomputed",
+            tflops=round(tf, 1), unit="TFLOP/s", shapes=shapes,
+            roofline=dict(bound="mfma", achieved=round(tf, 1), peak=F16_MFMA_PEAK_TFLOPS,
+                          unit="TFLOP/s", frac=round(tf / F16_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                          kernel="k_gemm_pq2 (fp16 MFMA, fp32 accumulate)"),
+            fwht=dict(kernel="k_hadamard_rotate", shapes=fwht,
+                      roofline=dict(bound="hbm", achieved=max(f["gbs"] for f in fwht),
+                                    peak=HBM_PEAK_GBS, unit="GB/s",
+                                    frac=round(max(f["gbs"] for f in fwht) / HBM_PEAK_GBS, 4))))
+        log(f"prefill {tf:.0f} TFLOP/s; " + ", ".join(f"{s['matrix']} {s['tflops']} TF" for s in shapes))
+
+    # ----------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = []
+        for mat in w["matrices"]:
+            T, S = synth.workload_matrix(mat, seed)
+            xh = synth.workload_x(seed, 1, mat.k)
+            for fmt in fmts:
+                sample.append((fmt, oracle.pack(fmt, T), S, xh, oracle.format_bytes(fmt, mat.n, mat.k)))
+            del T
+        done_bytes, t_cpu, reps = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds:
+            for fmt, P, S, xh, nb in sample:
+                t1 = time.perf_counter()
+                oracle.linear(fmt, P, S, xh)
+                t_cpu += time.perf_counter() - t1
+                done_bytes += nb
+            reps += 1
+        cpu = dict(value=round(done_bytes / t_cpu / 1e9, 4), unit="GB/s", cores=oracle.num_threads(),
+                   kind="oracle",
+                   sample=f"the whole step (gate_up + down, PQ2_0 + PTQ1_0, M=1, unpack + dense "
+                          f"rotation + fp64 dot) run {reps} times, {t_cpu:.1f} s")
+        log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i32+f32", "data": "synthetic",
+        "config": {"workload": "projection: gate_up 17408x5120 + down 5120x17408, batch 1, "
+                               "PQ2_0 and PTQ1_0, Hadamard transform on every call",
+                   "global_batch": 1, "copies": args.copies,
+                   "packed_bytes_per_step": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "prefill_gemm": prefill,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

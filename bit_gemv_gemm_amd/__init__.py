@@ -13,6 +13,12 @@ import os
 
 import numpy as np
 
+# PyTorch ships its own HIP runtime (libamdhip64.so.7, same soname as the
+# system one).  libbgg.so must bind to the runtime PyTorch uses, so PyTorch
+# is loaded first; loading libbgg.so first would pull the system runtime into
+# the process and leave PyTorch running on a runtime it was not built for.
+import torch  # noqa: F401  (load order matters, see above)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbgg.so")
 
@@ -67,6 +73,8 @@ _SIGS = {
     "bgg_hadamard_rotate": ([_vp, _vp, _i64, _i64, _vp], _i32),
     "bgg_gemv_workspace_size": ([_P, _i64], _sz),
     "bgg_ternary_gemv": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
+    "bgg_gemv_prepare": ([_P, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
+    "bgg_gemv_run": ([_P, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
     "bgg_gemm_workspace_size": ([_P, _i64], _sz),
     "bgg_ternary_gemm": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_status_string": ([_i32], ctypes.c_char_p),
@@ -196,6 +204,21 @@ def bgg_ternary_gemv(desc, packed_dev, x_dev, y_dev, M: int, flags: int, workspa
     _ok(_lib.bgg_ternary_gemv(ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
                               _dev_ptr(x_dev, M * desc.K * 2, "x"), _dev_ptr(y_dev, M * desc.N * 2, "y"),
                               M, flags, ws, wsb, _stream(stream)), "bgg_ternary_gemv")
+
+
+def bgg_gemv_prepare(desc, x_dev, M: int, flags: int, workspace, stream=None) -> None:
+    ws = _dev_ptr(workspace, 0, "workspace")
+    wsb = workspace.numel() * workspace.element_size()
+    _ok(_lib.bgg_gemv_prepare(ctypes.byref(desc), _dev_ptr(x_dev, M * desc.K * 2, "x"), M, flags, ws,
+                              wsb, _stream(stream)), "bgg_gemv_prepare")
+
+
+def bgg_gemv_run(desc, packed_dev, y_dev, M: int, workspace, stream=None) -> None:
+    ws = _dev_ptr(workspace, 0, "workspace")
+    wsb = workspace.numel() * workspace.element_size()
+    _ok(_lib.bgg_gemv_run(ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
+                          _dev_ptr(y_dev, M * desc.N * 2, "y"), M, ws, wsb, _stream(stream)),
+        "bgg_gemv_run")
 
 
 def bgg_ternary_gemm(desc, packed_dev, x_dev, y_dev, M: int, flags: int, workspace, stream=None) -> None:

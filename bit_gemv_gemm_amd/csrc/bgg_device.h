@@ -1,0 +1,145 @@
+// Device helpers shared by the kernels of libbgg (gfx950).
+#pragma once
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bgg_internal.h"
+
+namespace bgg {
+
+constexpr int kGroup = BGG_GROUP;   // 128 weights per scale / Hadamard block
+constexpr int kTile = BGG_ROW_TILE;  // 64 weight rows per tile, one per lane
+
+// PTQ1_0 period: 5 groups = 640 trits = 128 row bytes = 8 chunks.  Group
+// ends fall inside bytes 25, 51, 76 and 102 of every period and at its end.
+constexpr int kPeriodGroups = 5;
+constexpr int kPeriodBytes = 128;
+constexpr int kPeriodChunks = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data that is read once (packed weights): non-temporal.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// 1/sqrt(128) rounded to fp32.
+constexpr float kHadamardNorm = 0.08838834764831845f;
+
+// Fast Walsh-Hadamard transform (Sylvester order, unnormalised) of one
+// 128-block held by 16 lanes, 8 consecutive values each (lane i of the 16
+// holds positions 8i..8i+7).  Butterflies (a, b) -> (a + b, a - b) over
+// strides 1..64, in fp32.
+__device__ __forceinline__ void fwht128_unscaled(float v[8], int lane16) {
+#pragma unroll
+  for (int s = 1; s < 8; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & s)) {
+        const float a = v[i], b = v[i + s];
+        v[i] = a + b;
+        v[i + s] = a - b;
+      }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const float sgn = (lane16 & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __shfl_xor(v[i], m, 16);
+      v[i] = fmaf(sgn, v[i], p);  // low lane: v + p; high lane: p - v
+    }
+  }
+}
+
+__device__ __forceinline__ void load8h(const uint16_t* p, float v[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = h2f((uint16_t)(w[i] & 0xFFFF));
+    v[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+  }
+}
+
+// Signed 4-bit digit L of q (|q| <= 2^14): q = d0 + 16 d1 + 256 d2 + 4096 d3,
+// every d in [-8, 7] (d3 in [-4, 4]).
+__device__ __forceinline__ int digit4(int q, int L) {
+  int d = 0;
+#pragma unroll
+  for (int i = 0; i <= 3; ++i) {
+    d = (int)((unsigned)q << 28) >> 28;  // sign-extended low nibble
+    if (i == L) break;
+    q = (q - d) >> 4;
+  }
+  return L == 3 ? q : d;
+}
+
+// PQ2_0: 16 codes of one word -> codes of even positions in the low two
+// bits of each nibble (E) and of odd positions likewise (O).
+__device__ __forceinline__ uint32_t pq2_even(uint32_t w) { return w & 0x33333333u; }
+__device__ __forceinline__ uint32_t pq2_odd(uint32_t w) { return (w >> 2) & 0x33333333u; }
+
+// PTQ1_0: the five base-3 digits of a byte (= t + 1 of five trits), one per
+// nibble 0..4.  Bytes 243..255 come from no trits; they decode as five zero
+// trits (digits 1).
+__device__ __forceinline__ uint32_t ptq1_entry(uint32_t b) {
+  if (b >= 243) return 0x11111u;
+  uint32_t e = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    e |= (b % 3u) << (4 * i);
+    b /= 3u;
+  }
+  return e;
+}
+
+// The LUT: 256 entries, each stored 32 times so that lane l reads copy l%32
+// and a wave's 64 random lookups hit 32 distinct banks (32 KiB of LDS).
+constexpr int kLutCopies = 32;
+__device__ __forceinline__ void build_lut(uint32_t* lut) {
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+    const uint32_t e = ptq1_entry((uint32_t)b);
+    const uint4 v = make_uint4(e, e, e, e);
+    uint4* dst = reinterpret_cast<uint4*>(lut + b * kLutCopies);
+#pragma unroll
+    for (int c = 0; c < kLutCopies / 4; ++c) dst[c] = v;
+  }
+}
+
+// The GEMV's LUT: 256 entries x 64 copies (64 KiB).  Entry e of copy c is
+// the word at byte address e * 256 + c * 4, so lane l reads copy l and the
+// address of byte j of a packed word w is one v_perm_b32:
+//   byte 0 = l * 4 (from lane_off), byte 1 = byte j of w, bytes 2-3 = 0.
+constexpr int kLut64Copies = 64;
+__device__ __forceinline__ void build_lut64(uint32_t* lut) {
+  for (int i = threadIdx.x; i < 256 * (kLut64Copies / 4); i += blockDim.x) {
+    const uint32_t e = ptq1_entry((uint32_t)(i / (kLut64Copies / 4)));
+    reinterpret_cast<uint4*>(lut)[i] = make_uint4(e, e, e, e);
+  }
+}
+template <int J>
+__device__ __forceinline__ uint32_t lut64_addr(uint32_t word, uint32_t lane_off) {
+  return __builtin_amdgcn_perm(word, lane_off, 0x0C0C0000u | ((4u + J) << 8));
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+inline bgg_status hip_check(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BGG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return BGG_OK;
+}
+
+}  // namespace bgg

@@ -1,0 +1,635 @@
+// Decode-time GEMV y[M][N] = x'[M][K] . (S*T)[N][K]^T for 1 <= M <= 16 on
+// gfx950, for both packings.
+//
+// What is computed: allhereai.com/news/1346 ("27B 模型压到 5.95GB…"), method
+// paragraph (trits, one FP16 scale per 128 weights, block-Hadamard-rotated
+// storage), runtime paragraph (the activations get the Hadamard transform at
+// run time) and packing paragraph (PQ2_0 and PTQ1_0; decoding PTQ1_0 costs
+// arithmetic); 10100.com/article/156675786, section "它怎么做到的".
+//
+// Design (one MI355X: 256 CUs in 8 XCDs, 64-lane waves, HBM3E):
+//   * activation prep (one small kernel per call): x -> x' in fp32 -> per
+//     128-group a power-of-two scale 2^(e-14) with max|x'| < 2^e and
+//     q = rint(x' 2^(14-e)), |q| <= 2^14, cut into four signed 4-bit digits
+//     packed eight to a word in the order the trit codes will meet them;
+//   * one lane per weight row: a wave reads a 64-row tile chunk by chunk
+//     with coalesced 16-byte loads (1 KiB per instruction), so all lanes sit
+//     at the same K and the digit words are wave-uniform: they live in
+//     scalar registers and cost no LDS or vector-cache bandwidth;
+//   * trits are never turned into floats: PQ2_0 codes c = t + 1 are spread
+//     into 4-bit lanes with one mask (even positions) or a shift and a mask
+//     (odd), PTQ1_0 bytes go through a base-3 LUT in LDS to five 4-bit codes,
+//     and v_dot8_i32_i4 multiplies 8 codes by 8 digits.  Per group the exact
+//     integer sum of c*q minus the sum of q is the sum of t*q; it is scaled
+//     by s * 2^(e-14) and accumulated in fp32;
+//   * K is split over the eight waves of a workgroup (reduced in LDS, fixed
+//     order) and, when the tiles alone cannot fill the chip, over
+//     workgroups; those partial sums are added in slice order by a second,
+//     small kernel (deterministic, no atomics, no cache-flushing fences).
+#include "bgg_device.h"
+
+#include <cstdlib>
+
+using namespace bgg;
+
+namespace {
+
+// Digit words of one PQ2_0 chunk (64 trits): 4 code words x {even, odd}
+// positions x 4 digits.
+constexpr int kPqFragWords = 32;
+// Digit words of one PTQ1_0 period: 4 per byte, plus 4 for the upper part
+// of each of the 4 bytes that straddle a group end.
+constexpr int kPtqFragWords = kPeriodBytes * 4 + 4 * 4;  // 528
+
+constexpr int kPrepGroups = 5;  // groups per prep workgroup (one PTQ1_0 period)
+constexpr int kPrepThreads = kPrepGroups * 16;
+
+// ---------------------------------------------------------------------------
+// activation prep
+// grid: (ceil(Gpad / 5), token slots); block: 80 threads = 5 groups x 16
+// lanes.  Tokens past Mreal get zeros.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ void __launch_bounds__(kPrepThreads)
+    k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
+                uint32_t* __restrict__ frag, int64_t frag_words_per_token,
+                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad) {
+  // the four 4-bit digits of every q of the workgroup's 640 positions
+  __shared__ uint16_t sd[kPrepGroups * kGroup];
+  const int tid = threadIdx.x;
+  const int m = blockIdx.y;
+  const int64_t G = K / kGroup;
+  const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
+  const int gl = tid >> 4, lane16 = tid & 15;
+  const int64_t g = g0 + gl;
+  const bool valid = g < G && m < Mreal;
+
+  float v[8];
+  if (valid) {
+    load8h(x + (int64_t)m * K + g * kGroup + lane16 * 8, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+  }
+  if (rotate) {
+    fwht128_unscaled(v, lane16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+  for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+  int e = 0;
+  frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1): |x'| < 2^e
+  int qsum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = amax > 0.0f ? (int)rintf(ldexpf(v[j], 14 - e)) : 0;
+    uint32_t nib = 0;
+#pragma unroll
+    for (int L = 0; L < 4; ++L) nib |= (uint32_t)(digit4(q, L) & 15) << (4 * L);
+    sd[gl * kGroup + lane16 * 8 + j] = (uint16_t)nib;
+    qsum += q;
+  }
+#pragma unroll
+  for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
+  if (lane16 == 0 && g < gpad) {
+    metaQ[(int64_t)m * gpad + g] = qsum;
+    metaF[(int64_t)m * gpad + g] = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
+  }
+  __syncthreads();
+
+  uint32_t* out = frag + (int64_t)m * frag_words_per_token;
+  if (FMT == BGG_FMT_PQ2_0) {
+    // 10 chunks x 32 words; word (d, par, L) of chunk c: nibble n = digit L
+    // of q at chunk position 16 d + 2 n + par.
+    const int64_t C = K / 64;
+    for (int w = tid; w < 2 * kPrepGroups * kPqFragWords; w += kPrepThreads) {
+      const int cl = w / kPqFragWords, r = w % kPqFragWords;
+      const int d = r >> 3, par = (r >> 2) & 1, L = r & 3;
+      const int64_t c = g0 * 2 + cl;
+      if (c >= C) continue;
+      uint32_t word = 0;
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        word |= ((uint32_t)(sd[cl * 64 + 16 * d + 2 * n + par] >> (4 * L)) & 15u) << (4 * n);
+      out[c * kPqFragWords + r] = word;
+    }
+  } else {
+    // one period, 528 words.  Word (byte jb, L), jb < 128: nibble i = digit L
+    // of q at period position 5 jb + i, kept only if that position is in the
+    // same group as 5 jb.  Word 512 + 4 s + L: the upper part of the s-th
+    // straddling byte (positions in the next group).
+    const int64_t p = g0 / kPeriodGroups;
+    for (int w = tid; w < kPtqFragWords; w += kPrepThreads) {
+      int jb, upper;
+      const int L = w & 3;
+      if (w < kPeriodBytes * 4) {
+        jb = w >> 2, upper = 0;
+      } else {
+        // the bytes whose five trits cross a group end: 25, 51, 76, 102
+        jb = (kGroup * (((w - kPeriodBytes * 4) >> 2) + 1)) / 5, upper = 1;
+      }
+      const int first_group = (5 * jb) / kGroup;
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int pos = 5 * jb + i;
+        if (pos / kGroup == first_group + upper)
+          word |= ((uint32_t)(sd[pos] >> (4 * L)) & 15u) << (4 * i);
+      }
+      out[p * kPtqFragWords + w] = word;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup end: the W waves' partial sums are added in wave order in LDS;
+// wave 0 writes y (when the workgroup covers all of K) or a partial row for
+// the reduce kernel.
+// ---------------------------------------------------------------------------
+template <int M, int W>
+__device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M][64], int wave,
+                                          int lane, int64_t row, int64_t N, int Mreal, int Sg,
+                                          int wgs, int64_t rows_pad, float* __restrict__ partial,
+                                          uint16_t* __restrict__ y) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) red[wave][m][lane] = acc[m];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float s = red[0][m][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) s += red[w][m][lane];
+    if (m < Mreal && row < N) {
+      if (Sg == 1)
+        y[(int64_t)m * N + row] = f2h(s);
+      else
+        partial[((int64_t)wgs * M + m) * rows_pad + row] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// PQ2_0: wave = 64 rows x BPS groups; workgroup = W consecutive K slices.
+// grid: NT * Sg workgroups of 64*W threads.
+// ---------------------------------------------------------------------------
+template <int M, int BPS, int W>
+__global__ void __launch_bounds__(64 * W)
+    k_gemv_pq2(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
+               int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
+               int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
+               const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
+               int64_t rows_pad, uint16_t* __restrict__ y) {
+  __shared__ float red[W][M][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile = blockIdx.x / Sg;
+  const int wgs = (int)(blockIdx.x % Sg);
+  const int64_t gbeg = ((int64_t)wgs * W + wave) * BPS;
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  if (gbeg < G) {
+    const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
+    const uint16_t* sdata =
+        reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile + lane;
+    // Every load of the slice is issued before any is used, without branches
+    // (a group past G re-reads group G-1 and gets a zero weight below).
+    uint4 w[2 * BPS];
+    uint16_t sc[BPS];
+#pragma unroll
+    for (int i = 0; i < BPS; ++i) {
+      const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
+      w[2 * i] = ld_stream(tdata + (2 * g) * kTile);
+      w[2 * i + 1] = ld_stream(tdata + (2 * g + 1) * kTile);
+      sc[i] = sdata[g * kTile];
+    }
+    // per-group activation scale and digit sum, for every token
+    float gf[BPS][M];
+    int gq[BPS][M];
+#pragma unroll
+    for (int i = 0; i < BPS; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const bool gv = gbeg + i < G;
+        const int64_t g = gv ? gbeg + i : G - 1;
+        gf[i][m] = gv ? metaF[(int64_t)m * gpad + g] : 0.0f;
+        gq[i][m] = metaQ[(int64_t)m * gpad + g];
+      }
+    // keep the scheduler from sinking the loads towards their uses
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int i = 0; i < BPS; ++i) {
+      const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
+      const float s = h2f(sc[i]);
+      uint32_t E[8], O[8];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t cw[4] = {w[2 * i + c].x, w[2 * i + c].y, w[2 * i + c].z, w[2 * i + c].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          E[c * 4 + d] = pq2_even(cw[d]);
+          O[c * 4 + d] = pq2_odd(cw[d]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint32_t* xf = frag + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
+        int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t* f = xf + c * kPqFragWords + d * 8;
+            const int e = (int)E[c * 4 + d], o = (int)O[c * 4 + d];
+            a0 = __builtin_amdgcn_sdot8(e, (int)f[0], a0, false);
+            a1 = __builtin_amdgcn_sdot8(e, (int)f[1], a1, false);
+            a2 = __builtin_amdgcn_sdot8(e, (int)f[2], a2, false);
+            a3 = __builtin_amdgcn_sdot8(e, (int)f[3], a3, false);
+            a0 = __builtin_amdgcn_sdot8(o, (int)f[4], a0, false);
+            a1 = __builtin_amdgcn_sdot8(o, (int)f[5], a1, false);
+            a2 = __builtin_amdgcn_sdot8(o, (int)f[6], a2, false);
+            a3 = __builtin_amdgcn_sdot8(o, (int)f[7], a3, false);
+          }
+        const int p = a0 + (a1 << 4) + (a2 << 8) + (a3 << 12) - gq[i][m];
+        acc[m] = fmaf(s * gf[i][m], (float)p, acc[m]);
+      }
+    }
+  }
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
+                  y);
+}
+
+// ---------------------------------------------------------------------------
+// PTQ1_0: wave = 64 rows x PPS periods (5 groups each); workgroup = W
+// consecutive K slices sharing one 64-copy LUT.
+// ---------------------------------------------------------------------------
+template <int M>
+__device__ __forceinline__ void ptq1_close(int (&a)[M][4], float (&acc)[M], const float (&gf)[M],
+                                           const int (&gq)[M], float s) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int p = a[m][0] + (a[m][1] << 4) + (a[m][2] << 8) + (a[m][3] << 12) - gq[m];
+    acc[m] = fmaf(s * gf[m], (float)p, acc[m]);
+#pragma unroll
+    for (int L = 0; L < 4; ++L) a[m][L] = 0;
+  }
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t word_of(const uint4& c) {
+  return J == 0 ? c.x : J == 1 ? c.y : J == 2 ? c.z : c.w;
+}
+
+template <int M, int PPS, int W>
+__global__ void __launch_bounds__(64 * W)
+    k_gemv_ptq1(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
+                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
+                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
+                const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
+                int64_t rows_pad, uint16_t* __restrict__ y) {
+  __shared__ uint32_t lut[256 * kLut64Copies];
+  __shared__ float red[W][M][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile = blockIdx.x / Sg;
+  const int wgs = (int)(blockIdx.x % Sg);
+  const int64_t P = ceil_div(G, kPeriodGroups);
+  const int64_t pbeg = ((int64_t)wgs * W + wave) * PPS;
+  const bool active = pbeg < P;
+  const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
+  const uint16_t* sdata =
+      reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile + lane;
+  // All loads of the slice first -- before the LUT is built, so they are in
+  // flight meanwhile -- and branch-free: chunks past the row and groups past
+  // G re-read the last valid one and are zeroed / weighted 0 below.
+  uint4 wall[PPS][kPeriodChunks];
+  uint16_t scall[PPS][kPeriodGroups];
+  if (active) {
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      const int64_t p = pbeg + pp;
+#pragma unroll
+      for (int c = 0; c < kPeriodChunks; ++c) {
+        const int64_t j = p * kPeriodChunks + c;
+        wall[pp][c] = ld_stream(tdata + (j < C ? j : C - 1) * kTile);
+      }
+#pragma unroll
+      for (int k = 0; k < kPeriodGroups; ++k) {
+        const int64_t g = p * kPeriodGroups + k;
+        scall[pp][k] = sdata[(g < G ? g : G - 1) * kTile];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  build_lut64(lut);
+  __syncthreads();
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+  if (active) {
+    const uint32_t lane_off = (uint32_t)lane * 4u;
+    const char* lbase = reinterpret_cast<const char*>(lut);
+
+    int a[M][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int L = 0; L < 4; ++L) a[m][L] = 0;
+
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      const int64_t p = pbeg + pp;
+      if (p >= P) break;
+      const int64_t gp = p * kPeriodGroups;
+      uint4 w[kPeriodChunks];
+#pragma unroll
+      for (int c = 0; c < kPeriodChunks; ++c)
+        w[c] = p * kPeriodChunks + c < C ? wall[pp][c] : make_uint4(0, 0, 0, 0);
+      // group scales (zero past G) and the activations' group meta
+      float sc[kPeriodGroups], gf[kPeriodGroups][M];
+      int gq[kPeriodGroups][M];
+#pragma unroll
+      for (int k = 0; k < kPeriodGroups; ++k) {
+        const bool gv = gp + k < G;
+        sc[k] = gv ? h2f(scall[pp][k]) : 0.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
+          gq[k][m] = metaQ[(int64_t)m * gpad + gp + k];
+        }
+      }
+      const uint32_t* fp = frag + p * kPtqFragWords;
+      // fully unrolled: byte positions, group ends and straddles are constants
+#pragma clang loop unroll(full)
+      for (int jb = 0; jb < kPeriodBytes; ++jb) {
+        const uint32_t word = (jb >> 2 & 3) == 0 ? w[jb >> 4].x
+                              : (jb >> 2 & 3) == 1 ? w[jb >> 4].y
+                              : (jb >> 2 & 3) == 2 ? w[jb >> 4].z : w[jb >> 4].w;
+        uint32_t addr;
+        switch (jb & 3) {
+          case 0: addr = lut64_addr<0>(word, lane_off); break;
+          case 1: addr = lut64_addr<1>(word, lane_off); break;
+          case 2: addr = lut64_addr<2>(word, lane_off); break;
+          default: addr = lut64_addr<3>(word, lane_off); break;
+        }
+        const int codes = *reinterpret_cast<const int*>(lbase + addr);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint32_t* f = fp + m * frag_words_per_token + jb * 4;
+#pragma unroll
+          for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
+        }
+        const int k_first = (5 * jb) / kGroup, k_last = (5 * jb + 4) / kGroup;
+        if (k_last != k_first) {
+          // this byte's trits cross a group end: close the lower group and
+          // start the next one with the byte's upper trits
+          ptq1_close<M>(a, acc, gf[k_first], gq[k_first], sc[k_first]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const uint32_t* f = fp + m * frag_words_per_token + kPeriodBytes * 4 + k_first * 4;
+#pragma unroll
+            for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
+          }
+        } else if ((5 * jb + 5) % kGroup == 0) {
+          ptq1_close<M>(a, acc, gf[k_first], gq[k_first], sc[k_first]);
+        }
+      }
+    }
+  }
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
+                  y);
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the workgroup partial rows, in workgroup-slice order.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+    k_gemv_reduce(const float* __restrict__ partial, int Sg, int Mb, int Mreal, int64_t rows_pad,
+                  int64_t N, uint16_t* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Mreal * N) return;
+  const int64_t m = i / N, row = i % N;
+  float s = 0.0f;
+  for (int k = 0; k < Sg; ++k) s += partial[((int64_t)k * Mb + m) * rows_pad + row];
+  y[m * N + row] = f2h(s);
+}
+
+// ---------------------------------------------------------------------------
+// plan and launch
+// ---------------------------------------------------------------------------
+// Token counts one GEMV kernel handles at once; a larger M runs in groups of
+// kGemvTokens tokens (each group reads the weights again).
+constexpr int kGemvTokens = 4;
+inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+// Token slots of the prepared activations: padding tokens are zero.
+inline int64_t gemv_m_slots(int64_t M) {
+  return M <= 2 ? M : ((M + kGemvTokens - 1) / kGemvTokens) * kGemvTokens;
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+  const char* e = getenv(name);
+  const int64_t v = e ? atoll(e) : 0;
+  return v > 0 ? v : dflt;
+}
+
+// Split of K: units along K (PQ2_0: groups, PTQ1_0: periods of 5 groups),
+// units per wave slice, waves per workgroup W, slices S, workgroup slices
+// Sg = ceil(S / W) (Sg > 1 adds the reduce kernel), and the workspace layout
+// [digit words][group Q][group F][partial rows].
+struct GemvPlan {
+  int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
+  uint64_t off_meta_q, off_meta_f, off_partial, total;
+};
+
+GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
+  static const int64_t target = env_int("BGG_GEMV_TARGET_WAVES", 2048);
+  static const int64_t min_single = env_int("BGG_GEMV_MIN_WAVES", 1024);
+  GemvPlan p{};
+  p.G = d->groups;
+  p.NT = d->row_tiles;
+  p.rows_pad = p.NT * kTile;
+  p.slots = gemv_m_slots(M);
+  p.W = 8;
+  if (d->format == BGG_FMT_PQ2_0) {
+    p.gpad = p.G;
+    p.units = p.G;
+    p.frag_words_per_token = (d->K / 64) * kPqFragWords;
+    // one workgroup per tile (no reduce kernel) when that still fills the
+    // chip: the smallest groups-per-wave with all of K in 8 waves
+    const int64_t one_wg[] = {2, 4, 5, 8};
+    p.per_slice = 0;
+    for (int64_t b : one_wg)
+      if (ceil_div(p.units, b) <= p.W && p.NT * p.W >= min_single) {
+        p.per_slice = b;
+        break;
+      }
+    if (!p.per_slice) {
+      // else the largest groups-per-wave that gives the target wave count
+      p.per_slice = 8;
+      while (p.per_slice > 2 && p.NT * p.W * ceil_div(ceil_div(p.units, p.per_slice), p.W) < target)
+        p.per_slice /= 2;
+    }
+  } else {
+    const int64_t P = ceil_div(p.G, kPeriodGroups);
+    p.gpad = P * kPeriodGroups;
+    p.units = P;
+    p.frag_words_per_token = P * kPtqFragWords;
+    p.per_slice = (p.NT * P >= 2 * target) ? 2 : 1;
+  }
+  p.S = ceil_div(p.units, p.per_slice);
+  p.Sg = ceil_div(p.S, p.W);
+  const int64_t kb = gemv_m_bucket(M);
+  uint64_t off = align256((uint64_t)p.slots * p.frag_words_per_token * 4);
+  p.off_meta_q = off;
+  off = align256(off + (uint64_t)p.slots * p.gpad * 4);
+  p.off_meta_f = off;
+  off = align256(off + (uint64_t)p.slots * p.gpad * 4);
+  p.off_partial = off;
+  off = align256(off + (p.Sg > 1 ? (uint64_t)p.Sg * kb * p.rows_pad * 4 : 0));
+  p.total = off;
+  return p;
+}
+
+void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x, int64_t M,
+                 int rotate, uint8_t* ws, hipStream_t st) {
+  uint32_t* frag = reinterpret_cast<uint32_t*>(ws);
+  int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
+  float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
+  const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
+  if (d->format == BGG_FMT_PQ2_0)
+    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(kPrepThreads), 0, st, x, d->K, (int)M,
+                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
+  else
+    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(kPrepThreads), 0, st, x, d->K,
+                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
+}
+
+// GEMV (+ reduce) over all weight rows for tokens m0 .. m0+Mreal-1.
+template <int M>
+void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
+                 uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, hipStream_t st) {
+  const uint32_t* frag = reinterpret_cast<const uint32_t*>(ws) + m0 * p.frag_words_per_token;
+  const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
+  const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f) + m0 * p.gpad;
+  float* part = reinterpret_cast<float*>(ws + p.off_partial);
+  uint16_t* yg = y + m0 * d->N;
+  const int Sg = (int)p.Sg;
+  const dim3 grid((unsigned)(p.NT * Sg));
+  const dim3 block((unsigned)(64 * p.W));
+  if (d->format == BGG_FMT_PQ2_0) {
+#define BGG_PQ2(BPS)                                                                              \
+  hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
+                     d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
+                     p.gpad, part, p.rows_pad, yg)
+    switch (p.per_slice) {
+      case 8: BGG_PQ2(8); break;
+      case 5: BGG_PQ2(5); break;
+      case 4: BGG_PQ2(4); break;
+      default: BGG_PQ2(2); break;
+    }
+#undef BGG_PQ2
+  } else {
+#define BGG_PTQ1(PPS)                                                                             \
+  hipLaunchKernelGGL((k_gemv_ptq1<M, PPS, 8>), grid, block, 0, st, packed, d->scale_offset,      \
+                     d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
+                     p.gpad, part, p.rows_pad, yg)
+    if (p.per_slice == 2)
+      BGG_PTQ1(2);
+    else
+      BGG_PTQ1(1);
+#undef BGG_PTQ1
+  }
+  if (Sg > 1)
+    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(Mreal * d->N, 256)), dim3(256), 0, st,
+                       part, Sg, M, Mreal, p.rows_pad, d->N, yg);
+}
+
+bgg_status gemv_args_check(const char* who, const bgg_weights_desc* d, int64_t M,
+                           const void* workspace, size_t workspace_bytes, GemvPlan* plan) {
+  bgg_status st = check_desc(d);
+  if (st) return st;
+  if (!workspace) return fail(BGG_ERR_NULL, "%s: NULL workspace", who);
+  if (M < 1 || M > BGG_MAX_GEMV_M)
+    return fail(BGG_ERR_SHAPE, "%s: M must be in 1..16 (got %lld)", who, (long long)M);
+  if (!aligned16(workspace)) return fail(BGG_ERR_BUFFER, "%s: misaligned workspace", who);
+  *plan = plan_gemv(d, M);
+  if (workspace_bytes < plan->total)
+    return fail(BGG_ERR_BUFFER, "%s: workspace has %zu bytes, needs %llu", who, workspace_bytes,
+                (unsigned long long)plan->total);
+  return BGG_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t bgg_gemv_workspace_size(const bgg_weights_desc* d, int64_t M) {
+  if (check_desc(d) != BGG_OK || M < 1 || M > BGG_MAX_GEMV_M) return 0;
+  return (size_t)plan_gemv(d, M).total;
+}
+
+bgg_status bgg_gemv_prepare(const bgg_weights_desc* d, const void* x_dev, int64_t M, uint32_t flags,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  GemvPlan p;
+  bgg_status st = gemv_args_check("bgg_gemv_prepare", d, M, workspace, workspace_bytes, &p);
+  if (st) return st;
+  if (!x_dev) return fail(BGG_ERR_NULL, "bgg_gemv_prepare: NULL x");
+  if (!aligned16(x_dev)) return fail(BGG_ERR_BUFFER, "bgg_gemv_prepare: misaligned x");
+  if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
+    return fail(BGG_ERR_SHAPE, "bgg_gemv_prepare: unknown flags 0x%x", flags);
+  launch_prep(d, p, (const uint16_t*)x_dev, M, (flags & BGG_ROTATE_INPUT) ? 1 : 0,
+              (uint8_t*)workspace, (hipStream_t)stream);
+  return hip_check("bgg_gemv_prepare");
+}
+
+bgg_status bgg_gemv_run(const bgg_weights_desc* d, const void* packed_dev, void* y_dev, int64_t M,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  GemvPlan p;
+  bgg_status st = gemv_args_check("bgg_gemv_run", d, M, workspace, workspace_bytes, &p);
+  if (st) return st;
+  if (!packed_dev || !y_dev) return fail(BGG_ERR_NULL, "bgg_gemv_run: NULL buffer");
+  if (!aligned16(packed_dev) || ((uintptr_t)y_dev & 1))
+    return fail(BGG_ERR_BUFFER, "bgg_gemv_run: misaligned buffer");
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* pk = (const uint8_t*)packed_dev;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint16_t* y = (uint16_t*)y_dev;
+  for (int64_t m0 = 0; m0 < M; m0 += kGemvTokens) {
+    const int mg = (int)(M - m0 < kGemvTokens ? M - m0 : kGemvTokens);
+    switch (gemv_m_bucket(mg)) {
+      case 1: launch_gemv<1>(d, p, pk, y, m0, mg, ws, s); break;
+      case 2: launch_gemv<2>(d, p, pk, y, m0, mg, ws, s); break;
+      default: launch_gemv<4>(d, p, pk, y, m0, mg, ws, s); break;
+    }
+    if ((st = hip_check("bgg_gemv_run"))) return st;
+  }
+  return BGG_OK;
+}
+
+bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, const void* x_dev,
+                            void* y_dev, int64_t M, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  bgg_status st = check_desc(d);
+  if (st) return st;
+  if (!packed_dev || !y_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemv: NULL buffer");
+  if (!aligned16(packed_dev) || ((uintptr_t)y_dev & 1))
+    return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned buffer");
+  st = bgg_gemv_prepare(d, x_dev, M, flags, workspace, workspace_bytes, stream);
+  if (st) return st;
+  return bgg_gemv_run(d, packed_dev, y_dev, M, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -174,6 +174,7 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *   y_dev       device fp16 [M][N]
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
  *               bytes; its contents need no initialisation and are scratch.
+ * Equivalent to bgg_gemv_prepare followed by bgg_gemv_run.
  * Each 64-row tile is read once per call, all M tokens at a time.  The
  * activations are carried as 15-bit integers with a power-of-two scale per
  * 128-block (absolute error at most 2^-14 of the block's largest |x'|), the
@@ -185,6 +186,26 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
 bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev,
                             const void* x_dev, void* y_dev, int64_t M, uint32_t flags,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of bgg_ternary_gemv, for projections that share an input
+ * (q, k and v, or gate and up, read the same x).
+ *
+ * bgg_gemv_prepare: transform (with BGG_ROTATE_INPUT) and encode the M
+ * activation rows x_dev (fp16 [M][K]) into `workspace`.  What it writes
+ * depends only on the format, K and M of `desc`.
+ *
+ * bgg_gemv_run: y_dev (fp16 [M][N]) = the product of the packed matrix with
+ * the activations last prepared in `workspace` (stream order).  Any matrix
+ * whose descriptor has the same format and K may use one preparation, as
+ * long as the workspace is at least bgg_gemv_workspace_size of that matrix;
+ * runs that share a workspace must not overlap in time.
+ * Errors of both: as bgg_ternary_gemv.
+ */
+bgg_status bgg_gemv_prepare(const bgg_weights_desc* desc, const void* x_dev, int64_t M,
+                            uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, void* y_dev,
+                        int64_t M, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace bytes that bgg_ternary_gemm needs for M tokens. */
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);

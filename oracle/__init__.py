@@ -61,6 +61,8 @@ def configure(lib):
     lib.oracle_unpack.argtypes = [ci, vp, i64, i64, vp]
     lib.oracle_matvec.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.oracle_linear.argtypes = [ci, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ci
     for f in (lib.oracle_sylvester, lib.oracle_rotate, lib.oracle_pack, lib.oracle_unpack,
               lib.oracle_matvec, lib.oracle_linear):
         f.restype = ci
@@ -105,6 +107,11 @@ def _f16bits(a) -> np.ndarray:
     if a.dtype == np.uint16:
         return a
     raise TypeError("expected float16 (or its uint16 bits)")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def f16_to_f64(bits: int) -> float:

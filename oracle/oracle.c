@@ -210,3 +210,15 @@ int oracle_linear(int fmt, const uint8_t* packed, const uint16_t* S, const uint1
   free(xr);
   return rc;
 }
+
+/* Threads the OpenMP loops above run on (for reporting only). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

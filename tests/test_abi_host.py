@@ -189,3 +189,12 @@ def test_null_pointers_are_errors_not_crashes():
     dp = bgg.bgg_describe("PTQ1_0", 64, 128)
     lib.bgg_ternary_gemm.argtypes = lib.bgg_ternary_gemv.argtypes
     assert lib.bgg_ternary_gemm(ctypes.addressof(dp), 16, 16, 16, 4, 0, None, 0, None) == 2
+
+
+def test_one_hip_runtime_in_the_process():
+    """libbgg.so binds to the HIP runtime PyTorch loaded (two runtimes with
+    one soname in one process break PyTorch's device calls)."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(hip) == 1, hip

@@ -329,3 +329,29 @@ def test_gemm_prefill_full_size_sampled(env, name):
     e = relerr(y[rows], ref)
     say(f"  rel err max {e.max():.3g}")
     assert np.all(e <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_shared_preparation(env, fmt):
+    """q, k and v read the same input: one prepare, three runs."""
+    bgg, torch = env
+    say(f"gemv shared prepare {fmt}")
+    K, M = 5120, 2
+    x = synth.activations_f16(81, 9, M, K)
+    mats = [(6144, 1), (1024, 2), (1024, 3)]
+    devs = []
+    for N, mid in mats:
+        T, S = gen_matrix(81, mid, N, K)
+        devs.append((Dev(bgg, torch, fmt, T, S), T, S))
+    wsb = max(bgg.bgg_gemv_workspace_size(d.desc, M) for d, _, _ in devs)
+    ws = bgg.workspace(wsb)
+    xd = torch.from_numpy(x).cuda()
+    bgg.bgg_gemv_prepare(devs[0][0].desc, xd, M, bgg.BGG_ROTATE_INPUT, ws)
+    outs = []
+    for d, T, S in devs:
+        yd = torch.empty((M, d.N), dtype=torch.float16, device="cuda")
+        bgg.bgg_gemv_run(d.desc, d.packed, yd, M, ws)
+        outs.append(yd)
+    torch.cuda.synchronize()
+    for (d, T, S), yd in zip(devs, outs):
+        assert np.all(relerr(yd.cpu().numpy(), oracle_y(fmt, T, S, x)) <= TOL)
