@@ -113,14 +113,23 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
   }
 }
 
-// The GEMV's LUT: 256 entries x 64 copies (64 KiB).  Entry e of copy c is
-// the word at byte address e * 256 + c * 4, so lane l reads copy l and the
-// address of byte j of a packed word w is one v_perm_b32:
-//   byte 0 = l * 4 (from lane_off), byte 1 = byte j of w, bytes 2-3 = 0.
+// The GEMV's LUT holds the trits themselves, t = c - 1 as signed 4-bit
+// nibbles (-1 = 0xF), five to a word: 256 entries x 64 copies (64 KiB).
+// Entry e of copy c is the word at byte address e * 256 + c * 4, so lane l
+// reads copy l and the address of byte j of a packed word w is one
+// v_perm_b32: byte 0 = l * 4 (from lane_off), byte 1 = byte j of w,
+// bytes 2-3 = 0.
 constexpr int kLut64Copies = 64;
+__device__ __forceinline__ uint32_t ptq1_trit_nibbles(uint32_t b) {
+  const uint32_t c = ptq1_entry(b);
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t |= ((((c >> (4 * i)) & 15u) + 15u) & 15u) << (4 * i);
+  return t;
+}
 __device__ __forceinline__ void build_lut64(uint32_t* lut) {
   for (int i = threadIdx.x; i < 256 * (kLut64Copies / 4); i += blockDim.x) {
-    const uint32_t e = ptq1_entry((uint32_t)(i / (kLut64Copies / 4)));
+    const uint32_t e = ptq1_trit_nibbles((uint32_t)(i / (kLut64Copies / 4)));
     reinterpret_cast<uint4*>(lut)[i] = make_uint4(e, e, e, e);
   }
 }

@@ -268,33 +268,88 @@ __global__ void __launch_bounds__(64 * W)
 }
 
 // ---------------------------------------------------------------------------
-// PTQ1_0: wave = 64 rows x PPS periods (5 groups each); workgroup = W
-// consecutive K slices sharing one 64-copy LUT.
+// PTQ1_0: wave = 64 rows x one part of one period (a period is 5 groups =
+// 128 row bytes, cut into H parts); workgroup = W consecutive parts of one
+// tile sharing a 64-copy LUT.
+//
+// The LUT yields the trits t themselves as signed nibbles, so a group's
+// integer sum is sum t*q directly (no digit-sum correction), and a group
+// cut by a part boundary is finished by each part for its own trits.
 // ---------------------------------------------------------------------------
 template <int M>
 __device__ __forceinline__ void ptq1_close(int (&a)[M][4], float (&acc)[M], const float (&gf)[M],
-                                           const int (&gq)[M], float s) {
+                                           float s) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int p = a[m][0] + (a[m][1] << 4) + (a[m][2] << 8) + (a[m][3] << 12) - gq[m];
+    const int p = a[m][0] + (a[m][1] << 4) + (a[m][2] << 8) + (a[m][3] << 12);
     acc[m] = fmaf(s * gf[m], (float)p, acc[m]);
 #pragma unroll
     for (int L = 0; L < 4; ++L) a[m][L] = 0;
   }
 }
 
-template <int J>
-__device__ __forceinline__ uint32_t word_of(const uint4& c) {
-  return J == 0 ? c.x : J == 1 ? c.y : J == 2 ? c.z : c.w;
+// Bytes [B0, B0 + 128/H) of one period for all M tokens.
+template <int M, int H, int PART>
+__device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (&sc)[kPeriodGroups],
+                                          const float (&gf)[kPeriodGroups][M],
+                                          const uint32_t* __restrict__ fp, int64_t fwpt,
+                                          const char* lbase, uint32_t lane_off, float (&acc)[M]) {
+  constexpr int BP = kPeriodBytes / H, B0 = PART * BP, B1 = B0 + BP;
+  int a[M][4];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int L = 0; L < 4; ++L) a[m][L] = 0;
+#pragma clang loop unroll(full)
+  for (int jb = B0; jb < B1; ++jb) {
+    const uint4& ch = w[(jb - B0) >> 4];
+    const uint32_t word = (jb >> 2 & 3) == 0 ? ch.x : (jb >> 2 & 3) == 1 ? ch.y
+                          : (jb >> 2 & 3) == 2 ? ch.z : ch.w;
+    uint32_t addr;
+    switch (jb & 3) {
+      case 0: addr = lut64_addr<0>(word, lane_off); break;
+      case 1: addr = lut64_addr<1>(word, lane_off); break;
+      case 2: addr = lut64_addr<2>(word, lane_off); break;
+      default: addr = lut64_addr<3>(word, lane_off); break;
+    }
+    const int codes = *reinterpret_cast<const int*>(lbase + addr);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t* f = fp + m * fwpt + jb * 4;
+#pragma unroll
+      for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
+    }
+    const int k_first = (5 * jb) / kGroup, k_last = (5 * jb + 4) / kGroup;
+    if (k_last != k_first) {
+      // this byte's trits cross a group end: close the lower group and
+      // start the next one with the byte's upper trits
+      ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint32_t* f = fp + m * fwpt + kPeriodBytes * 4 + k_first * 4;
+#pragma unroll
+        for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
+      }
+    } else if ((5 * jb + 5) % kGroup == 0) {
+      ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
+    }
+  }
+  // a group still open at the part's end is finished here for this part
+  constexpr int last = B1 - 1;
+  if ((5 * last + 5) % kGroup != 0) {
+    constexpr int k = (5 * last + 4) / kGroup;
+    ptq1_close<M>(a, acc, gf[k], sc[k]);
+  }
 }
 
-template <int M, int PPS, int W>
+template <int M, int H, int W>
 __global__ void __launch_bounds__(64 * W)
     k_gemv_ptq1(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
                 int64_t rows_pad, uint16_t* __restrict__ y) {
+  constexpr int CH = kPeriodChunks / H;  // chunks per part
   __shared__ uint32_t lut[256 * kLut64Copies];
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
@@ -302,30 +357,28 @@ __global__ void __launch_bounds__(64 * W)
   const int64_t tile = blockIdx.x / Sg;
   const int wgs = (int)(blockIdx.x % Sg);
   const int64_t P = ceil_div(G, kPeriodGroups);
-  const int64_t pbeg = ((int64_t)wgs * W + wave) * PPS;
-  const bool active = pbeg < P;
+  const int64_t item = (int64_t)wgs * W + wave;  // (period, part) of this wave
+  const int64_t p = item / H;
+  const int part = (int)(item % H);
+  const bool active = p < P;
   const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
   const uint16_t* sdata =
       reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile + lane;
-  // All loads of the slice first -- before the LUT is built, so they are in
-  // flight meanwhile -- and branch-free: chunks past the row and groups past
-  // G re-read the last valid one and are zeroed / weighted 0 below.
-  uint4 wall[PPS][kPeriodChunks];
-  uint16_t scall[PPS][kPeriodGroups];
+  // The part's loads first -- before the LUT is built, so they are in flight
+  // meanwhile -- and branch-free: chunks past the row and groups past G
+  // re-read the last valid one and are zeroed / weighted 0 below.
+  uint4 w[CH];
+  uint16_t sr[kPeriodGroups];
   if (active) {
 #pragma unroll
-    for (int pp = 0; pp < PPS; ++pp) {
-      const int64_t p = pbeg + pp;
+    for (int c = 0; c < CH; ++c) {
+      const int64_t j = p * kPeriodChunks + part * CH + c;
+      w[c] = ld_stream(tdata + (j < C ? j : C - 1) * kTile);
+    }
 #pragma unroll
-      for (int c = 0; c < kPeriodChunks; ++c) {
-        const int64_t j = p * kPeriodChunks + c;
-        wall[pp][c] = ld_stream(tdata + (j < C ? j : C - 1) * kTile);
-      }
-#pragma unroll
-      for (int k = 0; k < kPeriodGroups; ++k) {
-        const int64_t g = p * kPeriodGroups + k;
-        scall[pp][k] = sdata[(g < G ? g : G - 1) * kTile];
-      }
+    for (int k = 0; k < kPeriodGroups; ++k) {
+      const int64_t g = p * kPeriodGroups + k;
+      sr[k] = sdata[(g < G ? g : G - 1) * kTile];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -337,72 +390,36 @@ __global__ void __launch_bounds__(64 * W)
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
   if (active) {
+    const int64_t gp = p * kPeriodGroups;
+    if (p * kPeriodChunks + (part + 1) * CH > C) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (p * kPeriodChunks + part * CH + c >= C) w[c] = make_uint4(0, 0, 0, 0);
+    }
+    // group scales (zero past G) and the activations' group meta
+    float sc[kPeriodGroups], gf[kPeriodGroups][M];
+#pragma unroll
+    for (int k = 0; k < kPeriodGroups; ++k) {
+      sc[k] = gp + k < G ? h2f(sr[k]) : 0.0f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
+    }
+    const uint32_t* fp = frag + p * kPtqFragWords;
     const uint32_t lane_off = (uint32_t)lane * 4u;
     const char* lbase = reinterpret_cast<const char*>(lut);
-
-    int a[M][4];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int L = 0; L < 4; ++L) a[m][L] = 0;
-
-#pragma unroll
-    for (int pp = 0; pp < PPS; ++pp) {
-      const int64_t p = pbeg + pp;
-      if (p >= P) break;
-      const int64_t gp = p * kPeriodGroups;
-      uint4 w[kPeriodChunks];
-#pragma unroll
-      for (int c = 0; c < kPeriodChunks; ++c)
-        w[c] = p * kPeriodChunks + c < C ? wall[pp][c] : make_uint4(0, 0, 0, 0);
-      // group scales (zero past G) and the activations' group meta
-      float sc[kPeriodGroups], gf[kPeriodGroups][M];
-      int gq[kPeriodGroups][M];
-#pragma unroll
-      for (int k = 0; k < kPeriodGroups; ++k) {
-        const bool gv = gp + k < G;
-        sc[k] = gv ? h2f(scall[pp][k]) : 0.0f;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
-          gq[k][m] = metaQ[(int64_t)m * gpad + gp + k];
-        }
-      }
-      const uint32_t* fp = frag + p * kPtqFragWords;
-      // fully unrolled: byte positions, group ends and straddles are constants
-#pragma clang loop unroll(full)
-      for (int jb = 0; jb < kPeriodBytes; ++jb) {
-        const uint32_t word = (jb >> 2 & 3) == 0 ? w[jb >> 4].x
-                              : (jb >> 2 & 3) == 1 ? w[jb >> 4].y
-                              : (jb >> 2 & 3) == 2 ? w[jb >> 4].z : w[jb >> 4].w;
-        uint32_t addr;
-        switch (jb & 3) {
-          case 0: addr = lut64_addr<0>(word, lane_off); break;
-          case 1: addr = lut64_addr<1>(word, lane_off); break;
-          case 2: addr = lut64_addr<2>(word, lane_off); break;
-          default: addr = lut64_addr<3>(word, lane_off); break;
-        }
-        const int codes = *reinterpret_cast<const int*>(lbase + addr);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const uint32_t* f = fp + m * frag_words_per_token + jb * 4;
-#pragma unroll
-          for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
-        }
-        const int k_first = (5 * jb) / kGroup, k_last = (5 * jb + 4) / kGroup;
-        if (k_last != k_first) {
-          // this byte's trits cross a group end: close the lower group and
-          // start the next one with the byte's upper trits
-          ptq1_close<M>(a, acc, gf[k_first], gq[k_first], sc[k_first]);
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint32_t* f = fp + m * frag_words_per_token + kPeriodBytes * 4 + k_first * 4;
-#pragma unroll
-            for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
-          }
-        } else if ((5 * jb + 5) % kGroup == 0) {
-          ptq1_close<M>(a, acc, gf[k_first], gq[k_first], sc[k_first]);
-        }
+    if (H == 1) {
+      ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
+    } else if (H == 2) {
+      if (part == 0)
+        ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
+      else
+        ptq1_part<M, H, (H > 1 ? 1 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
+    } else {
+      switch (part) {
+        case 0: ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
+        case 1: ptq1_part<M, H, (H > 1 ? 1 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
+        case 2: ptq1_part<M, H, (H > 2 ? 2 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
+        default: ptq1_part<M, H, (H > 3 ? 3 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
       }
     }
   }
@@ -454,6 +471,7 @@ struct GemvPlan {
 GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   static const int64_t target = env_int("BGG_GEMV_TARGET_WAVES", 2048);
   static const int64_t min_single = env_int("BGG_GEMV_MIN_WAVES", 1024);
+  static const int64_t ptq1_target = env_int("BGG_GEMV_PTQ1_WAVES", 4096);
   GemvPlan p{};
   p.G = d->groups;
   p.NT = d->row_tiles;
@@ -479,14 +497,20 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
       while (p.per_slice > 2 && p.NT * p.W * ceil_div(ceil_div(p.units, p.per_slice), p.W) < target)
         p.per_slice /= 2;
     }
+    p.S = ceil_div(p.units, p.per_slice);
   } else {
+    // units are period parts: H parts per period, H in {1, 2, 4}, the
+    // fewest that give the target wave count; 16 waves per workgroup (8 for
+    // four tokens, whose kernel needs more registers)
     const int64_t P = ceil_div(p.G, kPeriodGroups);
     p.gpad = P * kPeriodGroups;
-    p.units = P;
     p.frag_words_per_token = P * kPtqFragWords;
-    p.per_slice = (p.NT * P >= 2 * target) ? 2 : 1;
+    p.W = gemv_m_bucket(M) >= 4 ? 8 : 16;  // every token group of this M runs with p.W
+    p.per_slice = 1;
+    while (p.per_slice < 4 && p.NT * P * p.per_slice < ptq1_target) p.per_slice *= 2;
+    p.units = P * p.per_slice;
+    p.S = p.units;
   }
-  p.S = ceil_div(p.units, p.per_slice);
   p.Sg = ceil_div(p.S, p.W);
   const int64_t kb = gemv_m_bucket(M);
   uint64_t off = align256((uint64_t)p.slots * p.frag_words_per_token * 4);
@@ -539,14 +563,26 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
     }
 #undef BGG_PQ2
   } else {
-#define BGG_PTQ1(PPS)                                                                             \
-  hipLaunchKernelGGL((k_gemv_ptq1<M, PPS, 8>), grid, block, 0, st, packed, d->scale_offset,      \
+    // 16-wave workgroups only for the one- and two-token kernels (register
+    // budget); p.W says which one the plan was made for
+    constexpr int W16 = M >= 4 ? 8 : 16;
+#define BGG_PTQ1(H, WW)                                                                           \
+  hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
                      p.gpad, part, p.rows_pad, yg)
-    if (p.per_slice == 2)
-      BGG_PTQ1(2);
-    else
-      BGG_PTQ1(1);
+    if (p.W == 16) {
+      switch (p.per_slice) {
+        case 4: BGG_PTQ1(4, W16); break;
+        case 2: BGG_PTQ1(2, W16); break;
+        default: BGG_PTQ1(1, W16); break;
+      }
+    } else {
+      switch (p.per_slice) {
+        case 4: BGG_PTQ1(4, 8); break;
+        case 2: BGG_PTQ1(2, 8); break;
+        default: BGG_PTQ1(1, 8); break;
+      }
+    }
 #undef BGG_PTQ1
   }
   if (Sg > 1)
