@@ -27,6 +27,19 @@ __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
 }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// The fp16 scale of lane `lane` from a row of 64 scales at p: each lane reads
+// the aligned 32-bit word holding its scale and its neighbour's (neighbouring
+// lanes read the same word; the access stays one coalesced 256-byte read) and
+// keeps its half later with scale_half().  A 16-bit load would let the
+// compiler pack two scales into one register right after the loads, which
+// makes the wave wait for every load issued before them at that point.
+__device__ __forceinline__ uint32_t ld_scale_pair(const uint16_t* row64, int lane) {
+  return reinterpret_cast<const uint32_t*>(row64)[lane >> 1];
+}
+__device__ __forceinline__ float scale_half(uint32_t pair, int lane) {
+  return h2f((uint16_t)(pair >> ((lane & 1) * 16)));
+}
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 // 1/sqrt(128) rounded to fp32.
@@ -127,12 +140,23 @@ __device__ __forceinline__ uint32_t ptq1_trit_nibbles(uint32_t b) {
   for (int i = 0; i < 5; ++i) t |= ((((c >> (4 * i)) & 15u) + 15u) & 15u) << (4 * i);
   return t;
 }
-__device__ __forceinline__ void build_lut64(uint32_t* lut) {
+// Built in two steps: the first 256 threads each decode one byte value into
+// seed[], then (after a barrier) every thread copies entries out, 16 bytes
+// per store.  Needs blockDim.x >= 256; the caller synchronises afterwards.
+__device__ __forceinline__ void build_lut64(uint32_t* lut, uint32_t* seed) {
+  if (threadIdx.x < 256) seed[threadIdx.x] = ptq1_trit_nibbles(threadIdx.x);
+  __syncthreads();
   for (int i = threadIdx.x; i < 256 * (kLut64Copies / 4); i += blockDim.x) {
-    const uint32_t e = ptq1_trit_nibbles((uint32_t)(i / (kLut64Copies / 4)));
+    const uint32_t e = seed[i / (kLut64Copies / 4)];
     reinterpret_cast<uint4*>(lut)[i] = make_uint4(e, e, e, e);
   }
 }
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone (gfx9 encoding:
+// vmcnt 63, expcnt 7).  LDS reads and scalar loads share this counter and
+// scalar loads may return out of order, so a kernel that wants its scalar
+// loads to overlap LDS work waits for both explicitly at the point it picks.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 template <int J>
 __device__ __forceinline__ uint32_t lut64_addr(uint32_t word, uint32_t lane_off) {
   return __builtin_amdgcn_perm(word, lane_off, 0x0C0C0000u | ((4u + J) << 8));

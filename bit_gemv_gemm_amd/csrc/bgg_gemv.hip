@@ -41,6 +41,11 @@ constexpr int kPqFragWords = 32;
 // of each of the 4 bytes that straddle a group end.
 constexpr int kPtqFragWords = kPeriodBytes * 4 + 4 * 4;  // 528
 
+// Token counts one GEMV kernel handles at once; a larger M runs in groups of
+// kGemvTokens tokens (each group reads the weights again).
+constexpr int kGemvTokens = 4;
+__host__ __device__ inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
+
 constexpr int kPrepGroups = 5;  // groups per prep workgroup (one PTQ1_0 period)
 constexpr int kPrepThreads = kPrepGroups * 16;
 
@@ -118,19 +123,27 @@ __global__ void __launch_bounds__(kPrepThreads)
       out[c * kPqFragWords + r] = word;
     }
   } else {
-    // one period, 528 words.  Word (byte jb, L), jb < 128: nibble i = digit L
-    // of q at period position 5 jb + i, kept only if that position is in the
-    // same group as 5 jb.  Word 512 + 4 s + L: the upper part of the s-th
-    // straddling byte (positions in the next group).
+    // one period, 528 words per token.  Word (byte jb, L), jb < 128: nibble
+    // i = digit L of q at period position 5 jb + i, kept only if that
+    // position is in the same group as 5 jb.  Word (128 + s, L): the upper
+    // part of the s-th straddling byte (positions in the next group).
+    // Tokens are interleaved within their GEMV token group of b slots
+    // (b = 1, 2 or 4): word (r, L) of slot t sits at (r b + t) 4 + L, so the
+    // words one wave needs for a few consecutive bytes are contiguous.
+    const int tg = m / kGemvTokens, slot = m % kGemvTokens;
+    const int b = gemv_m_bucket(Mreal - tg * kGemvTokens < kGemvTokens ? Mreal - tg * kGemvTokens
+                                                                       : kGemvTokens);
+    if (slot >= b) return;  // a slot no GEMV token group reads
+    out = frag + (int64_t)tg * kGemvTokens * frag_words_per_token;
     const int64_t p = g0 / kPeriodGroups;
     for (int w = tid; w < kPtqFragWords; w += kPrepThreads) {
       int jb, upper;
-      const int L = w & 3;
-      if (w < kPeriodBytes * 4) {
-        jb = w >> 2, upper = 0;
+      const int L = w & 3, r = w >> 2;
+      if (r < kPeriodBytes) {
+        jb = r, upper = 0;
       } else {
         // the bytes whose five trits cross a group end: 25, 51, 76, 102
-        jb = (kGroup * (((w - kPeriodBytes * 4) >> 2) + 1)) / 5, upper = 1;
+        jb = (kGroup * (r - kPeriodBytes + 1)) / 5, upper = 1;
       }
       const int first_group = (5 * jb) / kGroup;
       uint32_t word = 0;
@@ -140,7 +153,7 @@ __global__ void __launch_bounds__(kPrepThreads)
         if (pos / kGroup == first_group + upper)
           word |= ((uint32_t)(sd[pos] >> (4 * L)) & 15u) << (4 * i);
       }
-      out[p * kPtqFragWords + w] = word;
+      out[p * kPtqFragWords * b + (r * b + slot) * 4 + L] = word;
     }
   }
 }
@@ -198,17 +211,17 @@ __global__ void __launch_bounds__(64 * W)
   if (gbeg < G) {
     const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
     const uint16_t* sdata =
-        reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile + lane;
+        reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
     // Every load of the slice is issued before any is used, without branches
     // (a group past G re-reads group G-1 and gets a zero weight below).
     uint4 w[2 * BPS];
-    uint16_t sc[BPS];
+    uint32_t sc[BPS];
 #pragma unroll
     for (int i = 0; i < BPS; ++i) {
       const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
       w[2 * i] = ld_stream(tdata + (2 * g) * kTile);
       w[2 * i + 1] = ld_stream(tdata + (2 * g + 1) * kTile);
-      sc[i] = sdata[g * kTile];
+      sc[i] = ld_scale_pair(sdata + g * kTile, lane);
     }
     // per-group activation scale and digit sum, for every token
     float gf[BPS][M];
@@ -228,7 +241,7 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
     for (int i = 0; i < BPS; ++i) {
       const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
-      const float s = h2f(sc[i]);
+      const float s = scale_half(sc[i], lane);
       uint32_t E[8], O[8];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -289,49 +302,87 @@ __device__ __forceinline__ void ptq1_close(int (&a)[M][4], float (&acc)[M], cons
 }
 
 // Bytes [B0, B0 + 128/H) of one period for all M tokens.
+//
+// Software pipeline over batches of BB = 4/M bytes (16 digit words): the LUT
+// reads and digit-word loads of batch b+1 are issued, then batch b is
+// computed, then both are awaited.  Without the explicit wait the compiler
+// waits for everything at the first use of batch b, i.e. right after issuing
+// batch b+1, and the scalar-load latency is paid once per batch.
 template <int M, int H, int PART>
 __device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (&sc)[kPeriodGroups],
                                           const float (&gf)[kPeriodGroups][M],
-                                          const uint32_t* __restrict__ fp, int64_t fwpt,
-                                          const char* lbase, uint32_t lane_off, float (&acc)[M]) {
+                                          const uint32_t* __restrict__ fp, const char* lbase, uint32_t lane_off, float (&acc)[M]) {
   constexpr int BP = kPeriodBytes / H, B0 = PART * BP, B1 = B0 + BP;
+  constexpr int BB = 4 / M, NB = BP / BB;
+  static_assert(BP % BB == 0, "batch size");
   int a[M][4];
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int L = 0; L < 4; ++L) a[m][L] = 0;
-#pragma clang loop unroll(full)
-  for (int jb = B0; jb < B1; ++jb) {
-    const uint4& ch = w[(jb - B0) >> 4];
-    const uint32_t word = (jb >> 2 & 3) == 0 ? ch.x : (jb >> 2 & 3) == 1 ? ch.y
-                          : (jb >> 2 & 3) == 2 ? ch.z : ch.w;
-    uint32_t addr;
-    switch (jb & 3) {
-      case 0: addr = lut64_addr<0>(word, lane_off); break;
-      case 1: addr = lut64_addr<1>(word, lane_off); break;
-      case 2: addr = lut64_addr<2>(word, lane_off); break;
-      default: addr = lut64_addr<3>(word, lane_off); break;
-    }
-    const int codes = *reinterpret_cast<const int*>(lbase + addr);
+
+  uint32_t lv[2][BB];           // LUT words of the batch's bytes
+  uint32_t fr[2][BB][M][4];     // digit words of the batch's bytes
+  uint32_t up[2][M][4];         // digit words of a straddling byte's upper trits
+  auto issue = [&](int nb, int buf) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint32_t* f = fp + m * fwpt + jb * 4;
-#pragma unroll
-      for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
-    }
-    const int k_first = (5 * jb) / kGroup, k_last = (5 * jb + 4) / kGroup;
-    if (k_last != k_first) {
-      // this byte's trits cross a group end: close the lower group and
-      // start the next one with the byte's upper trits
-      ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint32_t* f = fp + m * fwpt + kPeriodBytes * 4 + k_first * 4;
-#pragma unroll
-        for (int L = 0; L < 4; ++L) a[m][L] = __builtin_amdgcn_sdot8(codes, (int)f[L], a[m][L], false);
+    for (int j = 0; j < BB; ++j) {
+      const int jb = B0 + nb * BB + j;
+      const uint4& ch = w[(jb - B0) >> 4];
+      const uint32_t word = (jb >> 2 & 3) == 0 ? ch.x : (jb >> 2 & 3) == 1 ? ch.y
+                            : (jb >> 2 & 3) == 2 ? ch.z : ch.w;
+      uint32_t addr;
+      switch (jb & 3) {
+        case 0: addr = lut64_addr<0>(word, lane_off); break;
+        case 1: addr = lut64_addr<1>(word, lane_off); break;
+        case 2: addr = lut64_addr<2>(word, lane_off); break;
+        default: addr = lut64_addr<3>(word, lane_off); break;
       }
-    } else if ((5 * jb + 5) % kGroup == 0) {
-      ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
+      lv[buf][j] = *reinterpret_cast<const uint32_t*>(lbase + addr);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int L = 0; L < 4; ++L) fr[buf][j][m][L] = fp[(jb * M + m) * 4 + L];
+      const int k_first = (5 * jb) / kGroup;
+      if ((5 * jb + 4) / kGroup != k_first) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int L = 0; L < 4; ++L) up[buf][m][L] = fp[(kPeriodBytes * M + k_first * M + m) * 4 + L];
+      }
+    }
+  };
+
+  issue(0, 0);
+#pragma clang loop unroll(full)
+  for (int nb = 0; nb < NB; ++nb) {
+    const int buf = nb & 1;
+    wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+    if (nb + 1 < NB) issue(nb + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < BB; ++j) {
+      const int jb = B0 + nb * BB + j;
+      const int codes = (int)lv[buf][j];
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int L = 0; L < 4; ++L)
+          a[m][L] = __builtin_amdgcn_sdot8(codes, (int)fr[buf][j][m][L], a[m][L], false);
+      const int k_first = (5 * jb) / kGroup, k_last = (5 * jb + 4) / kGroup;
+      if (k_last != k_first) {
+        // this byte's trits cross a group end: close the lower group and
+        // start the next one with the byte's upper trits
+        ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int L = 0; L < 4; ++L)
+            a[m][L] = __builtin_amdgcn_sdot8(codes, (int)up[buf][m][L], a[m][L], false);
+      } else if ((5 * jb + 5) % kGroup == 0) {
+        ptq1_close<M>(a, acc, gf[k_first], sc[k_first]);
+      }
     }
   }
   // a group still open at the part's end is finished here for this part
@@ -350,7 +401,9 @@ __global__ void __launch_bounds__(64 * W)
                 const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
                 int64_t rows_pad, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
+  static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
   __shared__ uint32_t lut[256 * kLut64Copies];
+  __shared__ uint32_t lut_seed[256];
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -363,26 +416,30 @@ __global__ void __launch_bounds__(64 * W)
   const bool active = p < P;
   const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
   const uint16_t* sdata =
-      reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile + lane;
+      reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
   // The part's loads first -- before the LUT is built, so they are in flight
   // meanwhile -- and branch-free: chunks past the row and groups past G
-  // re-read the last valid one and are zeroed / weighted 0 below.
+  // re-read the last valid one.  Their trits meet digit words that are zero
+  // (the prep writes zeros for positions past K) and scales set to 0 below,
+  // so they add nothing, and no use of the loaded words has to wait for all
+  // of them.
   uint4 w[CH];
-  uint16_t sr[kPeriodGroups];
+  uint32_t sr[kPeriodGroups];
   if (active) {
+    // scales first: all of them are needed before the first byte
+#pragma unroll
+    for (int k = 0; k < kPeriodGroups; ++k) {
+      const int64_t g = p * kPeriodGroups + k;
+      sr[k] = ld_scale_pair(sdata + (g < G ? g : G - 1) * kTile, lane);
+    }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t j = p * kPeriodChunks + part * CH + c;
       w[c] = ld_stream(tdata + (j < C ? j : C - 1) * kTile);
     }
-#pragma unroll
-    for (int k = 0; k < kPeriodGroups; ++k) {
-      const int64_t g = p * kPeriodGroups + k;
-      sr[k] = sdata[(g < G ? g : G - 1) * kTile];
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  build_lut64(lut);
+  build_lut64(lut, lut_seed);
   __syncthreads();
 
   float acc[M];
@@ -391,37 +448,22 @@ __global__ void __launch_bounds__(64 * W)
 
   if (active) {
     const int64_t gp = p * kPeriodGroups;
-    if (p * kPeriodChunks + (part + 1) * CH > C) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (p * kPeriodChunks + part * CH + c >= C) w[c] = make_uint4(0, 0, 0, 0);
-    }
     // group scales (zero past G) and the activations' group meta
     float sc[kPeriodGroups], gf[kPeriodGroups][M];
 #pragma unroll
     for (int k = 0; k < kPeriodGroups; ++k) {
-      sc[k] = gp + k < G ? h2f(sr[k]) : 0.0f;
+      sc[k] = gp + k < G ? scale_half(sr[k], lane) : 0.0f;
 #pragma unroll
       for (int m = 0; m < M; ++m) gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
     }
-    const uint32_t* fp = frag + p * kPtqFragWords;
+    const uint32_t* fp = frag + p * kPtqFragWords * M;
     const uint32_t lane_off = (uint32_t)lane * 4u;
     const char* lbase = reinterpret_cast<const char*>(lut);
-    if (H == 1) {
-      ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
-    } else if (H == 2) {
-      if (part == 0)
-        ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
-      else
-        ptq1_part<M, H, (H > 1 ? 1 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc);
-    } else {
-      switch (part) {
-        case 0: ptq1_part<M, H, 0>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
-        case 1: ptq1_part<M, H, (H > 1 ? 1 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
-        case 2: ptq1_part<M, H, (H > 2 ? 2 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
-        default: ptq1_part<M, H, (H > 3 ? 3 : 0)>(w, sc, gf, fp, frag_words_per_token, lbase, lane_off, acc); break;
-      }
-    }
+    static_assert(H == 1 || H == 2, "one or two parts per period");
+    if (H == 1 || part == 0)
+      ptq1_part<M, H, 0>(w, sc, gf, fp, lbase, lane_off, acc);
+    else
+      ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
   }
   wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
                   y);
@@ -444,10 +486,6 @@ __global__ void __launch_bounds__(256)
 // ---------------------------------------------------------------------------
 // plan and launch
 // ---------------------------------------------------------------------------
-// Token counts one GEMV kernel handles at once; a larger M runs in groups of
-// kGemvTokens tokens (each group reads the weights again).
-constexpr int kGemvTokens = 4;
-inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 // Token slots of the prepared activations: padding tokens are zero.
 inline int64_t gemv_m_slots(int64_t M) {
   return M <= 2 ? M : ((M + kGemvTokens - 1) / kGemvTokens) * kGemvTokens;
@@ -471,7 +509,7 @@ struct GemvPlan {
 GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   static const int64_t target = env_int("BGG_GEMV_TARGET_WAVES", 2048);
   static const int64_t min_single = env_int("BGG_GEMV_MIN_WAVES", 1024);
-  static const int64_t ptq1_target = env_int("BGG_GEMV_PTQ1_WAVES", 4096);
+  static const int64_t ptq1_target = env_int("BGG_GEMV_PTQ1_WAVES", 2048);
   GemvPlan p{};
   p.G = d->groups;
   p.NT = d->row_tiles;
@@ -499,15 +537,20 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     }
     p.S = ceil_div(p.units, p.per_slice);
   } else {
-    // units are period parts: H parts per period, H in {1, 2, 4}, the
-    // fewest that give the target wave count; 16 waves per workgroup (8 for
-    // four tokens, whose kernel needs more registers)
+    // units are period parts: H parts per period, H = 2 only for one token
+    // and only when whole periods give fewer waves than the target (more
+    // parts mean more per-wave and per-workgroup overhead; for several
+    // tokens the digit words need the scalar registers); 8 waves per
+    // workgroup by default (16 measured slower: the LUT barrier waits for
+    // more waves)
     const int64_t P = ceil_div(p.G, kPeriodGroups);
     p.gpad = P * kPeriodGroups;
     p.frag_words_per_token = P * kPtqFragWords;
-    p.W = gemv_m_bucket(M) >= 4 ? 8 : 16;  // every token group of this M runs with p.W
+    static const int64_t ptq1_w = env_int("BGG_GEMV_PTQ1_W", 8) >= 16 ? 16 : 8;
+    p.W = gemv_m_bucket(M) >= 4 ? 8 : ptq1_w;  // every token group of this M runs with p.W
     p.per_slice = 1;
-    while (p.per_slice < 4 && p.NT * P * p.per_slice < ptq1_target) p.per_slice *= 2;
+    while (p.per_slice < 2 && gemv_m_bucket(M) == 1 && p.NT * P * p.per_slice < ptq1_target)
+      p.per_slice *= 2;
     p.units = P * p.per_slice;
     p.S = p.units;
   }
@@ -570,18 +613,11 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
   hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
                      p.gpad, part, p.rows_pad, yg)
+    constexpr int H2 = M == 1 ? 2 : 1;
     if (p.W == 16) {
-      switch (p.per_slice) {
-        case 4: BGG_PTQ1(4, W16); break;
-        case 2: BGG_PTQ1(2, W16); break;
-        default: BGG_PTQ1(1, W16); break;
-      }
+      if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
     } else {
-      switch (p.per_slice) {
-        case 4: BGG_PTQ1(4, 8); break;
-        case 2: BGG_PTQ1(2, 8); break;
-        default: BGG_PTQ1(1, 8); break;
-      }
+      if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
     }
 #undef BGG_PTQ1
   }
