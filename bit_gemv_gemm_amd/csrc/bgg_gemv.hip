@@ -24,8 +24,9 @@
 //     by s * 2^(e-14) and accumulated in fp32;
 //   * K is split over the eight waves of a workgroup (reduced in LDS, fixed
 //     order) and, when the tiles alone cannot fill the chip, over
-//     workgroups; those partial sums are added in slice order by a second,
-//     small kernel (deterministic, no atomics, no cache-flushing fences).
+//     workgroups; the last workgroup of a tile to finish adds their partial
+//     sums in slice order (deterministic, one launch, no cache-flushing
+//     fences, no waiting on other workgroups).
 #include "bgg_device.h"
 
 #include <cstdlib>
@@ -58,10 +59,17 @@ template <int FMT>
 __global__ void __launch_bounds__(kPrepThreads)
     k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
                 uint32_t* __restrict__ frag, int64_t frag_words_per_token,
-                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad) {
+                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad,
+                int* __restrict__ counters, int ncounters) {
   // the four 4-bit digits of every q of the workgroup's 640 positions
   __shared__ uint16_t sd[kPrepGroups * kGroup];
   const int tid = threadIdx.x;
+  {
+    const int nth = (int)(gridDim.x * gridDim.y) * kPrepThreads;
+    for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * kPrepThreads + tid; i < ncounters;
+         i += nth)
+      counters[i] = 0;
+  }
   const int m = blockIdx.y;
   const int64_t G = K / kGroup;
   const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
@@ -159,31 +167,62 @@ __global__ void __launch_bounds__(kPrepThreads)
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup end: the W waves' partial sums are added in wave order in LDS;
-// wave 0 writes y (when the workgroup covers all of K) or a partial row for
-// the reduce kernel.
+// Workgroup end: the W waves' partial sums are added in wave order in LDS and
+// wave 0 writes y when the workgroup covers all of K.  Otherwise (Sg
+// workgroups per tile) wave 0 stores its partial row, and the workgroup that
+// finishes the tile last -- found with a per-tile arrival counter -- adds the
+// Sg partial rows in slice order (the same order whoever arrives last, so the
+// result is deterministic), writes y and resets the counter to 0.
+//
+// Cross-workgroup visibility without cache-flushing fences: partial rows are
+// stored and read back with device-scope relaxed atomic accesses, which on
+// this chip bypass the per-XCD L2 (the L2s are not coherent with each other),
+// and each wave waits for its stores to complete before it counts itself in.
+// Nothing ever waits on another workgroup, so no schedule can hang.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 template <int M, int W>
 __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M][64], int wave,
                                           int lane, int64_t row, int64_t N, int Mreal, int Sg,
                                           int wgs, int64_t rows_pad, float* __restrict__ partial,
-                                          uint16_t* __restrict__ y) {
+                                          int* __restrict__ counter, uint16_t* __restrict__ y) {
 #pragma unroll
   for (int m = 0; m < M; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
   if (wave != 0) return;
+  float s[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float s = red[0][m][lane];
+    s[m] = red[0][m][lane];
 #pragma unroll
-    for (int w = 1; w < W; ++w) s += red[w][m][lane];
-    if (m < Mreal && row < N) {
-      if (Sg == 1)
-        y[(int64_t)m * N + row] = f2h(s);
-      else
-        partial[((int64_t)wgs * M + m) * rows_pad + row] = s;
-    }
+    for (int w = 1; w < W; ++w) s[m] += red[w][m][lane];
   }
+  if (Sg == 1) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h(s[m]);
+    return;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    __hip_atomic_store(&partial[((int64_t)wgs * M + m) * rows_pad + row], s[m], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  wait_vm0();  // this wave's partial row is in place before it is counted
+  int before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before != Sg - 1) return;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float t = 0.0f;
+    for (int k = 0; k < Sg; ++k)
+      t += __hip_atomic_load(&partial[((int64_t)k * M + m) * rows_pad + row], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h(t);
+  }
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,11 +235,12 @@ __global__ void __launch_bounds__(64 * W)
                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-               int64_t rows_pad, uint16_t* __restrict__ y) {
+               int64_t rows_pad, int* __restrict__ counters, int64_t tile0,
+               uint16_t* __restrict__ y) {
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile = blockIdx.x / Sg;
+  const int64_t tile = tile0 + blockIdx.x / Sg;
   const int wgs = (int)(blockIdx.x % Sg);
   const int64_t gbeg = ((int64_t)wgs * W + wave) * BPS;
 
@@ -277,7 +317,7 @@ __global__ void __launch_bounds__(64 * W)
     }
   }
   wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
-                  y);
+                  counters + blockIdx.x / Sg, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -399,7 +439,8 @@ __global__ void __launch_bounds__(64 * W)
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-                int64_t rows_pad, uint16_t* __restrict__ y) {
+                int64_t rows_pad, int* __restrict__ counters, int64_t tile0,
+                uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
   __shared__ uint32_t lut[256 * kLut64Copies];
@@ -407,7 +448,7 @@ __global__ void __launch_bounds__(64 * W)
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile = blockIdx.x / Sg;
+  const int64_t tile = tile0 + blockIdx.x / Sg;
   const int wgs = (int)(blockIdx.x % Sg);
   const int64_t P = ceil_div(G, kPeriodGroups);
   const int64_t item = (int64_t)wgs * W + wave;  // (period, part) of this wave
@@ -466,21 +507,7 @@ __global__ void __launch_bounds__(64 * W)
       ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
   }
   wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
-                  y);
-}
-
-// ---------------------------------------------------------------------------
-// Sum of the workgroup partial rows, in workgroup-slice order.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-    k_gemv_reduce(const float* __restrict__ partial, int Sg, int Mb, int Mreal, int64_t rows_pad,
-                  int64_t N, uint16_t* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= Mreal * N) return;
-  const int64_t m = i / N, row = i % N;
-  float s = 0.0f;
-  for (int k = 0; k < Sg; ++k) s += partial[((int64_t)k * Mb + m) * rows_pad + row];
-  y[m * N + row] = f2h(s);
+                  counters + blockIdx.x / Sg, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,13 +524,18 @@ int64_t env_int(const char* name, int64_t dflt) {
   return v > 0 ? v : dflt;
 }
 
+// Arrival counters at the start of every GEMV workspace, one per tile of a
+// launch; a launch covers at most this many tiles.  The prep zeroes them and
+// every launch leaves them at zero.
+constexpr int64_t kCounterSlots = 4096;
+
 // Split of K: units along K (PQ2_0: groups, PTQ1_0: periods of 5 groups),
 // units per wave slice, waves per workgroup W, slices S, workgroup slices
-// Sg = ceil(S / W) (Sg > 1 adds the reduce kernel), and the workspace layout
-// [digit words][group Q][group F][partial rows].
+// Sg = ceil(S / W) (Sg > 1: partial rows, added up by the tile's last
+// workgroup), and the workspace layout.
 struct GemvPlan {
   int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
-  uint64_t off_meta_q, off_meta_f, off_partial, total;
+  uint64_t off_frag, off_meta_q, off_meta_f, off_partial, total;
 };
 
 GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
@@ -520,7 +552,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     p.gpad = p.G;
     p.units = p.G;
     p.frag_words_per_token = (d->K / 64) * kPqFragWords;
-    // one workgroup per tile (no reduce kernel) when that still fills the
+    // one workgroup per tile (no partial rows) when that still fills the
     // chip: the smallest groups-per-wave with all of K in 8 waves
     const int64_t one_wg[] = {2, 4, 5, 8};
     p.per_slice = 0;
@@ -556,7 +588,10 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   }
   p.Sg = ceil_div(p.S, p.W);
   const int64_t kb = gemv_m_bucket(M);
-  uint64_t off = align256((uint64_t)p.slots * p.frag_words_per_token * 4);
+  // [tile arrival counters][digit words][group Q][group F][partial rows]:
+  // everything up to the partial rows depends only on the format, K and M
+  p.off_frag = kCounterSlots * 4;
+  uint64_t off = align256(p.off_frag + (uint64_t)p.slots * p.frag_words_per_token * 4);
   p.off_meta_q = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   p.off_meta_f = off;
@@ -569,61 +604,67 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
 
 void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x, int64_t M,
                  int rotate, uint8_t* ws, hipStream_t st) {
-  uint32_t* frag = reinterpret_cast<uint32_t*>(ws);
+  int* cnt = reinterpret_cast<int*>(ws);
+  uint32_t* frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
   int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
   if (d->format == BGG_FMT_PQ2_0)
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(kPrepThreads), 0, st, x, d->K, (int)M,
-                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
+                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, cnt,
+                       (int)kCounterSlots);
   else
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(kPrepThreads), 0, st, x, d->K,
-                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
+                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, cnt,
+                       (int)kCounterSlots);
 }
 
-// GEMV (+ reduce) over all weight rows for tokens m0 .. m0+Mreal-1.
+// GEMV over all weight rows for tokens m0 .. m0+Mreal-1: one launch, or one
+// per kCounterSlots tiles when the tiles are split over workgroups.
 template <int M>
 void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
                  uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, hipStream_t st) {
-  const uint32_t* frag = reinterpret_cast<const uint32_t*>(ws) + m0 * p.frag_words_per_token;
+  const uint32_t* frag =
+      reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
   const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
   const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f) + m0 * p.gpad;
   float* part = reinterpret_cast<float*>(ws + p.off_partial);
+  int* cnt = reinterpret_cast<int*>(ws);
   uint16_t* yg = y + m0 * d->N;
   const int Sg = (int)p.Sg;
-  const dim3 grid((unsigned)(p.NT * Sg));
+  const int64_t chunk = Sg > 1 ? kCounterSlots : p.NT;
   const dim3 block((unsigned)(64 * p.W));
-  if (d->format == BGG_FMT_PQ2_0) {
+  for (int64_t t0 = 0; t0 < p.NT; t0 += chunk) {
+    const dim3 grid((unsigned)((p.NT - t0 < chunk ? p.NT - t0 : chunk) * Sg));
+    if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
   hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, yg)
-    switch (p.per_slice) {
-      case 8: BGG_PQ2(8); break;
-      case 5: BGG_PQ2(5); break;
-      case 4: BGG_PQ2(4); break;
-      default: BGG_PQ2(2); break;
-    }
+                     p.gpad, part, p.rows_pad, cnt, t0, yg)
+      switch (p.per_slice) {
+        case 8: BGG_PQ2(8); break;
+        case 5: BGG_PQ2(5); break;
+        case 4: BGG_PQ2(4); break;
+        default: BGG_PQ2(2); break;
+      }
 #undef BGG_PQ2
-  } else {
-    // 16-wave workgroups only for the one- and two-token kernels (register
-    // budget); p.W says which one the plan was made for
-    constexpr int W16 = M >= 4 ? 8 : 16;
+    } else {
+      // 16-wave workgroups only for the one- and two-token kernels (register
+      // budget); p.W says which one the plan was made for
+      constexpr int W16 = M >= 4 ? 8 : 16;
+      constexpr int H2 = M == 1 ? 2 : 1;
 #define BGG_PTQ1(H, WW)                                                                           \
   hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, yg)
-    constexpr int H2 = M == 1 ? 2 : 1;
-    if (p.W == 16) {
-      if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
-    } else {
-      if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
-    }
+                     p.gpad, part, p.rows_pad, cnt, t0, yg)
+      if (p.W == 16) {
+        if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
+      } else {
+        if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
+      }
 #undef BGG_PTQ1
+    }
   }
-  if (Sg > 1)
-    hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)ceil_div(Mreal * d->N, 256)), dim3(256), 0, st,
-                       part, Sg, M, Mreal, p.rows_pad, d->N, yg);
 }
 
 bgg_status gemv_args_check(const char* who, const bgg_weights_desc* d, int64_t M,

@@ -175,11 +175,13 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
  *               bytes; its contents need no initialisation and are scratch.
  * Equivalent to bgg_gemv_prepare followed by bgg_gemv_run.
- * Each 64-row tile is read once per call, all M tokens at a time.  The
+ * Each 64-row tile is read once per group of up to four tokens (one kernel
+ * launch per group), all tokens of the group at a time.  The
  * activations are carried as 15-bit integers with a power-of-two scale per
  * 128-block (absolute error at most 2^-14 of the block's largest |x'|), the
  * trit products are exact integer sums, and each group's sum is scaled and
- * accumulated in fp32; y is rounded to fp16 once.
+ * accumulated in fp32 in a fixed order; y is rounded to fp16 once, and the
+ * same inputs always give bit-identical y.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER,
  * BGG_ERR_HIP.
  */
