@@ -14,10 +14,11 @@ value = packed weight bytes of the step (format bytes: trits + fp16 scales)
         / wall time of one step.
 
 Also printed in the same JSON line: the roofline of the dominant GEMV kernel
-(its own average duration from HIP events recorded around every launch in
-the timed region), per-kernel figures, the prefill GEMM (4096 tokens) in
-TFLOP/s with its MFMA roofline and the activation transform in GB/s, and
-the CPU oracle timed on this host on the whole step.
+(the kernel, by name, with the largest share of a step; its launch duration
+from HIP events around back-to-back launches of each call, right after the
+timed region), per-kernel figures, the prefill GEMM (4096 tokens) in TFLOP/s
+with its MFMA roofline and the activation transform in GB/s, and the CPU
+oracle timed on this host on a sample of the step.
 """
 from __future__ import annotations
 
@@ -50,8 +51,9 @@ def source_hash() -> str:
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    if it was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of `kernel` (its name as the profiler lists it)
+    from the committed counter summary, if that was taken on the current
+    kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "gemv_traffic.json")
     if not os.path.exists(path):
         return None
@@ -72,6 +74,10 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-reps", type=int, default=100,
+                    help="back-to-back launches per per-kernel timing")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run a device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,50 +117,89 @@ def main() -> int:
     resident = sum(it["desc"].total_bytes * args.copies for it in items)
     log(f"setup {time.time() - t0:.1f}s; {resident / 2**20:.0f} MiB of packed weights resident")
 
-    def step(i, events=None):
+    def step(i):
         c = i % args.copies
-        for j, it in enumerate(items):
+        for it in items:
             bgg.bgg_gemv_prepare(it["desc"], it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
-            if events is not None:
-                events[j][0].record(stream)
             bgg.bgg_gemv_run(it["desc"], it["copies"][c], it["y"], 1, it["ws"], stream)
-            if events is not None:
-                events[j][1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in items] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # ------------------------------------------------------ the timed region
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall / args.steps * 1e3
     step_bytes = sum(it["bytes"] for it in items)
     value = step_bytes / (wall / args.steps) / 1e9
 
+    # ---------------------------------------------- per-kernel launch times
+    # HIP events on the launch stream around `reps` back-to-back launches of
+    # one call (an event pair around every single launch would add the
+    # event overhead, several microseconds, to each).  bgg_gemv_run is one
+    # kernel launch at M = 1.
+    reps = args.kernel_reps
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(reps):
+            fn(r)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps  # us per launch
+
     kernels = []
-    for j, it in enumerate(items):
-        us = float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)])) * 1e3
-        kname = f"k_gemv_{'pq2' if it['fmt'] == 'PQ2_0' else 'ptq1'}"
-        kernels.append(dict(kernel=kname, format=it["fmt"], matrix=it["name"], n=it["n"], k=it["k"],
-                            bytes_per_launch=it["bytes"], avg_us=round(us, 3),
-                            gbs=round(it["bytes"] / us / 1e3, 1),
-                            frac=round(it["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)))
-    dom = max(kernels, key=lambda k: k["avg_us"])
-    traffic = measured_traffic(f"{dom['kernel']}:{dom['format']}:{dom['matrix']}")
-    roofline = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(dom["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel=f"{dom['kernel']} ({dom['format']}, {dom['matrix']} {dom['n']}x{dom['k']})",
-                    bytes_per_launch=dom["bytes_per_launch"], avg_us=dom["avg_us"])
+    for it in items:
+        d = it["desc"]
+        bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
+        run_us = timed(lambda r: bgg.bgg_gemv_run(d, it["copies"][r % args.copies], it["y"], 1,
+                                                  it["ws"], stream))
+        prep_us = timed(lambda r: bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT,
+                                                       it["ws"], stream))
+        kernels.append(dict(kernel=bgg.bgg_gemv_kernel_name(d, 1), format=it["fmt"],
+                            matrix=it["name"], n=it["n"], k=it["k"],
+                            bytes_per_launch=it["bytes"], avg_us=round(run_us, 3),
+                            gbs=round(it["bytes"] / run_us / 1e3, 1),
+                            frac=round(it["bytes"] / run_us / 1e3 / HBM_PEAK_GBS, 4),
+                            prep_kernel="k_gemv_prep", prep_avg_us=round(prep_us, 3)))
+    # the dominant kernel: the GEMV kernel (by name) with the largest share
+    # of a step; its roofline counts the packed bytes of all its launches
+    by_name = {}
+    for k in kernels:
+        e = by_name.setdefault(k["kernel"], dict(us=0.0, bytes=0, calls=[]))
+        e["us"] += k["avg_us"]
+        e["bytes"] += k["bytes_per_launch"]
+        e["calls"].append(f"{k['format']} {k['matrix']} {k['n']}x{k['k']}")
+    dom_name, dom = max(by_name.items(), key=lambda kv: kv[1]["us"])
+    n_launch = len(dom["calls"])
+    achieved = dom["bytes"] / dom["us"] / 1e3
+    traffic = measured_traffic(dom_name)
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel=dom_name, launches=dom["calls"],
+                    bytes_per_launch=round(dom["bytes"] / n_launch),
+                    avg_us=round(dom["us"] / n_launch, 3))
     log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; kernels: " +
-        ", ".join(f"{k['format']}/{k['matrix']} {k['avg_us']:.2f}us {k['gbs']:.0f}GB/s" for k in kernels))
+        ", ".join(f"{k['format']}/{k['matrix']} {k['kernel']} {k['avg_us']:.2f}us "
+                  f"{k['gbs']:.0f}GB/s (prep {k['prep_avg_us']:.2f}us)" for k in kernels))
     for it in items:
         del it["copies"]
+
+    # calibration for the HBM byte counters: a plain device-to-device copy
+    # of known size (run only when asked, for the counter profiles)
+    if args.calib_copy:
+        src = torch.empty(args.calib_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy} MiB x 3")
+        del src, dst
 
     # --------------------------------------------------------- prefill GEMM
     prefill = None

@@ -75,6 +75,7 @@ _SIGS = {
     "bgg_ternary_gemv": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_gemv_prepare": ([_P, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_gemv_run": ([_P, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
+    "bgg_gemv_kernel_name": ([_P, _i64, ctypes.c_char_p, _sz], _i32),
     "bgg_gemm_workspace_size": ([_P, _i64], _sz),
     "bgg_ternary_gemm": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_status_string": ([_i32], ctypes.c_char_p),
@@ -176,6 +177,12 @@ def bgg_abi_version() -> int:
 
 def bgg_gemv_workspace_size(desc: bgg_weights_desc, M: int) -> int:
     return int(_lib.bgg_gemv_workspace_size(ctypes.byref(desc), M))
+
+
+def bgg_gemv_kernel_name(desc: bgg_weights_desc, M: int) -> str:
+    buf = ctypes.create_string_buffer(96)
+    _ok(_lib.bgg_gemv_kernel_name(ctypes.byref(desc), M, buf, len(buf)), "bgg_gemv_kernel_name")
+    return buf.value.decode()
 
 
 def bgg_gemm_workspace_size(desc: bgg_weights_desc, M: int) -> int:

@@ -29,6 +29,7 @@
 //     fences, no waiting on other workgroups).
 #include "bgg_device.h"
 
+#include <cstdio>
 #include <cstdlib>
 
 using namespace bgg;
@@ -692,6 +693,26 @@ extern "C" {
 size_t bgg_gemv_workspace_size(const bgg_weights_desc* d, int64_t M) {
   if (check_desc(d) != BGG_OK || M < 1 || M > BGG_MAX_GEMV_M) return 0;
   return (size_t)plan_gemv(d, M).total;
+}
+
+bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
+  bgg_status st = check_desc(d);
+  if (st) return st;
+  if (!out) return fail(BGG_ERR_NULL, "bgg_gemv_kernel_name: NULL out");
+  if (M < 1 || M > BGG_MAX_GEMV_M)
+    return fail(BGG_ERR_SHAPE, "bgg_gemv_kernel_name: M must be in 1..16 (got %lld)", (long long)M);
+  const GemvPlan p = plan_gemv(d, M);
+  const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
+  int n;
+  if (d->format == BGG_FMT_PQ2_0) {
+    n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8>", mb, (int)p.per_slice);
+  } else {
+    const int h = (p.per_slice == 2 && mb == 1) ? 2 : 1;
+    n = snprintf(out, cap, "k_gemv_ptq1<%d, %d, %d>", mb, h, mb >= 4 ? 8 : (int)p.W);
+  }
+  if (n < 0 || (size_t)n >= cap)
+    return fail(BGG_ERR_BUFFER, "bgg_gemv_kernel_name: %zu bytes are too few", cap);
+  return BGG_OK;
 }
 
 bgg_status bgg_gemv_prepare(const bgg_weights_desc* d, const void* x_dev, int64_t M, uint32_t flags,

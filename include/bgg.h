@@ -209,6 +209,13 @@ bgg_status bgg_gemv_prepare(const bgg_weights_desc* desc, const void* x_dev, int
 bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, void* y_dev,
                         int64_t M, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The name under which a profiler lists the GEMV kernel that
+ * bgg_gemv_run launches for the first group of up to four of M tokens, e.g.
+ * "k_gemv_ptq1<1, 1, 8>" (host only; for matching profiles to calls).
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
+ * small for the name and its terminating zero). */
+bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);
+
 /* Device workspace bytes that bgg_ternary_gemm needs for M tokens. */
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
 
