@@ -7,17 +7,20 @@
 // (exact: the value is +-s or 0) straight into LDS and multiplied with fp16
 // x' tiles by v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //
-// Tiling: a 256-thread workgroup computes a 128 (tokens) x 128 (weight rows)
-// block of Y, four waves of 64 x 64 (2 x 2 MFMA tiles of 32 x 32), stepping
-// K by 64 (one 16-byte packed chunk per weight row, half a scale group) with
-// double-buffered LDS: global loads of step k+1 are in flight while the
-// matrix cores work on step k.
-//
-// K order inside LDS: within every 16 consecutive k the elements are stored
-// as k = 0,8,1,9,...,7,15.  Decoding a 2-bit code word yields exactly these
-// pairs ((w >> 2j) & 0x00030003 holds codes j and j+8), and the activation
-// tile is permuted the same way while it is copied to LDS, so the two MFMA
-// operands always agree on k.
+// Tiling: a 256-thread workgroup computes a 128 (tokens) x 256 (weight rows)
+// block of Y; each of its four waves owns 64 weight rows (one row tile of
+// the packed layout) and all 128 tokens: 4 x 2 MFMA tiles of 32 x 32, K
+// stepping by 64 (one 16-byte packed chunk per weight row).
+//   * activations: the 128 x 64 fp16 tile of a step is staged in LDS
+//     (double-buffered, shared by the four waves); the loads of step k+1 are
+//     in flight while the matrix cores work on step k;
+//   * weights: every lane loads the packed chunk of its own weight row
+//     straight into registers (2 bits per weight: 1 KiB per wave per step)
+//     and decodes the codes it feeds to the MFMA to fp16 s*t in registers --
+//     exact, since the value is +-s or 0 -- so the weights never touch LDS.
+//     The decode (a few VALU operations per pair of weights) overlaps the
+//     MFMAs of the other waves; the tall wave tile (128 tokens) spreads it
+//     over four MFMA rows.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -27,142 +30,148 @@ using bgg::fail;
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // halves per LDS row (+16 bytes against bank conflicts)
 constexpr int kTileRows = BGG_ROW_TILE;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// (x_{2j}, x_{2j+1}) words of 16 activations -> (x_j, x_{j+8}) words.
-__device__ __forceinline__ void permute16(const uint32_t in[8], uint32_t out[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    out[j] = perm(in[4 + j / 2], in[j / 2], (j & 1) ? 0x07060302u : 0x05040100u);
-}
-
-// 16 PQ2_0 codes (one word) and an fp16 scale -> 8 words of fp16 pairs
-// (s*t_j, s*t_{j+8}).  0x6400 | c is the fp16 1024 + c; subtracting 1025
-// gives t = c - 1 exactly, and t * s is exact.
-__device__ __forceinline__ void decode16(uint32_t w, __half2 s2, uint32_t out[8]) {
+// Eight consecutive PQ2_0 codes (16 bits of a code word: code i in bits
+// 2i..2i+1) and a scale -> the fp16 MFMA operand (s*t_0, ..., s*t_7).
+// A nibble (c1 << 2 | c0) times 0x4001 puts c0 in bits 0-1 and c1 in bits
+// 16-17; 0x6400 | c is the fp16 1024 + c, and subtracting 1025 gives t = c-1
+// exactly; t * s is exact.
+__device__ __forceinline__ f16x8 decode8(uint32_t codes16, __half2 s2) {
   const __half2 bias = __halves2half2(__ushort_as_half(0xE401), __ushort_as_half(0xE401));  // -1025
+  uint32_t out[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t p = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t nib = (codes16 >> (4 * j)) & 0xFu;
+    uint32_t p = ((nib * 0x4001u) & 0x00030003u) | 0x64006400u;
     __half2 h = *reinterpret_cast<__half2*>(&p);
     h = __hmul2(__hadd2(h, bias), s2);
     out[j] = *reinterpret_cast<uint32_t*>(&h);
   }
+  f16x8 r;
+  __builtin_memcpy(&r, out, sizeof(r));
+  return r;
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
     k_gemm_pq2(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
                uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
-               int64_t rows_pad, uint16_t* __restrict__ Y) {
+               int64_t NT, uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsStride];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
 
-  // loader roles: A: row tid/2, 16-blocks 2*(tid%2) and 2*(tid%2)+1;
-  //               B: weight row tid/2, code words 2*(tid%2) and 2*(tid%2)+1
+  // activation loader: row tid/2 of the tile, k half tid%2 (32 values);
+  // rows past M re-read row M-1 (never stored)
   const int lr = tid >> 1, lh = tid & 1;
-  const int64_t am = m0 + lr;
-  const bool a_ok = am < M;
+  const int64_t am = m0 + lr < M ? m0 + lr : M - 1;
   const uint16_t* a_src = X + am * K + lh * 32;
-  const int64_t bn = n0 + lr;
-  const bool b_ok = bn < rows_pad;
-  const uint2* b_src = reinterpret_cast<const uint2*>(packed) +
-                       ((bn / kTileRows) * C * kTileRows + (bn % kTileRows)) * 2 + lh;
-  const uint16_t* s_src = reinterpret_cast<const uint16_t*>(packed + scale_offset) +
-                          (bn / kTileRows) * G * kTileRows + (bn % kTileRows);
 
-  uint4 ra[4];
-  uint2 rb;
-  uint16_t rs;
-  auto gload = [&](int64_t ks) {
-    const int64_t k0 = ks * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = a_ok ? *reinterpret_cast<const uint4*>(a_src + k0 + i * 8) : make_uint4(0, 0, 0, 0);
-    rb = b_ok ? b_src[ks * kTileRows * 2] : make_uint2(0x55555555u, 0x55555555u);
-    rs = b_ok ? s_src[(k0 / 128) * kTileRows] : 0;
-  };
-  auto lstore = [&](int buf) {
-    uint32_t in[8], out[8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint4 u0 = ra[2 * blk], u1 = ra[2 * blk + 1];
-      in[0] = u0.x, in[1] = u0.y, in[2] = u0.z, in[3] = u0.w;
-      in[4] = u1.x, in[5] = u1.y, in[6] = u1.z, in[7] = u1.w;
-      permute16(in, out);
-      uint4* dst = reinterpret_cast<uint4*>(&As[buf][lr * kLdsStride + lh * 32 + blk * 16]);
-      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-    }
-    const __half sh = __ushort_as_half(rs);
-    const __half2 s2 = __halves2half2(sh, sh);
-    const uint32_t cw[2] = {rb.x, rb.y};
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      decode16(cw[blk], s2, out);
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][lr * kLdsStride + lh * 32 + blk * 16]);
-      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-    }
-  };
+  // this wave's weight rows: row tile n0/64 + wave (past the last tile it
+  // re-reads the last one and stores nothing); N-subtile j holds rows
+  // j*32 + li of the tile
+  const int64_t tw = n0 / kTileRows + wave;
+  const bool w_ok = tw < NT;
+  const int64_t tcl = w_ok ? tw : NT - 1;
+  const uint4* b_src = reinterpret_cast<const uint4*>(packed) + tcl * C * kTileRows + li;
+  const uint16_t* s_src =
+      reinterpret_cast<const uint16_t*>(packed + scale_offset) + tcl * G * kTileRows + li;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Software pipeline over K steps of 64: the activation pieces of step
+  // ks+2 and the packed chunks and scales of step ks+1 are loaded while step
+  // ks is multiplied; step ks+1's activations (loaded one iteration earlier)
+  // go to the other LDS buffer at the end of the iteration.  Loads past the
+  // last step re-read the last step (no branch splits the registers), and
+  // the two activation register sets alternate, so the loop is unrolled by
+  // two (K / 64 is even since K is a multiple of 128).
   const int64_t steps = K / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int li = lane & 31, lk = (lane >> 5) * 8;
-  for (int64_t ks = 0; ks < steps; ++ks) {
-    const int cur = (int)(ks & 1);
-    if (ks + 1 < steps) gload(ks + 1);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      f16x8 a[2], b[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const f16x8*>(&As[cur][(wm * 64 + t * 32 + li) * kLdsStride + kk * 16 + lk]);
-        b[t] = *reinterpret_cast<const f16x8*>(&Bs[cur][(wn * 64 + t * 32 + li) * kLdsStride + kk * 16 + lk]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < steps) lstore(cur ^ 1);
-    __syncthreads();
-  }
+  uint4 xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3, b0, b1;
+  uint16_t s0, s1;
+#define BGG_LOAD_A(KS, R0, R1, R2, R3)                                       \
+  do {                                                                       \
+    const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                     \
+    const uint4* ap_ = reinterpret_cast<const uint4*>(a_src + kc_ * kBK);    \
+    R0 = ap_[0], R1 = ap_[1], R2 = ap_[2], R3 = ap_[3];                      \
+  } while (0)
+#define BGG_LOAD_B(KS)                                                       \
+  do {                                                                       \
+    const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                     \
+    b0 = b_src[kc_ * kTileRows], b1 = b_src[kc_ * kTileRows + 32];           \
+    s0 = s_src[(kc_ / 2) * kTileRows], s1 = s_src[(kc_ / 2) * kTileRows + 32]; \
+  } while (0)
+#define BGG_STORE_A(BUF, R0, R1, R2, R3)                                     \
+  do {                                                                       \
+    uint4* d_ = reinterpret_cast<uint4*>(&As[BUF][lr * kLdsStride + lh * 32]); \
+    d_[0] = R0, d_[1] = R1, d_[2] = R2, d_[3] = R3;                          \
+  } while (0)
+#define BGG_STEP(KS, CUR, L0, L1, L2, L3, S0, S1, S2, S3)                    \
+  do {                                                                       \
+    const uint4 bw[2] = {b0, b1};                                            \
+    __half2 s2[2];                                                           \
+    s2[0] = __halves2half2(__ushort_as_half(s0), __ushort_as_half(s0));      \
+    s2[1] = __halves2half2(__ushort_as_half(s1), __ushort_as_half(s1));      \
+    BGG_LOAD_A((KS) + 2, L0, L1, L2, L3);                                    \
+    BGG_LOAD_B((KS) + 1);                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                \
+      f16x8 a[4], b[2];                                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) a[i] =                   \
+          *reinterpret_cast<const f16x8*>(                                   \
+              &As[CUR][(i * 32 + li) * kLdsStride + kk * 16 + h * 8]);       \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                        \
+        const uint32_t w_ = kk == 0 ? bw[j].x : kk == 1 ? bw[j].y            \
+                            : kk == 2 ? bw[j].z : bw[j].w;                   \
+        b[j] = decode8(w_ >> (16 * h), s2[j]);                               \
+      }                                                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                          \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =           \
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0); \
+    }                                                                        \
+    BGG_STORE_A((CUR) ^ 1, S0, S1, S2, S3);                                  \
+    __syncthreads();                                                         \
+  } while (0)
 
-  // D layout of a 32x32 tile: lane l holds column l%32, rows
-  // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+  BGG_LOAD_A(0, xa0, xa1, xa2, xa3);
+  BGG_LOAD_B(0);
+  BGG_STORE_A(0, xa0, xa1, xa2, xa3);
+  BGG_LOAD_A(1, ya0, ya1, ya2, ya3);
+  __syncthreads();
+  for (int64_t ks = 0; ks < steps; ks += 2) {
+    BGG_STEP(ks, 0, xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3);
+    BGG_STEP(ks + 1, 1, ya0, ya1, ya2, ya3, xa0, xa1, xa2, xa3);
+  }
+#undef BGG_LOAD_A
+#undef BGG_LOAD_B
+#undef BGG_STORE_A
+#undef BGG_STEP
+
+  // D layout of a 32x32 tile: lane l holds column l%32 (a weight row), rows
+  // (tokens) 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+  if (!w_ok) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + li;
+      const int64_t n = tw * kTileRows + j * 32 + li;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+        const int64_t m = m0 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
         if (m < M && n < N) Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
       }
     }
@@ -206,7 +215,7 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
   const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   hipLaunchKernelGGL(k_gemm_pq2, grid, dim3(256), 0, s, (const uint16_t*)xr,
                      (const uint8_t*)packed_dev, d->scale_offset, M, d->N, d->K, d->chunks,
-                     d->groups, d->row_tiles * (int64_t)kTileRows, (uint16_t*)y_dev);
+                     d->groups, d->row_tiles, (uint16_t*)y_dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BGG_ERR_HIP, "bgg_ternary_gemm: %s", hipGetErrorString(e));
   return BGG_OK;
