@@ -217,10 +217,20 @@ __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M]
   if (before != Sg - 1) return;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
+    // the partial rows are loaded eight at a time (independent loads in
+    // flight together) and added in slice order
     float t = 0.0f;
-    for (int k = 0; k < Sg; ++k)
-      t += __hip_atomic_load(&partial[((int64_t)k * M + m) * rows_pad + row], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    for (int k0 = 0; k0 < Sg; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = k0 + i < Sg ? __hip_atomic_load(&partial[((int64_t)(k0 + i) * M + m) * rows_pad + row],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 + i < Sg) t += v[i];
+    }
     if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h(t);
   }
   if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -519,10 +529,10 @@ inline int64_t gemv_m_slots(int64_t M) {
   return M <= 2 ? M : ((M + kGemvTokens - 1) / kGemvTokens) * kGemvTokens;
 }
 
+// A tuning override from the environment (unset or empty: dflt).
 int64_t env_int(const char* name, int64_t dflt) {
   const char* e = getenv(name);
-  const int64_t v = e ? atoll(e) : 0;
-  return v > 0 ? v : dflt;
+  return e && *e ? atoll(e) : dflt;
 }
 
 // Arrival counters at the start of every GEMV workspace, one per tile of a
