@@ -237,6 +237,35 @@ __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M]
 }
 
 // ---------------------------------------------------------------------------
+// Which tile and K slice a workgroup takes.  The first nta tiles of a launch
+// are cut into sga slices of W waves each.  The tiles after them -- left
+// over when the tile count is just above a multiple of the CU count, e.g.
+// 272 tiles on 256 CUs -- are cut into sgb slices of one wave each: those
+// workgroups are light and sit beside the full ones on the CUs, instead of
+// giving a few CUs twice the work of the rest.
+// ---------------------------------------------------------------------------
+struct WgSlot {
+  int64_t tile, local;  // tile index, and its index within the launch
+  int wgs, Sg;          // slice of the tile, slices of the tile
+  bool one;             // a one-wave slice (only wave 0 works)
+};
+__device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nta, int sga,
+                                          int sgb) {
+  // the one-wave slices come first in launch order: they carry the longer
+  // tail (their partial rows are added across workgroups)
+  const int64_t b = blockIdx.x, nb = (ntl - nta) * sgb;
+  WgSlot s;
+  if (b >= nb) {
+    const int64_t r = b - nb;
+    s.local = r / sga, s.wgs = (int)(r % sga), s.Sg = sga, s.one = false;
+  } else {
+    s.local = nta + b / sgb, s.wgs = (int)(b % sgb), s.Sg = sgb, s.one = true;
+  }
+  s.tile = tile0 + s.local;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
 // PQ2_0: wave = 64 rows x BPS groups; workgroup = W consecutive K slices.
 // grid: NT * Sg workgroups of 64*W threads.
 // ---------------------------------------------------------------------------
@@ -246,14 +275,15 @@ __global__ void __launch_bounds__(64 * W)
                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-               int64_t rows_pad, int* __restrict__ counters, int64_t tile0,
-               uint16_t* __restrict__ y) {
+               int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
+               int64_t nta, int sgb, uint16_t* __restrict__ y) {
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile = tile0 + blockIdx.x / Sg;
-  const int wgs = (int)(blockIdx.x % Sg);
-  const int64_t gbeg = ((int64_t)wgs * W + wave) * BPS;
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb);
+  const int64_t tile = ws.tile;
+  const int64_t gbeg =
+      ws.one ? (wave == 0 ? (int64_t)ws.wgs * BPS : G) : ((int64_t)ws.wgs * W + wave) * BPS;
 
   float acc[M];
 #pragma unroll
@@ -327,8 +357,8 @@ __global__ void __launch_bounds__(64 * W)
       }
     }
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
-                  counters + blockIdx.x / Sg, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, ws.wgs, rows_pad,
+                  partial, counters + ws.local, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -450,8 +480,8 @@ __global__ void __launch_bounds__(64 * W)
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-                int64_t rows_pad, int* __restrict__ counters, int64_t tile0,
-                uint16_t* __restrict__ y) {
+                int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
+                int64_t nta, int sgb, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
   __shared__ uint32_t lut[256 * kLut64Copies];
@@ -459,10 +489,11 @@ __global__ void __launch_bounds__(64 * W)
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile = tile0 + blockIdx.x / Sg;
-  const int wgs = (int)(blockIdx.x % Sg);
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb);
+  const int64_t tile = ws.tile;
   const int64_t P = ceil_div(G, kPeriodGroups);
-  const int64_t item = (int64_t)wgs * W + wave;  // (period, part) of this wave
+  // (period, part) of this wave
+  const int64_t item = ws.one ? (wave == 0 ? ws.wgs : P * H) : (int64_t)ws.wgs * W + wave;
   const int64_t p = item / H;
   const int part = (int)(item % H);
   const bool active = p < P;
@@ -517,8 +548,8 @@ __global__ void __launch_bounds__(64 * W)
     else
       ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, Sg, wgs, rows_pad, partial,
-                  counters + blockIdx.x / Sg, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, ws.wgs, rows_pad,
+                  partial, counters + ws.local, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -547,7 +578,22 @@ constexpr int64_t kCounterSlots = 4096;
 struct GemvPlan {
   int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
   uint64_t off_frag, off_meta_q, off_meta_f, off_partial, total;
+  int64_t nta, sgb;  // tiles with Sg slices; one-wave slices of the rest
 };
+
+// Compute units of the current device (cached per device).
+int64_t device_cus() {
+  static int64_t cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   static const int64_t target = env_int("BGG_GEMV_TARGET_WAVES", 2048);
@@ -598,6 +644,17 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     p.S = p.units;
   }
   p.Sg = ceil_div(p.S, p.W);
+  // tiles left over above a multiple of the CU count: one-wave slices
+  p.nta = p.NT;
+  p.sgb = 1;
+  static const int64_t split_rest = env_int("BGG_GEMV_SPLIT_REST", 1);
+  if (split_rest && p.Sg == 1 && p.NT <= kCounterSlots) {
+    const int64_t ncu = device_cus(), r = p.NT % ncu;
+    if (p.NT > ncu && r != 0 && r * p.S <= 2 * ncu) {
+      p.nta = p.NT - r;
+      p.sgb = p.S;
+    }
+  }
   const int64_t kb = gemv_m_bucket(M);
   // [tile arrival counters][digit words][group Q][group F][partial rows]:
   // everything up to the partial rows depends only on the format, K and M
@@ -608,7 +665,8 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   p.off_partial = off;
-  off = align256(off + (p.Sg > 1 ? (uint64_t)p.Sg * kb * p.rows_pad * 4 : 0));
+  const int64_t slices = p.Sg > p.sgb ? p.Sg : p.sgb;
+  off = align256(off + (slices > 1 ? (uint64_t)slices * kb * p.rows_pad * 4 : 0));
   p.total = off;
   return p;
 }
@@ -646,12 +704,17 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
   const int64_t chunk = Sg > 1 ? kCounterSlots : p.NT;
   const dim3 block((unsigned)(64 * p.W));
   for (int64_t t0 = 0; t0 < p.NT; t0 += chunk) {
-    const dim3 grid((unsigned)((p.NT - t0 < chunk ? p.NT - t0 : chunk) * Sg));
+    // with one-wave slices (p.sgb > 1, one launch): nta full tiles, the
+    // rest in one-wave slices; else every tile of the launch has Sg slices
+    const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
+    const int64_t nta = p.sgb > 1 ? p.nta : ntl;
+    const int sgb = (int)p.sgb;
+    const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
     if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
   hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, yg)
+                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, yg)
       switch (p.per_slice) {
         case 8: BGG_PQ2(8); break;
         case 5: BGG_PQ2(5); break;
@@ -667,7 +730,7 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
 #define BGG_PTQ1(H, WW)                                                                           \
   hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, yg)
+                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, yg)
       if (p.W == 16) {
         if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
       } else {
