@@ -250,16 +250,26 @@ struct WgSlot {
   bool one;             // a one-wave slice (only wave 0 works)
 };
 __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nta, int sga,
-                                          int sgb) {
-  // the one-wave slices come first in launch order: they carry the longer
-  // tail (their partial rows are added across workgroups)
+                                          int sgb, bool light_last) {
+  // Light workgroups come first in launch order, so the dispatcher spreads
+  // them over the CUs before the full ones: the one-wave slices, and (with
+  // light_last) the last slice of every tile when it has fewer waves than
+  // the others.
   const int64_t b = blockIdx.x, nb = (ntl - nta) * sgb;
   WgSlot s;
-  if (b >= nb) {
-    const int64_t r = b - nb;
-    s.local = r / sga, s.wgs = (int)(r % sga), s.Sg = sga, s.one = false;
-  } else {
+  s.one = false;
+  if (b < nb) {
     s.local = nta + b / sgb, s.wgs = (int)(b % sgb), s.Sg = sgb, s.one = true;
+  } else if (light_last && sga > 1) {
+    const int64_t r = b - nb;
+    if (r < nta)
+      s.local = r, s.wgs = sga - 1;
+    else
+      s.local = (r - nta) / (sga - 1), s.wgs = (int)((r - nta) % (sga - 1));
+    s.Sg = sga;
+  } else {
+    const int64_t r = b - nb;
+    s.local = r / sga, s.wgs = (int)(r % sga), s.Sg = sga;
   }
   s.tile = tile0 + s.local;
   return s;
@@ -276,11 +286,11 @@ __global__ void __launch_bounds__(64 * W)
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
                int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
-               int64_t nta, int sgb, uint16_t* __restrict__ y) {
+               int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb);
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
   const int64_t tile = ws.tile;
   const int64_t gbeg =
       ws.one ? (wave == 0 ? (int64_t)ws.wgs * BPS : G) : ((int64_t)ws.wgs * W + wave) * BPS;
@@ -481,7 +491,7 @@ __global__ void __launch_bounds__(64 * W)
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
                 int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
-                int64_t nta, int sgb, uint16_t* __restrict__ y) {
+                int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
   __shared__ uint32_t lut[256 * kLut64Copies];
@@ -489,7 +499,7 @@ __global__ void __launch_bounds__(64 * W)
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb);
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
   const int64_t tile = ws.tile;
   const int64_t P = ceil_div(G, kPeriodGroups);
   // (period, part) of this wave
@@ -709,12 +719,14 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
     const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
     const int64_t nta = p.sgb > 1 ? p.nta : ntl;
     const int sgb = (int)p.sgb;
+    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
+    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
     const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
     if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
   hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, yg)
+                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, light, yg)
       switch (p.per_slice) {
         case 8: BGG_PQ2(8); break;
         case 5: BGG_PQ2(5); break;
@@ -730,7 +742,7 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
 #define BGG_PTQ1(H, WW)                                                                           \
   hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, yg)
+                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, light, yg)
       if (p.W == 16) {
         if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
       } else {
