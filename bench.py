@@ -13,12 +13,17 @@ cannot serve them.
 value = packed weight bytes of the step (format bytes: trits + fp16 scales)
         / wall time of one step.
 
+The steps are launched from a captured HIP graph (replayed K/copies
+times), so the timed region measures the GPU, not the Python interpreter
+that would otherwise issue every launch.
+
 Also printed in the same JSON line: the roofline of the dominant GEMV kernel
 (the kernel, by name, with the largest share of a step; its launch duration
-from HIP events around back-to-back launches of each call, right after the
-timed region), per-kernel figures, the prefill GEMM (4096 tokens) in TFLOP/s
-with its MFMA roofline and the activation transform in GB/s, and the CPU
-oracle timed on this host on a sample of the step.
+from HIP events around the replay of a graph of back-to-back launches of
+each call, right after the timed region), per-kernel figures, the prefill
+GEMM (4096 tokens) in TFLOP/s with its MFMA roofline and the activation
+transform in GB/s, and the CPU oracle timed on this host on a sample of the
+step.
 """
 from __future__ import annotations
 
@@ -117,39 +122,61 @@ def main() -> int:
     resident = sum(it["desc"].total_bytes * args.copies for it in items)
     log(f"setup {time.time() - t0:.1f}s; {resident / 2**20:.0f} MiB of packed weights resident")
 
-    def step(i):
-        c = i % args.copies
+    # Launches go through HIP graphs (captured once, replayed): a ctypes call
+    # from Python costs several microseconds, as long as the kernels it
+    # launches, so eager launching would time the interpreter.
+    def step(c, st):
         for it in items:
-            bgg.bgg_gemv_prepare(it["desc"], it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
-            bgg.bgg_gemv_run(it["desc"], it["copies"][c], it["y"], 1, it["ws"], stream)
+            bgg.bgg_gemv_prepare(it["desc"], it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], st)
+            bgg.bgg_gemv_run(it["desc"], it["copies"][c], it["y"], 1, it["ws"], st)
 
-    for i in range(args.warmup):
-        step(i)
+    def capture(fn):
+        """A graph of fn(stream), captured after one eager run of fn."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return g
+
+    # one replay = one step per weight copy
+    g_steps = capture(lambda st: [step(c, st) for c in range(args.copies)])
+    rounds = max(1, args.steps // args.copies)
+    steps = rounds * args.copies
+    for _ in range(max(1, args.warmup // args.copies)):
+        g_steps.replay()
     torch.cuda.synchronize()
 
     # ------------------------------------------------------ the timed region
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for _ in range(rounds):
+        g_steps.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall / steps * 1e3
     step_bytes = sum(it["bytes"] for it in items)
-    value = step_bytes / (wall / args.steps) / 1e9
+    value = step_bytes / (wall / steps) / 1e9
 
     # ---------------------------------------------- per-kernel launch times
-    # HIP events on the launch stream around `reps` back-to-back launches of
-    # one call (an event pair around every single launch would add the
-    # event overhead, several microseconds, to each).  bgg_gemv_run is one
+    # HIP events on the replay stream around a graph of `reps` back-to-back
+    # launches of one call (an event pair around every single launch would
+    # add the event overhead, microseconds, to each).  bgg_gemv_run is one
     # kernel launch at M = 1.
     reps = args.kernel_reps
 
     def timed(fn):
+        g = capture(lambda st: [fn(r, st) for r in range(reps)])
+        g.replay()
+        cur = torch.cuda.current_stream()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for r in range(reps):
-            fn(r)
-        b.record(stream)
+        a.record(cur)
+        g.replay()
+        b.record(cur)
         b.synchronize()
         return a.elapsed_time(b) * 1e3 / reps  # us per launch
 
@@ -157,10 +184,10 @@ def main() -> int:
     for it in items:
         d = it["desc"]
         bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
-        run_us = timed(lambda r: bgg.bgg_gemv_run(d, it["copies"][r % args.copies], it["y"], 1,
-                                                  it["ws"], stream))
-        prep_us = timed(lambda r: bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT,
-                                                       it["ws"], stream))
+        run_us = timed(lambda r, st: bgg.bgg_gemv_run(d, it["copies"][r % args.copies], it["y"], 1,
+                                                      it["ws"], st))
+        prep_us = timed(lambda r, st: bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT,
+                                                           it["ws"], st))
         kernels.append(dict(kernel=bgg.bgg_gemv_kernel_name(d, 1), format=it["fmt"],
                             matrix=it["name"], n=it["n"], k=it["k"],
                             bytes_per_launch=it["bytes"], avg_us=round(run_us, 3),
@@ -277,7 +304,7 @@ def main() -> int:
         log(f"cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i32+f32", "data": "synthetic",
         "config": {"workload": "projection: gate_up 17408x5120 + down 5120x17408, batch 1, "

@@ -355,3 +355,45 @@ def test_gemv_shared_preparation(env, fmt):
     torch.cuda.synchronize()
     for (d, T, S), yd in zip(devs, outs):
         assert np.all(relerr(yd.cpu().numpy(), oracle_y(fmt, T, S, x)) <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (300, 640)])
+def test_gemv_graph_replay_matches_eager(env, fmt, N, K):
+    """prepare + run captured in a HIP graph: every replay, with other eager
+    work and synchronisations between replays, gives the eager result bit
+    for bit (the kernels are deterministic; the prep zeroes the split-tile
+    arrival counters with a kernel, and each run leaves them at zero)."""
+    bgg, torch = env
+    say(f"gemv graph replay {fmt} {N}x{K}")
+    T, S = gen_matrix(91, 3, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    x = torch.from_numpy(synth.activations_f16(91, 4, 1, K)).cuda()
+    x_other = torch.from_numpy(synth.activations_f16(91, 5, 1, K)).cuda()
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 1))
+    y_eager = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    bgg.bgg_ternary_gemv(d.desc, d.packed, x, y_eager, 1, bgg.BGG_ROTATE_INPUT, ws)
+    torch.cuda.synchronize()
+    want = y_eager.cpu().numpy()
+    assert np.all(relerr(want, oracle_y(fmt, T, S, x.cpu().numpy())) <= TOL)
+
+    y_graph = torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bgg.bgg_ternary_gemv(d.desc, d.packed, x, y_graph, 1, bgg.BGG_ROTATE_INPUT, ws, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bgg.bgg_ternary_gemv(d.desc, d.packed, x, y_graph, 1, bgg.BGG_ROTATE_INPUT, ws,
+                             torch.cuda.current_stream())
+    y_other = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    for rep in range(4):
+        y_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y_graph.cpu().numpy(), want), f"replay {rep}"
+        # eager work on the same workspace between replays
+        bgg.bgg_ternary_gemv(d.desc, d.packed, x_other, y_other, 1, bgg.BGG_ROTATE_INPUT, ws)
+        torch.cuda.synchronize()
