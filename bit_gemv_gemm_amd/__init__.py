@@ -37,6 +37,7 @@ BGG_GROUP = 128
 BGG_ROW_TILE = 64
 BGG_CHUNK = 16
 BGG_MAX_GEMV_M = 16
+BGG_READ_SLACK = 8192
 STATUS = {0: "BGG_OK", 1: "BGG_ERR_NULL", 2: "BGG_ERR_FORMAT", 3: "BGG_ERR_SHAPE",
           4: "BGG_ERR_TRIT", 5: "BGG_ERR_PACKED_BYTE", 6: "BGG_ERR_BUFFER", 7: "BGG_ERR_DESC",
           8: "BGG_ERR_HIP", 9: "BGG_ERR_SCALE"}

@@ -255,21 +255,26 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
   // them over the CUs before the full ones: the one-wave slices, and (with
   // light_last) the last slice of every tile when it has fewer waves than
   // the others.
-  const int64_t b = blockIdx.x, nb = (ntl - nta) * sgb;
+  // (32-bit arithmetic: block and tile counts of a launch fit, and it keeps
+  // the divisions short)
+  const uint32_t b = blockIdx.x, nb = (uint32_t)(ntl - nta) * (uint32_t)sgb;
+  const uint32_t na = (uint32_t)nta, ga = (uint32_t)sga, gb = (uint32_t)sgb;
   WgSlot s;
   s.one = false;
   if (b < nb) {
-    s.local = nta + b / sgb, s.wgs = (int)(b % sgb), s.Sg = sgb, s.one = true;
-  } else if (light_last && sga > 1) {
-    const int64_t r = b - nb;
-    if (r < nta)
+    s.local = na + b / gb, s.wgs = (int)(b % gb), s.Sg = sgb, s.one = true;
+  } else if (ga == 1) {
+    s.local = b - nb, s.wgs = 0, s.Sg = 1;
+  } else if (light_last) {
+    const uint32_t r = b - nb;
+    if (r < na)
       s.local = r, s.wgs = sga - 1;
     else
-      s.local = (r - nta) / (sga - 1), s.wgs = (int)((r - nta) % (sga - 1));
+      s.local = (r - na) / (ga - 1), s.wgs = (int)((r - na) % (ga - 1));
     s.Sg = sga;
   } else {
-    const int64_t r = b - nb;
-    s.local = r / sga, s.wgs = (int)(r % sga), s.Sg = sga;
+    const uint32_t r = b - nb;
+    s.local = r / ga, s.wgs = (int)(r % ga), s.Sg = sga;
   }
   s.tile = tile0 + s.local;
   return s;
@@ -511,25 +516,19 @@ __global__ void __launch_bounds__(64 * W)
   const uint16_t* sdata =
       reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
   // The part's loads first -- before the LUT is built, so they are in flight
-  // meanwhile -- and branch-free: chunks past the row and groups past G
-  // re-read the last valid one.  Their trits meet digit words that are zero
-  // (the prep writes zeros for positions past K) and scales set to 0 below,
-  // so they add nothing, and no use of the loaded words has to wait for all
-  // of them.
+  // meanwhile -- without bounds checks: chunks past the row and groups past
+  // G read the next tile's bytes or the buffer's zero slack.  Their trits
+  // meet digit words and activation scales that are zero (the prep writes
+  // zeros for positions past K), so they add nothing.
   uint4 w[CH];
   uint32_t sr[kPeriodGroups];
   if (active) {
     // scales first: all of them are needed before the first byte
 #pragma unroll
-    for (int k = 0; k < kPeriodGroups; ++k) {
-      const int64_t g = p * kPeriodGroups + k;
-      sr[k] = ld_scale_pair(sdata + (g < G ? g : G - 1) * kTile, lane);
-    }
+    for (int k = 0; k < kPeriodGroups; ++k)
+      sr[k] = ld_scale_pair(sdata + (p * kPeriodGroups + k) * kTile, lane);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t j = p * kPeriodChunks + part * CH + c;
-      w[c] = ld_stream(tdata + (j < C ? j : C - 1) * kTile);
-    }
+    for (int c = 0; c < CH; ++c) w[c] = ld_stream(tdata + (p * kPeriodChunks + part * CH + c) * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
   build_lut64(lut, lut_seed);
@@ -545,7 +544,7 @@ __global__ void __launch_bounds__(64 * W)
     float sc[kPeriodGroups], gf[kPeriodGroups][M];
 #pragma unroll
     for (int k = 0; k < kPeriodGroups; ++k) {
-      sc[k] = gp + k < G ? scale_half(sr[k], lane) : 0.0f;
+      sc[k] = scale_half(sr[k], lane);
 #pragma unroll
       for (int m = 0; m < M; ++m) gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
     }

@@ -88,7 +88,7 @@ bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* 
   d.trit_bytes = (uint64_t)d.row_tiles * d.chunks * BGG_ROW_TILE * BGG_CHUNK;
   d.scale_offset = (d.trit_bytes + 255) & ~uint64_t(255);
   d.scale_bytes = (uint64_t)d.row_tiles * d.groups * BGG_ROW_TILE * 2;
-  d.total_bytes = d.scale_offset + d.scale_bytes;
+  d.total_bytes = d.scale_offset + d.scale_bytes + BGG_READ_SLACK;
   d.format_bytes = (uint64_t)N * d.row_bytes + (uint64_t)N * d.groups * 2;
   *out = d;
   clear_error();
@@ -107,6 +107,7 @@ static void place_rows(const bgg_weights_desc* d, uint8_t* dst,
   const int64_t rows = d->row_tiles * BGG_ROW_TILE;
   uint16_t* sdst = reinterpret_cast<uint16_t*>(dst + d->scale_offset);
   std::memset(dst + d->trit_bytes, 0, d->scale_offset - d->trit_bytes);
+  std::memset(dst + d->scale_offset + d->scale_bytes, 0, BGG_READ_SLACK);
   auto work = [&](int64_t r0, int64_t r1) {
     std::vector<uint8_t> row(padded_row);
     for (int64_t r = r0; r < r1; ++r) {
@@ -233,6 +234,8 @@ bgg_status bgg_validate_packed(const bgg_weights_desc* d, const void* packed) {
     const int64_t r = (i / (G * BGG_ROW_TILE)) * BGG_ROW_TILE + i % BGG_ROW_TILE;
     if (r >= d->N && s[i] != 0) return fail(BGG_ERR_SCALE, "bgg_validate_packed: padding scale");
   }
+  for (uint64_t i = d->scale_offset + d->scale_bytes; i < d->total_bytes; ++i)
+    if (p[i] != 0) return fail(BGG_ERR_BUFFER, "bgg_validate_packed: slack byte is not zero");
   clear_error();
   return BGG_OK;
 }

@@ -80,9 +80,10 @@ enum {
 #define BGG_ROW_TILE 64   /* rows per tile of the device layout (one row per lane) */
 #define BGG_CHUNK 16      /* bytes of one row that one lane loads at once */
 #define BGG_MAX_GEMV_M 16 /* largest token count of bgg_ternary_gemv */
+#define BGG_READ_SLACK 8192 /* zero bytes after the scales of a packed buffer (see below) */
 
 #define BGG_DESC_MAGIC 0x57474742u /* "BGGW" */
-#define BGG_DESC_VERSION 1u
+#define BGG_DESC_VERSION 2u
 
 /*
  * Descriptor of a packed weight matrix W [N out][K in].  Host struct, filled
@@ -98,6 +99,11 @@ enum {
  *     past N hold zero trits, bytes past the row stream hold zero trits.
  *   scale region, at scale_offset: fp16 scale of row 64*t + l, group g at
  *     byte scale_offset + ((t*groups + g)*64 + l)*2; rows past N hold 0.
+ *   slack, at scale_offset + scale_bytes: BGG_READ_SLACK zero bytes.  The
+ *     kernels read whole work units without bounds checks, up to seven
+ *     chunks past a tile's last chunk and four groups past its last scale;
+ *     those bytes meet zero activation terms and add nothing, and the slack
+ *     keeps the reads of the last tile inside the buffer.
  */
 typedef struct bgg_weights_desc {
   uint32_t magic;        /* BGG_DESC_MAGIC */
@@ -113,7 +119,7 @@ typedef struct bgg_weights_desc {
   uint64_t trit_bytes;   /* row_tiles * chunks * 1024 */
   uint64_t scale_offset; /* trit_bytes rounded up to 256 */
   uint64_t scale_bytes;  /* row_tiles * groups * 128 */
-  uint64_t total_bytes;  /* scale_offset + scale_bytes */
+  uint64_t total_bytes;  /* scale_offset + scale_bytes + BGG_READ_SLACK */
   uint64_t format_bytes; /* N*row_bytes + N*groups*2: the format's own size, no padding */
 } bgg_weights_desc;
 

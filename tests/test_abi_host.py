@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bgg.bgg_abi_version() == 1
+    assert bgg.bgg_abi_version() == 2
     for s in range(10):
         assert bgg.bgg_status_string(s)
     assert bgg.bgg_status_string(0) == "ok"
@@ -50,7 +50,8 @@ def test_describe_sizes(fmt, N, K):
     assert d.chunks == -(-d.row_bytes // 16)
     assert d.trit_bytes == d.row_tiles * d.chunks * 1024
     assert d.scale_offset % 256 == 0 and d.scale_offset >= d.trit_bytes
-    assert d.total_bytes == d.scale_offset + d.row_tiles * d.groups * 128
+    assert d.scale_bytes == d.row_tiles * d.groups * 128
+    assert d.total_bytes == d.scale_offset + d.scale_bytes + bgg.BGG_READ_SLACK
 
 
 def test_describe_rejects_bad_shapes_and_formats():
@@ -143,7 +144,7 @@ def test_descriptor_tampering_is_rejected():
     T = np.zeros((64, 256), np.int8)
     S = np.zeros((64, 2), np.float16)
     bgg.bgg_pack_weights(d, T, S)
-    for field, val in (("magic", 1), ("version", 2), ("format", 2), ("N", 65), ("total_bytes", 5)):
+    for field, val in (("magic", 1), ("version", 99), ("format", 2), ("N", 65), ("total_bytes", 5)):
         d2 = bgg.bgg_weights_desc.from_buffer_copy(d)
         setattr(d2, field, val)
         with pytest.raises(bgg.BggError) as e:
