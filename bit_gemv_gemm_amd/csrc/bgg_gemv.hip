@@ -49,12 +49,15 @@ constexpr int kGemvTokens = 4;
 __host__ __device__ inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
 constexpr int kPrepGroups = 5;  // groups per prep workgroup (one PTQ1_0 period)
-constexpr int kPrepThreads = kPrepGroups * 16;
+// 5 groups x 16 lanes transform; one thread per period byte (PTQ1_0) or per
+// (chunk, 16-position block, parity) (PQ2_0) packs the digit words
+constexpr int kPrepThreads = 128;
 
 // ---------------------------------------------------------------------------
 // activation prep
-// grid: (ceil(Gpad / 5), token slots); block: 80 threads = 5 groups x 16
-// lanes.  Tokens past Mreal get zeros.
+// grid: (ceil(Gpad / 5), token slots); block: 128 threads, the first 80 of
+// them (5 groups x 16 lanes) transform and encode.  Tokens past Mreal get
+// zeros.
 // ---------------------------------------------------------------------------
 template <int FMT>
 __global__ void __launch_bounds__(kPrepThreads)
@@ -74,9 +77,9 @@ __global__ void __launch_bounds__(kPrepThreads)
   const int m = blockIdx.y;
   const int64_t G = K / kGroup;
   const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
-  const int gl = tid >> 4, lane16 = tid & 15;
+  const int gl = tid >> 4, lane16 = tid & 15;  // gl >= 5: threads idle in the transform
   const int64_t g = g0 + gl;
-  const bool valid = g < G && m < Mreal;
+  const bool valid = gl < kPrepGroups && g < G && m < Mreal;
 
   float v[8];
   if (valid) {
@@ -104,12 +107,12 @@ __global__ void __launch_bounds__(kPrepThreads)
     uint32_t nib = 0;
 #pragma unroll
     for (int L = 0; L < 4; ++L) nib |= (uint32_t)(digit4(q, L) & 15) << (4 * L);
-    sd[gl * kGroup + lane16 * 8 + j] = (uint16_t)nib;
+    if (gl < kPrepGroups) sd[gl * kGroup + lane16 * 8 + j] = (uint16_t)nib;
     qsum += q;
   }
 #pragma unroll
   for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
-  if (lane16 == 0 && g < gpad) {
+  if (gl < kPrepGroups && lane16 == 0 && g < gpad) {
     metaQ[(int64_t)m * gpad + g] = qsum;
     metaF[(int64_t)m * gpad + g] = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
   }
@@ -118,18 +121,23 @@ __global__ void __launch_bounds__(kPrepThreads)
   uint32_t* out = frag + (int64_t)m * frag_words_per_token;
   if (FMT == BGG_FMT_PQ2_0) {
     // 10 chunks x 32 words; word (d, par, L) of chunk c: nibble n = digit L
-    // of q at chunk position 16 d + 2 n + par.
+    // of q at chunk position 16 d + 2 n + par.  Thread (chunk, d, par) packs
+    // the four words L = 0..3, which sit next to each other.
     const int64_t C = K / 64;
-    for (int w = tid; w < 2 * kPrepGroups * kPqFragWords; w += kPrepThreads) {
-      const int cl = w / kPqFragWords, r = w % kPqFragWords;
-      const int d = r >> 3, par = (r >> 2) & 1, L = r & 3;
+    if (tid < 2 * kPrepGroups * 8) {
+      const int cl = tid >> 3, d = (tid >> 1) & 3, par = tid & 1;
       const int64_t c = g0 * 2 + cl;
-      if (c >= C) continue;
-      uint32_t word = 0;
+      if (c < C) {
+        uint32_t wd[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
-        word |= ((uint32_t)(sd[cl * 64 + 16 * d + 2 * n + par] >> (4 * L)) & 15u) << (4 * n);
-      out[c * kPqFragWords + r] = word;
+        for (int n = 0; n < 8; ++n) {
+          const uint32_t v = sd[cl * 64 + 16 * d + 2 * n + par];
+#pragma unroll
+          for (int L = 0; L < 4; ++L) wd[L] |= ((v >> (4 * L)) & 15u) << (4 * n);
+        }
+        *reinterpret_cast<uint4*>(out + c * kPqFragWords + d * 8 + par * 4) =
+            make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
     }
   } else {
     // one period, 528 words per token.  Word (byte jb, L), jb < 128: nibble
@@ -139,31 +147,35 @@ __global__ void __launch_bounds__(kPrepThreads)
     // Tokens are interleaved within their GEMV token group of b slots
     // (b = 1, 2 or 4): word (r, L) of slot t sits at (r b + t) 4 + L, so the
     // words one wave needs for a few consecutive bytes are contiguous.
+    // Thread jb packs the four words of byte jb (and the upper four of a
+    // straddling byte).
     const int tg = m / kGemvTokens, slot = m % kGemvTokens;
     const int b = gemv_m_bucket(Mreal - tg * kGemvTokens < kGemvTokens ? Mreal - tg * kGemvTokens
                                                                        : kGemvTokens);
     if (slot >= b) return;  // a slot no GEMV token group reads
-    out = frag + (int64_t)tg * kGemvTokens * frag_words_per_token;
-    const int64_t p = g0 / kPeriodGroups;
-    for (int w = tid; w < kPtqFragWords; w += kPrepThreads) {
-      int jb, upper;
-      const int L = w & 3, r = w >> 2;
-      if (r < kPeriodBytes) {
-        jb = r, upper = 0;
-      } else {
-        // the bytes whose five trits cross a group end: 25, 51, 76, 102
-        jb = (kGroup * (r - kPeriodBytes + 1)) / 5, upper = 1;
-      }
-      const int first_group = (5 * jb) / kGroup;
-      uint32_t word = 0;
+    out = frag + (int64_t)tg * kGemvTokens * frag_words_per_token +
+          (g0 / kPeriodGroups) * kPtqFragWords * b;
+    const int jb = tid;  // 128 threads, 128 bytes
+    const int first_group = (5 * jb) / kGroup;
+    uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const int pos = 5 * jb + i;
-        if (pos / kGroup == first_group + upper)
-          word |= ((uint32_t)(sd[pos] >> (4 * L)) & 15u) << (4 * i);
+    for (int i = 0; i < 5; ++i) {
+      const int pos = 5 * jb + i;
+      const uint32_t v = sd[pos];
+      const bool upper = pos / kGroup != first_group;
+#pragma unroll
+      for (int L = 0; L < 4; ++L) {
+        const uint32_t nib = ((v >> (4 * L)) & 15u) << (4 * i);
+        if (upper)
+          hi[L] |= nib;
+        else
+          lo[L] |= nib;
       }
-      out[p * kPtqFragWords * b + (r * b + slot) * 4 + L] = word;
     }
+    *reinterpret_cast<uint4*>(out + (jb * b + slot) * 4) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if ((5 * jb + 4) / kGroup != first_group)  // bytes 25, 51, 76, 102: s = first_group
+      *reinterpret_cast<uint4*>(out + ((kPeriodBytes + first_group) * b + slot) * 4) =
+          make_uint4(hi[0], hi[1], hi[2], hi[3]);
   }
 }
 
