@@ -24,9 +24,11 @@
 //     by s * 2^(e-14) and accumulated in fp32;
 //   * K is split over the eight waves of a workgroup (reduced in LDS, fixed
 //     order) and, when the tiles alone cannot fill the chip, over
-//     workgroups; the last workgroup of a tile to finish adds their partial
-//     sums in slice order (deterministic, one launch, no cache-flushing
-//     fences, no waiting on other workgroups).
+//     workgroups, which add their partial rows as fixed-point integers with
+//     one 64-bit atomic per row; the atomic also counts the arrivals, and
+//     the last workgroup to arrive at a row writes it (deterministic: integer
+//     addition does not depend on the order; one launch, no waiting on other
+//     workgroups).
 #include "bgg_device.h"
 
 #include <cstdio>
@@ -64,15 +66,17 @@ __global__ void __launch_bounds__(kPrepThreads)
     k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
                 uint32_t* __restrict__ frag, int64_t frag_words_per_token,
                 int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad,
-                int* __restrict__ counters, int ncounters) {
+                uint4* __restrict__ zero, int64_t nzero) {
   // the four 4-bit digits of every q of the workgroup's 640 positions
   __shared__ uint16_t sd[kPrepGroups * kGroup];
   const int tid = threadIdx.x;
   {
-    const int nth = (int)(gridDim.x * gridDim.y) * kPrepThreads;
-    for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * kPrepThreads + tid; i < ncounters;
+    // clear the row sums of the split-K GEMV (every GEMV launch leaves them
+    // at zero again; this covers a workspace that was used for something else)
+    const int64_t nth = (int64_t)(gridDim.x * gridDim.y) * kPrepThreads;
+    for (int64_t i = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * kPrepThreads + tid; i < nzero;
          i += nth)
-      counters[i] = 0;
+      zero[i] = make_uint4(0, 0, 0, 0);
   }
   const int m = blockIdx.y;
   const int64_t G = K / kGroup;
@@ -182,24 +186,35 @@ __global__ void __launch_bounds__(kPrepThreads)
 // ---------------------------------------------------------------------------
 // Workgroup end: the W waves' partial sums are added in wave order in LDS and
 // wave 0 writes y when the workgroup covers all of K.  Otherwise (Sg
-// workgroups per tile) wave 0 stores its partial row, and the workgroup that
-// finishes the tile last -- found with a per-tile arrival counter -- adds the
-// Sg partial rows in slice order (the same order whoever arrives last, so the
-// result is deterministic), writes y and resets the counter to 0.
-//
-// Cross-workgroup visibility without cache-flushing fences: partial rows are
-// stored and read back with device-scope relaxed atomic accesses, which on
-// this chip bypass the per-XCD L2 (the L2s are not coherent with each other),
-// and each wave waits for its stores to complete before it counts itself in.
-// Nothing ever waits on another workgroup, so no schedule can hang.
+// workgroups per tile) each lane adds its row's partial sum into the row's
+// 64-bit word with one device-scope atomic add:
+//   bits 0..56   sum over the arrived workgroups of (v + 2^49), where
+//                v = round(partial * 2^30), clamped to |v| < 2^49
+//   bits 57..63  number of arrived workgroups
+// The lane that sees Sg - 1 arrivals before its own has the whole sum: it
+// removes the biases, writes y and sets the word back to zero for the next
+// launch.  Integer addition is exact, so y does not depend on the order of
+// arrival (deterministic), and one atomic replaces a store, a wait for it, a
+// counter update and reloads of the other partial rows.  Partial sums are
+// kept to 2^-30 absolute (far below an fp16 ulp of any normal y) and up to
+// 2^19 in magnitude (beyond fp16's range).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+constexpr int kSumCountShift = 57;
+constexpr uint64_t kSumBias = 1ull << 49;
+constexpr uint64_t kSumMask = (1ull << kSumCountShift) - 1;
+constexpr int kMaxSumSlices = 127;  // arrivals the count field holds
+
+__device__ __forceinline__ uint64_t sum_term(float s) {
+  const double lim = (double)(kSumBias - 1);
+  const double v = fmin(fmax(rint((double)s * 0x1p30), -lim), lim);
+  return (uint64_t)((int64_t)v + (int64_t)kSumBias);
+}
 
 template <int M, int W>
 __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M][64], int wave,
                                           int lane, int64_t row, int64_t N, int Mreal, int Sg,
-                                          int wgs, int64_t rows_pad, float* __restrict__ partial,
-                                          int* __restrict__ counter, uint16_t* __restrict__ y) {
+                                          int64_t rows_pad, unsigned long long* __restrict__ sums,
+                                          uint16_t* __restrict__ y) {
 #pragma unroll
   for (int m = 0; m < M; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
@@ -218,34 +233,17 @@ __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M]
     return;
   }
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-    __hip_atomic_store(&partial[((int64_t)wgs * M + m) * rows_pad + row], s[m], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  wait_vm0();  // this wave's partial row is in place before it is counted
-  int before = 0;
-  if (lane == 0)
-    before = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  before = __builtin_amdgcn_readfirstlane(before);
-  if (before != Sg - 1) return;
-#pragma unroll
   for (int m = 0; m < M; ++m) {
-    // the partial rows are loaded eight at a time (independent loads in
-    // flight together) and added in slice order
-    float t = 0.0f;
-    for (int k0 = 0; k0 < Sg; k0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = k0 + i < Sg ? __hip_atomic_load(&partial[((int64_t)(k0 + i) * M + m) * rows_pad + row],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (k0 + i < Sg) t += v[i];
+    unsigned long long* word = &sums[(int64_t)m * rows_pad + row];
+    const uint64_t term = sum_term(s[m]);
+    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)(old >> kSumCountShift) == Sg - 1) {
+      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)Sg * (int64_t)kSumBias;
+      if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h((float)((double)tot * 0x1p-30));
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h(t);
   }
-  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -301,8 +299,8 @@ __global__ void __launch_bounds__(64 * W)
     k_gemv_pq2(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
-               const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-               int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
+               const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
+               int64_t rows_pad, int64_t tile0, int64_t ntl,
                int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
@@ -384,8 +382,7 @@ __global__ void __launch_bounds__(64 * W)
       }
     }
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, ws.wgs, rows_pad,
-                  partial, counters + ws.local, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, rows_pad, sums, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -506,8 +503,8 @@ __global__ void __launch_bounds__(64 * W)
     k_gemv_ptq1(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
-                const float* __restrict__ metaF, int64_t gpad, float* __restrict__ partial,
-                int64_t rows_pad, int* __restrict__ counters, int64_t tile0, int64_t ntl,
+                const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
+                int64_t rows_pad, int64_t tile0, int64_t ntl,
                 int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
@@ -569,8 +566,7 @@ __global__ void __launch_bounds__(64 * W)
     else
       ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, ws.wgs, rows_pad,
-                  partial, counters + ws.local, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, rows_pad, sums, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -587,18 +583,13 @@ int64_t env_int(const char* name, int64_t dflt) {
   return e && *e ? atoll(e) : dflt;
 }
 
-// Arrival counters at the start of every GEMV workspace, one per tile of a
-// launch; a launch covers at most this many tiles.  The prep zeroes them and
-// every launch leaves them at zero.
-constexpr int64_t kCounterSlots = 4096;
-
 // Split of K: units along K (PQ2_0: groups, PTQ1_0: periods of 5 groups),
 // units per wave slice, waves per workgroup W, slices S, workgroup slices
-// Sg = ceil(S / W) (Sg > 1: partial rows, added up by the tile's last
-// workgroup), and the workspace layout.
+// Sg = ceil(S / W) (Sg > 1: the workgroups of a tile add their rows into
+// 64-bit row sums), and the workspace layout.
 struct GemvPlan {
   int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
-  uint64_t off_frag, off_meta_q, off_meta_f, off_partial, total;
+  uint64_t off_frag, off_meta_q, off_meta_f, off_sums, total;
   int64_t nta, sgb;  // tiles with Sg slices; one-wave slices of the rest
 };
 
@@ -665,11 +656,12 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     p.S = p.units;
   }
   p.Sg = ceil_div(p.S, p.W);
+  if (p.Sg > kMaxSumSlices) return GemvPlan{};  // K beyond what a row sum counts
   // tiles left over above a multiple of the CU count: one-wave slices
   p.nta = p.NT;
   p.sgb = 1;
   static const int64_t split_rest = env_int("BGG_GEMV_SPLIT_REST", 1);
-  if (split_rest && p.Sg == 1 && p.NT <= kCounterSlots) {
+  if (split_rest && p.Sg == 1 && p.S <= kMaxSumSlices) {
     const int64_t ncu = device_cus(), r = p.NT % ncu;
     if (p.NT > ncu && r != 0 && r * p.S <= 2 * ncu) {
       p.nta = p.NT - r;
@@ -677,40 +669,39 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     }
   }
   const int64_t kb = gemv_m_bucket(M);
-  // [tile arrival counters][digit words][group Q][group F][partial rows]:
-  // everything up to the partial rows depends only on the format, K and M
-  p.off_frag = kCounterSlots * 4;
+  // [digit words][group Q][group F][row sums]: everything before the row
+  // sums depends only on the format, K and M
+  p.off_frag = 0;
   uint64_t off = align256(p.off_frag + (uint64_t)p.slots * p.frag_words_per_token * 4);
   p.off_meta_q = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
-  p.off_partial = off;
-  const int64_t slices = p.Sg > p.sgb ? p.Sg : p.sgb;
-  off = align256(off + (slices > 1 ? (uint64_t)slices * kb * p.rows_pad * 4 : 0));
+  p.off_sums = off;
+  off = align256(off + (p.Sg > 1 || p.sgb > 1 ? (uint64_t)kb * p.rows_pad * 8 : 0));
   p.total = off;
   return p;
 }
 
 void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x, int64_t M,
-                 int rotate, uint8_t* ws, hipStream_t st) {
-  int* cnt = reinterpret_cast<int*>(ws);
+                 int rotate, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
+  // the row sums: everything from their offset to the end of the workspace
+  // (a workspace sized for the largest matrix that this preparation serves)
+  uint4* zero = reinterpret_cast<uint4*>(ws + p.off_sums);
+  const int64_t nzero = (int64_t)((ws_bytes - p.off_sums) / 16);
   uint32_t* frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
   int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
   if (d->format == BGG_FMT_PQ2_0)
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(kPrepThreads), 0, st, x, d->K, (int)M,
-                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, cnt,
-                       (int)kCounterSlots);
+                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
   else
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(kPrepThreads), 0, st, x, d->K,
-                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, cnt,
-                       (int)kCounterSlots);
+                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
 }
 
-// GEMV over all weight rows for tokens m0 .. m0+Mreal-1: one launch, or one
-// per kCounterSlots tiles when the tiles are split over workgroups.
+// GEMV over all weight rows for tokens m0 .. m0+Mreal-1, one launch.
 template <int M>
 void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
                  uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, hipStream_t st) {
@@ -718,49 +709,45 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
       reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
   const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
   const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f) + m0 * p.gpad;
-  float* part = reinterpret_cast<float*>(ws + p.off_partial);
-  int* cnt = reinterpret_cast<int*>(ws);
+  unsigned long long* sums = reinterpret_cast<unsigned long long*>(ws + p.off_sums);
   uint16_t* yg = y + m0 * d->N;
   const int Sg = (int)p.Sg;
-  const int64_t chunk = Sg > 1 ? kCounterSlots : p.NT;
   const dim3 block((unsigned)(64 * p.W));
-  for (int64_t t0 = 0; t0 < p.NT; t0 += chunk) {
-    // with one-wave slices (p.sgb > 1, one launch): nta full tiles, the
-    // rest in one-wave slices; else every tile of the launch has Sg slices
-    const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
-    const int64_t nta = p.sgb > 1 ? p.nta : ntl;
-    const int sgb = (int)p.sgb;
-    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
-    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
-    const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
-    if (d->format == BGG_FMT_PQ2_0) {
+  // with one-wave slices (p.sgb > 1): nta full tiles, the rest in one-wave
+  // slices; else every tile has Sg slices
+  const int64_t t0 = 0, ntl = p.NT;
+  const int64_t nta = p.sgb > 1 ? p.nta : ntl;
+  const int sgb = (int)p.sgb;
+  static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
+  const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
+  const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
+  if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
   hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, light, yg)
-      switch (p.per_slice) {
-        case 8: BGG_PQ2(8); break;
-        case 5: BGG_PQ2(5); break;
-        case 4: BGG_PQ2(4); break;
-        default: BGG_PQ2(2); break;
-      }
+                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, yg)
+    switch (p.per_slice) {
+      case 8: BGG_PQ2(8); break;
+      case 5: BGG_PQ2(5); break;
+      case 4: BGG_PQ2(4); break;
+      default: BGG_PQ2(2); break;
+    }
 #undef BGG_PQ2
-    } else {
-      // 16-wave workgroups only for the one- and two-token kernels (register
-      // budget); p.W says which one the plan was made for
-      constexpr int W16 = M >= 4 ? 8 : 16;
-      constexpr int H2 = M == 1 ? 2 : 1;
+  } else {
+    // 16-wave workgroups only for the one- and two-token kernels (register
+    // budget); p.W says which one the plan was made for
+    constexpr int W16 = M >= 4 ? 8 : 16;
+    constexpr int H2 = M == 1 ? 2 : 1;
 #define BGG_PTQ1(H, WW)                                                                           \
   hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, part, p.rows_pad, cnt, t0, ntl, nta, sgb, light, yg)
-      if (p.W == 16) {
-        if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
-      } else {
-        if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
-      }
-#undef BGG_PTQ1
+                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, yg)
+    if (p.W == 16) {
+      if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
+    } else {
+      if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
     }
+#undef BGG_PTQ1
   }
 }
 
@@ -773,6 +760,9 @@ bgg_status gemv_args_check(const char* who, const bgg_weights_desc* d, int64_t M
     return fail(BGG_ERR_SHAPE, "%s: M must be in 1..16 (got %lld)", who, (long long)M);
   if (!aligned16(workspace)) return fail(BGG_ERR_BUFFER, "%s: misaligned workspace", who);
   *plan = plan_gemv(d, M);
+  if (plan->total == 0)
+    return fail(BGG_ERR_SHAPE, "%s: K = %lld needs more K slices than a row sum counts", who,
+                (long long)d->K);
   if (workspace_bytes < plan->total)
     return fail(BGG_ERR_BUFFER, "%s: workspace has %zu bytes, needs %llu", who, workspace_bytes,
                 (unsigned long long)plan->total);
@@ -821,7 +811,7 @@ bgg_status bgg_gemv_prepare(const bgg_weights_desc* d, const void* x_dev, int64_
   if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
     return fail(BGG_ERR_SHAPE, "bgg_gemv_prepare: unknown flags 0x%x", flags);
   launch_prep(d, p, (const uint16_t*)x_dev, M, (flags & BGG_ROTATE_INPUT) ? 1 : 0,
-              (uint8_t*)workspace, (hipStream_t)stream);
+              (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
   return hip_check("bgg_gemv_prepare");
 }
 

@@ -186,8 +186,10 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * activations are carried as 15-bit integers with a power-of-two scale per
  * 128-block (absolute error at most 2^-14 of the block's largest |x'|), the
  * trit products are exact integer sums, and each group's sum is scaled and
- * accumulated in fp32 in a fixed order; y is rounded to fp16 once, and the
- * same inputs always give bit-identical y.
+ * accumulated in fp32 in a fixed order; where K is split over workgroups
+ * their partial rows are added as 64-bit fixed-point integers (resolution
+ * 2^-30, magnitude below 2^19), whose sum does not depend on the order.  y
+ * is rounded to fp16 once, and the same inputs always give bit-identical y.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER,
  * BGG_ERR_HIP.
  */
@@ -201,7 +203,10 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev
  *
  * bgg_gemv_prepare: transform (with BGG_ROTATE_INPUT) and encode the M
  * activation rows x_dev (fp16 [M][K]) into `workspace`.  What it writes
- * depends only on the format, K and M of `desc`.
+ * there depends only on the format, K and M of `desc`; it also clears the
+ * workspace from the end of that data to workspace_bytes (the row sums of
+ * split-K runs, which every run leaves cleared), so pass the size that the
+ * largest matrix to be run needs rather than a much larger buffer.
  *
  * bgg_gemv_run: y_dev (fp16 [M][N]) = the product of the packed matrix with
  * the activations last prepared in `workspace` (stream order).  Any matrix

@@ -362,8 +362,8 @@ def test_gemv_shared_preparation(env, fmt):
 def test_gemv_graph_replay_matches_eager(env, fmt, N, K):
     """prepare + run captured in a HIP graph: every replay, with other eager
     work and synchronisations between replays, gives the eager result bit
-    for bit (the kernels are deterministic; the prep zeroes the split-tile
-    arrival counters with a kernel, and each run leaves them at zero)."""
+    for bit (the kernels are deterministic; the prep clears the split-K row
+    sums with a kernel, and each run leaves them at zero)."""
     bgg, torch = env
     say(f"gemv graph replay {fmt} {N}x{K}")
     T, S = gen_matrix(91, 3, N, K)
