@@ -127,12 +127,16 @@ __device__ __forceinline__ void build_lut(uint32_t* lut) {
 }
 
 // The GEMV's LUT holds the trits themselves, t = c - 1 as signed 4-bit
-// nibbles (-1 = 0xF), five to a word: 256 entries x 64 copies (64 KiB).
-// Entry e of copy c is the word at byte address e * 256 + c * 4, so lane l
-// reads copy l and the address of byte j of a packed word w is one
-// v_perm_b32: byte 0 = l * 4 (from lane_off), byte 1 = byte j of w,
-// bytes 2-3 = 0.
-constexpr int kLut64Copies = 64;
+// nibbles (-1 = 0xF), five to a word.  Entry e occupies a 256-byte row at
+// e * 256; copy c of it is the word at e * 256 + c * 4, and lane l reads copy
+// l % 32, so the 32 lanes that the LDS serves together hit 32 different
+// banks whatever entries they want.  The address of byte j of a packed word
+// w is then one v_perm_b32: byte 0 = (l % 32) * 4 (from lane_off), byte 1 =
+// byte j of w, bytes 2-3 = 0.  Only the first 128 bytes of each row are
+// written (32 KiB of stores), but the rows span 64 KiB of LDS.  (64 copies,
+// one per lane, were measured no faster to read and twice as slow to build.)
+constexpr int kLutRowBytes = 256;
+constexpr int kLutCopies32 = 32;
 __device__ __forceinline__ uint32_t ptq1_trit_nibbles(uint32_t b) {
   const uint32_t c = ptq1_entry(b);
   uint32_t t = 0;
@@ -140,15 +144,18 @@ __device__ __forceinline__ uint32_t ptq1_trit_nibbles(uint32_t b) {
   for (int i = 0; i < 5; ++i) t |= ((((c >> (4 * i)) & 15u) + 15u) & 15u) << (4 * i);
   return t;
 }
+__device__ __forceinline__ uint32_t lut_lane_off(int lane) { return (uint32_t)(lane & 31) * 4u; }
 // Built in two steps: the first 256 threads each decode one byte value into
 // seed[], then (after a barrier) every thread copies entries out, 16 bytes
 // per store.  Needs blockDim.x >= 256; the caller synchronises afterwards.
-__device__ __forceinline__ void build_lut64(uint32_t* lut, uint32_t* seed) {
+__device__ __forceinline__ void build_lut32(uint32_t* lut, uint32_t* seed) {
   if (threadIdx.x < 256) seed[threadIdx.x] = ptq1_trit_nibbles(threadIdx.x);
   __syncthreads();
-  for (int i = threadIdx.x; i < 256 * (kLut64Copies / 4); i += blockDim.x) {
-    const uint32_t e = seed[i / (kLut64Copies / 4)];
-    reinterpret_cast<uint4*>(lut)[i] = make_uint4(e, e, e, e);
+  constexpr int kQuads = kLutCopies32 / 4, kRowQuads = kLutRowBytes / 16;
+  for (int i = threadIdx.x; i < 256 * kQuads; i += blockDim.x) {
+    const int e = i / kQuads, q = i % kQuads;
+    const uint32_t v = seed[e];
+    reinterpret_cast<uint4*>(lut)[e * kRowQuads + q] = make_uint4(v, v, v, v);
   }
 }
 
@@ -158,7 +165,7 @@ __device__ __forceinline__ void build_lut64(uint32_t* lut, uint32_t* seed) {
 // loads to overlap LDS work waits for both explicitly at the point it picks.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 template <int J>
-__device__ __forceinline__ uint32_t lut64_addr(uint32_t word, uint32_t lane_off) {
+__device__ __forceinline__ uint32_t lut_addr(uint32_t word, uint32_t lane_off) {
   return __builtin_amdgcn_perm(word, lane_off, 0x0C0C0000u | ((4u + J) << 8));
 }
 

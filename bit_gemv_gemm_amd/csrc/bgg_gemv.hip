@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(64 * W)
 // ---------------------------------------------------------------------------
 // PTQ1_0: wave = 64 rows x one part of one period (a period is 5 groups =
 // 128 row bytes, cut into H parts); workgroup = W consecutive parts of one
-// tile sharing a 64-copy LUT.
+// tile sharing a 32-copy LUT.
 //
 // The LUT yields the trits t themselves as signed nibbles, so a group's
 // integer sum is sum t*q directly (no digit-sum correction), and a group
@@ -438,10 +438,10 @@ __device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (
                             : (jb >> 2 & 3) == 2 ? ch.z : ch.w;
       uint32_t addr;
       switch (jb & 3) {
-        case 0: addr = lut64_addr<0>(word, lane_off); break;
-        case 1: addr = lut64_addr<1>(word, lane_off); break;
-        case 2: addr = lut64_addr<2>(word, lane_off); break;
-        default: addr = lut64_addr<3>(word, lane_off); break;
+        case 0: addr = lut_addr<0>(word, lane_off); break;
+        case 1: addr = lut_addr<1>(word, lane_off); break;
+        case 2: addr = lut_addr<2>(word, lane_off); break;
+        default: addr = lut_addr<3>(word, lane_off); break;
       }
       lv[buf][j] = *reinterpret_cast<const uint32_t*>(lbase + addr);
 #pragma unroll
@@ -508,7 +508,7 @@ __global__ void __launch_bounds__(64 * W)
                 int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
-  __shared__ uint32_t lut[256 * kLut64Copies];
+  __shared__ uint32_t lut[256 * kLutRowBytes / 4];
   __shared__ uint32_t lut_seed[256];
   __shared__ float red[W][M][64];
   const int lane = threadIdx.x & 63;
@@ -540,7 +540,7 @@ __global__ void __launch_bounds__(64 * W)
     for (int c = 0; c < CH; ++c) w[c] = ld_stream(tdata + (p * kPeriodChunks + part * CH + c) * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
-  build_lut64(lut, lut_seed);
+  build_lut32(lut, lut_seed);
   __syncthreads();
 
   float acc[M];
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(64 * W)
       for (int m = 0; m < M; ++m) gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
     }
     const uint32_t* fp = frag + p * kPtqFragWords * M;
-    const uint32_t lane_off = (uint32_t)lane * 4u;
+    const uint32_t lane_off = lut_lane_off(lane);
     const char* lbase = reinterpret_cast<const char*>(lut);
     static_assert(H == 1 || H == 2, "one or two parts per period");
     if (H == 1 || part == 0)
