@@ -81,19 +81,6 @@ __device__ __forceinline__ void load8h(const uint16_t* p, float v[8]) {
   }
 }
 
-// Signed 4-bit digit L of q (|q| <= 2^14): q = d0 + 16 d1 + 256 d2 + 4096 d3,
-// every d in [-8, 7] (d3 in [-4, 4]).
-__device__ __forceinline__ int digit4(int q, int L) {
-  int d = 0;
-#pragma unroll
-  for (int i = 0; i <= 3; ++i) {
-    d = (int)((unsigned)q << 28) >> 28;  // sign-extended low nibble
-    if (i == L) break;
-    q = (q - d) >> 4;
-  }
-  return L == 3 ? q : d;
-}
-
 // PQ2_0: 16 codes of one word -> codes of even positions in the low two
 // bits of each nibble (E) and of odd positions likewise (O).
 __device__ __forceinline__ uint32_t pq2_even(uint32_t w) { return w & 0x33333333u; }

@@ -50,116 +50,116 @@ constexpr int kPtqFragWords = kPeriodBytes * 4 + 4 * 4;  // 528
 constexpr int kGemvTokens = 4;
 __host__ __device__ inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : 4; }
 
-constexpr int kPrepGroups = 5;  // groups per prep workgroup (one PTQ1_0 period)
-// 5 groups x 16 lanes transform; one thread per period byte (PTQ1_0) or per
-// (chunk, 16-position block, parity) (PQ2_0) packs the digit words
-constexpr int kPrepThreads = 128;
-
 // ---------------------------------------------------------------------------
-// activation prep
-// grid: (ceil(Gpad / 5), token slots); block: 128 threads, the first 80 of
-// them (5 groups x 16 lanes) transform and encode.  Tokens past Mreal get
-// zeros.
+// activation encoding, one wave at a time
+//
+// wave_encode: NG consecutive 128-blocks g0 .. g0+NG-1 of one token row,
+// 16 lanes per block, four blocks per pass.  x -> x' (fp32 FWHT) -> the
+// block's exponent e (max|x'| < 2^e) -> q = rint(x' 2^(14-e)), |q| <= 2^14
+// -> the four signed 4-bit digits of q (q = d0 + 16 d1 + 256 d2 + 4096 d3,
+// d in [-8, 7]) packed into one 16-bit value, the nibbles of
+// (q + 0x8888) ^ 0x8888: adding 8 to every digit makes each nibble of the
+// sum d + 8 in [0, 15] without carries, and flipping bit 3 of each nibble
+// gives d's own 4-bit two's complement.  The packed values go to sd[] (this
+// wave's LDS staging area) and the block's sum of q and 2^(e-14) to
+// metaQ/metaF (zero for an all-zero block and for blocks past G).
 // ---------------------------------------------------------------------------
-template <int FMT>
-__global__ void __launch_bounds__(kPrepThreads)
-    k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
-                uint32_t* __restrict__ frag, int64_t frag_words_per_token,
-                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad,
-                uint4* __restrict__ zero, int64_t nzero) {
-  // the four 4-bit digits of every q of the workgroup's 640 positions
-  __shared__ uint16_t sd[kPrepGroups * kGroup];
-  const int tid = threadIdx.x;
-  {
-    // clear the row sums of the split-K GEMV (every GEMV launch leaves them
-    // at zero again; this covers a workspace that was used for something else)
-    const int64_t nth = (int64_t)(gridDim.x * gridDim.y) * kPrepThreads;
-    for (int64_t i = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * kPrepThreads + tid; i < nzero;
-         i += nth)
-      zero[i] = make_uint4(0, 0, 0, 0);
-  }
-  const int m = blockIdx.y;
-  const int64_t G = K / kGroup;
-  const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
-  const int gl = tid >> 4, lane16 = tid & 15;  // gl >= 5: threads idle in the transform
-  const int64_t g = g0 + gl;
-  const bool valid = gl < kPrepGroups && g < G && m < Mreal;
-
-  float v[8];
-  if (valid) {
-    load8h(x + (int64_t)m * K + g * kGroup + lane16 * 8, v);
-  } else {
+template <int NG>
+__device__ __forceinline__ void wave_encode(const uint16_t* __restrict__ x, int64_t G, int64_t g0,
+                                            bool token_valid, int rotate, uint16_t* sd, int lane,
+                                            int32_t* __restrict__ metaQ, float* __restrict__ metaF,
+                                            int64_t gpad) {
+  const int gl = lane >> 4, lane16 = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-  }
-  if (rotate) {
-    fwht128_unscaled(v, lane16);
+  for (int pass = 0; pass < (NG + 3) / 4; ++pass) {
+    const int gi = pass * 4 + gl;  // block within the NG
+    const int64_t g = g0 + gi;
+    const bool in_set = gi < NG;
+    float v[8];
+    if (in_set && g < G && token_valid) {
+      load8h(x + g * kGroup + lane16 * 8, v);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-#pragma unroll
-  for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
-  int e = 0;
-  frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1): |x'| < 2^e
-  int qsum = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int q = amax > 0.0f ? (int)rintf(ldexpf(v[j], 14 - e)) : 0;
-    uint32_t nib = 0;
-#pragma unroll
-    for (int L = 0; L < 4; ++L) nib |= (uint32_t)(digit4(q, L) & 15) << (4 * L);
-    if (gl < kPrepGroups) sd[gl * kGroup + lane16 * 8 + j] = (uint16_t)nib;
-    qsum += q;
-  }
-#pragma unroll
-  for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
-  if (gl < kPrepGroups && lane16 == 0 && g < gpad) {
-    metaQ[(int64_t)m * gpad + g] = qsum;
-    metaF[(int64_t)m * gpad + g] = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
-  }
-  __syncthreads();
-
-  uint32_t* out = frag + (int64_t)m * frag_words_per_token;
-  if (FMT == BGG_FMT_PQ2_0) {
-    // 10 chunks x 32 words; word (d, par, L) of chunk c: nibble n = digit L
-    // of q at chunk position 16 d + 2 n + par.  Thread (chunk, d, par) packs
-    // the four words L = 0..3, which sit next to each other.
-    const int64_t C = K / 64;
-    if (tid < 2 * kPrepGroups * 8) {
-      const int cl = tid >> 3, d = (tid >> 1) & 3, par = tid & 1;
-      const int64_t c = g0 * 2 + cl;
-      if (c < C) {
-        uint32_t wd[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const uint32_t v = sd[cl * 64 + 16 * d + 2 * n + par];
-#pragma unroll
-          for (int L = 0; L < 4; ++L) wd[L] |= ((v >> (4 * L)) & 15u) << (4 * n);
-        }
-        *reinterpret_cast<uint4*>(out + c * kPqFragWords + d * 8 + par * 4) =
-            make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-  } else {
-    // one period, 528 words per token.  Word (byte jb, L), jb < 128: nibble
-    // i = digit L of q at period position 5 jb + i, kept only if that
-    // position is in the same group as 5 jb.  Word (128 + s, L): the upper
-    // part of the s-th straddling byte (positions in the next group).
-    // Tokens are interleaved within their GEMV token group of b slots
-    // (b = 1, 2 or 4): word (r, L) of slot t sits at (r b + t) 4 + L, so the
-    // words one wave needs for a few consecutive bytes are contiguous.
-    // Thread jb packs the four words of byte jb (and the upper four of a
-    // straddling byte).
-    const int tg = m / kGemvTokens, slot = m % kGemvTokens;
-    const int b = gemv_m_bucket(Mreal - tg * kGemvTokens < kGemvTokens ? Mreal - tg * kGemvTokens
-                                                                       : kGemvTokens);
-    if (slot >= b) return;  // a slot no GEMV token group reads
-    out = frag + (int64_t)tg * kGemvTokens * frag_words_per_token +
-          (g0 / kPeriodGroups) * kPtqFragWords * b;
-    const int jb = tid;  // 128 threads, 128 bytes
+    if (rotate) {
+      fwht128_unscaled(v, lane16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+    int e = 0;
+    frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1): |x'| < 2^e
+    int qsum = 0;
+    uint32_t nib[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = amax > 0.0f ? (int)rintf(ldexpf(v[j], 14 - e)) : 0;
+      nib[j] = ((uint32_t)(q + 0x8888) ^ 0x8888u) & 0xFFFFu;
+      qsum += q;
+    }
+    if (in_set)
+      *reinterpret_cast<uint4*>(sd + gi * kGroup + lane16 * 8) =
+          make_uint4(nib[0] | nib[1] << 16, nib[2] | nib[3] << 16, nib[4] | nib[5] << 16,
+                     nib[6] | nib[7] << 16);
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
+    if (in_set && lane16 == 0 && g < gpad) {
+      metaQ[g] = qsum;
+      metaF[g] = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
+    }
+  }
+}
+
+// The wave's own LDS writes are visible to all its lanes after this (LDS
+// executes a wave's instructions in order; the clobber keeps the compiler
+// from moving memory accesses across it).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// PQ2_0 digit words of chunks c0 .. c0+2*NG-1 (those below C) from sd:
+// word (d, par, L) of chunk c holds in nibble n digit L of q at chunk
+// position 16 d + 2 n + par.  Lane item (chunk, d, par) packs the four words
+// L = 0..3, which sit next to each other (one 16-byte store).
+template <int NG>
+__device__ __forceinline__ void wave_pack_pq2(const uint16_t* sd, uint32_t* __restrict__ out,
+                                              int64_t c0, int64_t C, int lane) {
+#pragma unroll
+  for (int it0 = 0; it0 < NG * 16; it0 += 64) {
+    const int it = it0 + lane;
+    const int cl = it >> 3, d = (it >> 1) & 3, par = it & 1;
+    const int64_t c = c0 + cl;
+    if (it < NG * 16 && c < C) {
+      uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t v = sd[cl * 64 + 16 * d + 2 * n + par];
+#pragma unroll
+        for (int L = 0; L < 4; ++L) wd[L] |= ((v >> (4 * L)) & 15u) << (4 * n);
+      }
+      *reinterpret_cast<uint4*>(out + c * kPqFragWords + d * 8 + par * 4) =
+          make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  }
+}
+
+// PTQ1_0 digit words of one period (528 words per token) from sd.  Word
+// (byte jb, L), jb < 128: nibble i = digit L of q at period position
+// 5 jb + i, kept only if that position is in the same group as 5 jb.  Word
+// (128 + s, L): the upper part of the s-th straddling byte (positions in
+// the next group).  Tokens are interleaved within their GEMV token group of
+// b slots (b = 1, 2 or 4): word (r, L) of slot t sits at (r b + t) 4 + L, so
+// the words one wave needs for a few consecutive bytes are contiguous.
+// Lane jb packs the four words of byte jb (and the upper four of a
+// straddling byte), two bytes per lane.
+__device__ __forceinline__ void wave_pack_ptq1(const uint16_t* sd, uint32_t* __restrict__ out,
+                                               int b, int slot, int lane) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jb = h * 64 + lane;
     const int first_group = (5 * jb) / kGroup;
     uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -180,6 +180,55 @@ __global__ void __launch_bounds__(kPrepThreads)
     if ((5 * jb + 4) / kGroup != first_group)  // bytes 25, 51, 76, 102: s = first_group
       *reinterpret_cast<uint4*>(out + ((kPeriodBytes + first_group) * b + slot) * 4) =
           make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+}
+
+// Blocks per prep unit: one PTQ1_0 period, or five PQ2_0 groups.
+constexpr int kPrepGroups = 5;
+
+// The PTQ1_0 token group of token m: its base slot, its slot count b, and
+// m's slot within it.
+__device__ __forceinline__ void ptq1_token_slot(int m, int Mreal, int* tg0, int* b, int* slot) {
+  const int tg = m / kGemvTokens;
+  *tg0 = tg * kGemvTokens;
+  *slot = m % kGemvTokens;
+  *b = gemv_m_bucket(Mreal - *tg0 < kGemvTokens ? Mreal - *tg0 : kGemvTokens);
+}
+
+// ---------------------------------------------------------------------------
+// activation prep kernel: one wave per unit of five blocks and token slot.
+// grid: (ceil(Gpad / 5), token slots); block: 64 threads.  Tokens past Mreal
+// get zeros.  Also clears the split-K row sums.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ void __launch_bounds__(64)
+    k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
+                uint32_t* __restrict__ frag, int64_t frag_words_per_token,
+                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad,
+                uint4* __restrict__ zero, int64_t nzero) {
+  __shared__ __attribute__((aligned(16))) uint16_t sd[kPrepGroups * kGroup];
+  const int lane = threadIdx.x;
+  {
+    // clear the row sums of the split-K GEMV (every GEMV launch leaves them
+    // at zero again; this covers a workspace that was used for something else)
+    const int64_t nth = (int64_t)(gridDim.x * gridDim.y) * 64;
+    for (int64_t i = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * 64 + lane; i < nzero; i += nth)
+      zero[i] = make_uint4(0, 0, 0, 0);
+  }
+  const int m = blockIdx.y;
+  const int64_t G = K / kGroup;
+  const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
+  wave_encode<kPrepGroups>(x + (int64_t)m * K, G, g0, m < Mreal, rotate, sd, lane,
+                           metaQ + (int64_t)m * gpad, metaF + (int64_t)m * gpad, gpad);
+  wave_lds_sync();
+  if (FMT == BGG_FMT_PQ2_0) {
+    wave_pack_pq2<kPrepGroups>(sd, frag + (int64_t)m * frag_words_per_token, 2 * g0, K / 64, lane);
+  } else {
+    int tg0, b, slot;
+    ptq1_token_slot(m, Mreal, &tg0, &b, &slot);
+    if (slot >= b) return;  // a slot no GEMV token group reads
+    wave_pack_ptq1(sd, frag + (int64_t)tg0 * frag_words_per_token +
+                           (g0 / kPeriodGroups) * kPtqFragWords * b, b, slot, lane);
   }
 }
 
@@ -694,10 +743,10 @@ void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
   if (d->format == BGG_FMT_PQ2_0)
-    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(kPrepThreads), 0, st, x, d->K, (int)M,
+    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(64), 0, st, x, d->K, (int)M,
                        rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
   else
-    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(kPrepThreads), 0, st, x, d->K,
+    hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(64), 0, st, x, d->K,
                        (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
 }
 
