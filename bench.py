@@ -125,10 +125,12 @@ def main() -> int:
     # Launches go through HIP graphs (captured once, replayed): a ctypes call
     # from Python costs several microseconds, as long as the kernels it
     # launches, so eager launching would time the interpreter.
+    # One call per (format, matrix): at one token bgg_ternary_gemv is a
+    # single kernel that transforms and encodes x and computes y.
     def step(c, st):
         for it in items:
-            bgg.bgg_gemv_prepare(it["desc"], it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], st)
-            bgg.bgg_gemv_run(it["desc"], it["copies"][c], it["y"], 1, it["ws"], st)
+            bgg.bgg_ternary_gemv(it["desc"], it["copies"][c], it["x"], it["y"], 1,
+                                 bgg.BGG_ROTATE_INPUT, it["ws"], st)
 
     def capture(fn):
         """A graph of fn(stream), captured after one eager run of fn."""
@@ -165,8 +167,9 @@ def main() -> int:
     # ---------------------------------------------- per-kernel launch times
     # HIP events on the replay stream around a graph of `reps` back-to-back
     # launches of one call (an event pair around every single launch would
-    # add the event overhead, microseconds, to each).  bgg_gemv_run is one
-    # kernel launch at M = 1.
+    # add the event overhead, microseconds, to each).  At M = 1
+    # bgg_ternary_gemv, bgg_gemv_prepare and bgg_gemv_run are one kernel
+    # launch each; the last two are the two-step form, timed for comparison.
     reps = args.kernel_reps
 
     def timed(fn):
@@ -183,6 +186,9 @@ def main() -> int:
     kernels = []
     for it in items:
         d = it["desc"]
+        one_us = timed(lambda r, st: bgg.bgg_ternary_gemv(d, it["copies"][r % args.copies], it["x"],
+                                                          it["y"], 1, bgg.BGG_ROTATE_INPUT,
+                                                          it["ws"], st))
         bgg.bgg_gemv_prepare(d, it["x"], 1, bgg.BGG_ROTATE_INPUT, it["ws"], stream)
         run_us = timed(lambda r, st: bgg.bgg_gemv_run(d, it["copies"][r % args.copies], it["y"], 1,
                                                       it["ws"], st))
@@ -190,10 +196,11 @@ def main() -> int:
                                                            it["ws"], st))
         kernels.append(dict(kernel=bgg.bgg_gemv_kernel_name(d, 1), format=it["fmt"],
                             matrix=it["name"], n=it["n"], k=it["k"],
-                            bytes_per_launch=it["bytes"], avg_us=round(run_us, 3),
-                            gbs=round(it["bytes"] / run_us / 1e3, 1),
-                            frac=round(it["bytes"] / run_us / 1e3 / HBM_PEAK_GBS, 4),
-                            prep_kernel="k_gemv_prep", prep_avg_us=round(prep_us, 3)))
+                            bytes_per_launch=it["bytes"], avg_us=round(one_us, 3),
+                            gbs=round(it["bytes"] / one_us / 1e3, 1),
+                            frac=round(it["bytes"] / one_us / 1e3 / HBM_PEAK_GBS, 4),
+                            two_step=dict(prep_kernel="k_gemv_prep", prep_avg_us=round(prep_us, 3),
+                                          run_avg_us=round(run_us, 3))))
     # the dominant kernel: the GEMV kernel (by name) with the largest share
     # of a step; its roofline counts the packed bytes of all its launches
     by_name = {}
@@ -213,7 +220,8 @@ def main() -> int:
                     avg_us=round(dom["us"] / n_launch, 3))
     log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; kernels: " +
         ", ".join(f"{k['format']}/{k['matrix']} {k['kernel']} {k['avg_us']:.2f}us "
-                  f"{k['gbs']:.0f}GB/s (prep {k['prep_avg_us']:.2f}us)" for k in kernels))
+                  f"{k['gbs']:.0f}GB/s (two-step: prep {k['two_step']['prep_avg_us']:.2f}us + run "
+                  f"{k['two_step']['run_avg_us']:.2f}us)" for k in kernels))
     for it in items:
         del it["copies"]
 

@@ -247,5 +247,7 @@ def upload(host_bytes: np.ndarray, device="cuda"):
 
 
 def workspace(nbytes: int, device="cuda"):
+    """A zero-filled device workspace (the GEMV's split-K row sums must start
+    at zero; every GEMV call leaves them so)."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)

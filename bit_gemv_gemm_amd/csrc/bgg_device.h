@@ -71,14 +71,16 @@ __device__ __forceinline__ void fwht128_unscaled(float v[8], int lane16) {
   }
 }
 
-__device__ __forceinline__ void load8h(const uint16_t* p, float v[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack8h(const uint4 u, float v[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = h2f((uint16_t)(w[i] & 0xFFFF));
     v[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
   }
+}
+__device__ __forceinline__ void load8h(const uint16_t* p, float v[8]) {
+  unpack8h(*reinterpret_cast<const uint4*>(p), v);
 }
 
 // PQ2_0: 16 codes of one word -> codes of even positions in the low two

@@ -64,24 +64,58 @@ __host__ __device__ inline int gemv_m_bucket(int64_t M) { return M <= 1 ? 1 : M 
 // wave's LDS staging area) and the block's sum of q and 2^(e-14) to
 // metaQ/metaF (zero for an all-zero block and for blocks past G).
 // ---------------------------------------------------------------------------
+// The raw fp16 values of the NG blocks, 16 bytes per lane and pass; a
+// kernel that also streams weights issues these loads first, so that waiting
+// for them does not wait for the weights (loads complete in issue order).
 template <int NG>
-__device__ __forceinline__ void wave_encode(const uint16_t* __restrict__ x, int64_t G, int64_t g0,
-                                            bool token_valid, int rotate, uint16_t* sd, int lane,
-                                            int32_t* __restrict__ metaQ, float* __restrict__ metaF,
-                                            int64_t gpad) {
+struct EncodeRaw {
+  uint4 v[(NG + 3) / 4];
+};
+// What wave_encode_finish leaves in registers: per pass, the sum of q and
+// 2^(e-14) of the block that the lane worked on (all 16 lanes of a block
+// hold them).
+template <int NG>
+struct EncodeMeta {
+  int q[(NG + 3) / 4];
+  float f[(NG + 3) / 4];
+  // block i's values, wave-uniform (read from lane 16 (i % 4))
+  __device__ __forceinline__ int q_of(int i) const {
+    return __builtin_amdgcn_readlane(q[i / 4], 16 * (i % 4));
+  }
+  __device__ __forceinline__ float f_of(int i) const {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f[i / 4]), 16 * (i % 4)));
+  }
+};
+template <int NG>
+__device__ __forceinline__ EncodeRaw<NG> wave_encode_load(const uint16_t* __restrict__ x, int64_t G,
+                                                          int64_t g0, bool token_valid, int lane) {
   const int gl = lane >> 4, lane16 = lane & 15;
+  EncodeRaw<NG> r;
+#pragma unroll
+  for (int pass = 0; pass < (NG + 3) / 4; ++pass) {
+    const int gi = pass * 4 + gl;
+    const int64_t g = g0 + gi;
+    r.v[pass] = gi < NG && g < G && token_valid
+                    ? *reinterpret_cast<const uint4*>(x + g * kGroup + lane16 * 8)
+                    : make_uint4(0, 0, 0, 0);
+  }
+  return r;
+}
+template <int NG>
+__device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>& r, int64_t g0,
+                                                             int rotate, uint16_t* sd, int lane,
+                                                             int32_t* __restrict__ metaQ,
+                                                             float* __restrict__ metaF,
+                                                             int64_t gpad) {
+  const int gl = lane >> 4, lane16 = lane & 15;
+  EncodeMeta<NG> meta;
 #pragma unroll
   for (int pass = 0; pass < (NG + 3) / 4; ++pass) {
     const int gi = pass * 4 + gl;  // block within the NG
     const int64_t g = g0 + gi;
     const bool in_set = gi < NG;
     float v[8];
-    if (in_set && g < G && token_valid) {
-      load8h(x + g * kGroup + lane16 * 8, v);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-    }
+    unpack8h(r.v[pass], v);
     if (rotate) {
       fwht128_unscaled(v, lane16);
 #pragma unroll
@@ -108,17 +142,24 @@ __device__ __forceinline__ void wave_encode(const uint16_t* __restrict__ x, int6
                      nib[6] | nib[7] << 16);
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
+    const float f = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
+    meta.q[pass] = qsum;
+    meta.f[pass] = f;
     if (in_set && lane16 == 0 && g < gpad) {
       metaQ[g] = qsum;
-      metaF[g] = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
+      metaF[g] = f;
     }
   }
+  return meta;
 }
 
-// The wave's own LDS writes are visible to all its lanes after this (LDS
-// executes a wave's instructions in order; the clobber keeps the compiler
-// from moving memory accesses across it).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// The wave's own LDS writes are visible to all its lanes after this: LDS
+// executes a wave's instructions in order, and the fence keeps the compiler
+// from moving the reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
 
 // PQ2_0 digit words of chunks c0 .. c0+2*NG-1 (those below C) from sd:
 // word (d, par, L) of chunk c holds in nibble n digit L of q at chunk
@@ -198,28 +239,22 @@ __device__ __forceinline__ void ptq1_token_slot(int m, int Mreal, int* tg0, int*
 // ---------------------------------------------------------------------------
 // activation prep kernel: one wave per unit of five blocks and token slot.
 // grid: (ceil(Gpad / 5), token slots); block: 64 threads.  Tokens past Mreal
-// get zeros.  Also clears the split-K row sums.
+// get zeros.
 // ---------------------------------------------------------------------------
 template <int FMT>
 __global__ void __launch_bounds__(64)
     k_gemv_prep(const uint16_t* __restrict__ x, int64_t K, int Mreal, int rotate,
                 uint32_t* __restrict__ frag, int64_t frag_words_per_token,
-                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad,
-                uint4* __restrict__ zero, int64_t nzero) {
+                int32_t* __restrict__ metaQ, float* __restrict__ metaF, int64_t gpad) {
   __shared__ __attribute__((aligned(16))) uint16_t sd[kPrepGroups * kGroup];
   const int lane = threadIdx.x;
-  {
-    // clear the row sums of the split-K GEMV (every GEMV launch leaves them
-    // at zero again; this covers a workspace that was used for something else)
-    const int64_t nth = (int64_t)(gridDim.x * gridDim.y) * 64;
-    for (int64_t i = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * 64 + lane; i < nzero; i += nth)
-      zero[i] = make_uint4(0, 0, 0, 0);
-  }
   const int m = blockIdx.y;
   const int64_t G = K / kGroup;
   const int64_t g0 = (int64_t)blockIdx.x * kPrepGroups;
-  wave_encode<kPrepGroups>(x + (int64_t)m * K, G, g0, m < Mreal, rotate, sd, lane,
-                           metaQ + (int64_t)m * gpad, metaF + (int64_t)m * gpad, gpad);
+  const EncodeRaw<kPrepGroups> raw = wave_encode_load<kPrepGroups>(x + (int64_t)m * K, G, g0,
+                                                                   m < Mreal, lane);
+  wave_encode_finish<kPrepGroups>(raw, g0, rotate, sd, lane, metaQ + (int64_t)m * gpad,
+                                  metaF + (int64_t)m * gpad, gpad);
   wave_lds_sync();
   if (FMT == BGG_FMT_PQ2_0) {
     wave_pack_pq2<kPrepGroups>(sd, frag + (int64_t)m * frag_words_per_token, 2 * g0, K / 64, lane);
@@ -252,6 +287,13 @@ constexpr int kSumCountShift = 57;
 constexpr uint64_t kSumBias = 1ull << 49;
 constexpr uint64_t kSumMask = (1ull << kSumCountShift) - 1;
 constexpr int kMaxSumSlices = 127;  // arrivals the count field holds
+// The row sums sit at the start of every GEMV workspace, whatever the format,
+// K, M and N: kSumSlots token slots of kSumRows words.  A launch covers at
+// most kSumRows rows of split tiles.  Every launch leaves the words it used
+// at zero, so a zero-filled workspace stays ready for any GEMV call.
+constexpr int64_t kSumSlots = 4;
+constexpr int64_t kSumRows = 65536;
+constexpr uint64_t kSumBytes = (uint64_t)kSumSlots * kSumRows * 8;  // 2 MiB
 
 __device__ __forceinline__ uint64_t sum_term(float s) {
   const double lim = (double)(kSumBias - 1);
@@ -262,7 +304,7 @@ __device__ __forceinline__ uint64_t sum_term(float s) {
 template <int M, int W>
 __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M][64], int wave,
                                           int lane, int64_t row, int64_t N, int Mreal, int Sg,
-                                          int64_t rows_pad, unsigned long long* __restrict__ sums,
+                                          int64_t local_row, unsigned long long* __restrict__ sums,
                                           uint16_t* __restrict__ y) {
 #pragma unroll
   for (int m = 0; m < M; ++m) red[wave][m][lane] = acc[m];
@@ -283,7 +325,7 @@ __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M]
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    unsigned long long* word = &sums[(int64_t)m * rows_pad + row];
+    unsigned long long* word = &sums[(int64_t)m * kSumRows + local_row];
     const uint64_t term = sum_term(s[m]);
     const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -340,18 +382,48 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
 }
 
 // ---------------------------------------------------------------------------
+// One-launch GEMV for one token: every wave first encodes the activation
+// blocks of its own K slice (the same words the prep kernel writes, at the
+// same places in the workspace), then reads them back with scalar loads.
+// Workgroups that cover the same K slice write identical words.  The wave
+// waits for its own stores (s_waitcnt vmcnt(0): stores complete in L2)
+// before its first scalar load; the scalar cache is invalidated at every
+// launch, and the digit words of a PQ2_0 group (256 bytes) or a PTQ1_0
+// period (2112 bytes) fill whole 64-byte lines, so a line is only read after
+// it was written and cannot hold another call's words.  The per-block meta
+// (4 bytes per block, many blocks to a line) is taken from the registers of
+// the lanes that computed it instead.  The writes
+// go through their own pointers so that the compiler, which cannot see that
+// they reach the memory the scalar loads read, keeps those loads scalar;
+// the wait and a scheduling barrier keep them after the stores.
+// ---------------------------------------------------------------------------
+struct FuseArgs {
+  const uint16_t* x;  // the token row, K fp16 values
+  uint32_t* frag;     // = the kernel's frag / metaQ / metaF
+  int32_t* metaQ;
+  float* metaF;
+  int rotate;
+};
+__device__ __forceinline__ void wait_own_stores() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
 // PQ2_0: wave = 64 rows x BPS groups; workgroup = W consecutive K slices.
 // grid: NT * Sg workgroups of 64*W threads.
 // ---------------------------------------------------------------------------
-template <int M, int BPS, int W>
+template <int M, int BPS, int W, bool FUSE>
 __global__ void __launch_bounds__(64 * W)
     k_gemv_pq2(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
                int64_t rows_pad, int64_t tile0, int64_t ntl,
-               int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
+               int64_t nta, int sgb, int light_last, FuseArgs fa, uint16_t* __restrict__ y) {
+  static_assert(!FUSE || M == 1, "the one-launch GEMV is for one token");
   __shared__ float red[W][M][64];
+  __shared__ __attribute__((aligned(16))) uint16_t sd_stage[FUSE ? W * BPS * kGroup : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
@@ -367,6 +439,8 @@ __global__ void __launch_bounds__(64 * W)
     const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
     const uint16_t* sdata =
         reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
+    EncodeRaw<BPS> xraw;
+    if (FUSE) xraw = wave_encode_load<BPS>(fa.x, G, gbeg, true, lane);
     // Every load of the slice is issued before any is used, without branches
     // (a group past G re-reads group G-1 and gets a zero weight below).
     uint4 w[2 * BPS];
@@ -381,15 +455,33 @@ __global__ void __launch_bounds__(64 * W)
     // per-group activation scale and digit sum, for every token
     float gf[BPS][M];
     int gq[BPS][M];
+    if (FUSE) {
+      __builtin_amdgcn_sched_barrier(0);
+      uint16_t* sdw = sd_stage + wave * (BPS * kGroup);
+      const EncodeMeta<BPS> em =
+          wave_encode_finish<BPS>(xraw, gbeg, fa.rotate, sdw, lane, fa.metaQ, fa.metaF, gpad);
+      wave_lds_sync();
+      wave_pack_pq2<BPS>(sdw, fa.frag, 2 * gbeg, C, lane);
+      // the group meta straight from the registers: other waves' meta share
+      // its cache lines, and a scalar load could cache them before they are
+      // written (zero past G, like the prepared meta)
 #pragma unroll
-    for (int i = 0; i < BPS; ++i)
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const bool gv = gbeg + i < G;
-        const int64_t g = gv ? gbeg + i : G - 1;
-        gf[i][m] = gv ? metaF[(int64_t)m * gpad + g] : 0.0f;
-        gq[i][m] = metaQ[(int64_t)m * gpad + g];
+      for (int i = 0; i < BPS; ++i) {
+        gf[i][0] = em.f_of(i);
+        gq[i][0] = em.q_of(i);
       }
+      wait_own_stores();
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPS; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const bool gv = gbeg + i < G;
+          const int64_t g = gv ? gbeg + i : G - 1;
+          gf[i][m] = gv ? metaF[(int64_t)m * gpad + g] : 0.0f;
+          gq[i][m] = metaQ[(int64_t)m * gpad + g];
+        }
+    }
     // keep the scheduler from sinking the loads towards their uses
     __builtin_amdgcn_sched_barrier(0);
 
@@ -431,7 +523,8 @@ __global__ void __launch_bounds__(64 * W)
       }
     }
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, rows_pad, sums, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg,
+                  ws.local * kTile + lane, sums, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -547,19 +640,21 @@ __device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (
   }
 }
 
-template <int M, int H, int W>
+template <int M, int H, int W, bool FUSE>
 __global__ void __launch_bounds__(64 * W)
     k_gemv_ptq1(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
                 int64_t rows_pad, int64_t tile0, int64_t ntl,
-                int64_t nta, int sgb, int light_last, uint16_t* __restrict__ y) {
+                int64_t nta, int sgb, int light_last, FuseArgs fa, uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
+  static_assert(!FUSE || M == 1, "the one-launch GEMV is for one token");
   __shared__ uint32_t lut[256 * kLutRowBytes / 4];
   __shared__ uint32_t lut_seed[256];
   __shared__ float red[W][M][64];
+  __shared__ __attribute__((aligned(16))) uint16_t sd_stage[FUSE ? W * kPeriodGroups * kGroup : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
@@ -580,6 +675,8 @@ __global__ void __launch_bounds__(64 * W)
   // zeros for positions past K), so they add nothing.
   uint4 w[CH];
   uint32_t sr[kPeriodGroups];
+  EncodeRaw<kPeriodGroups> xraw;
+  if (FUSE && active) xraw = wave_encode_load<kPeriodGroups>(fa.x, G, p * kPeriodGroups, true, lane);
   if (active) {
     // scales first: all of them are needed before the first byte
 #pragma unroll
@@ -589,8 +686,17 @@ __global__ void __launch_bounds__(64 * W)
     for (int c = 0; c < CH; ++c) w[c] = ld_stream(tdata + (p * kPeriodChunks + part * CH + c) * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
+  EncodeMeta<kPeriodGroups> em;
+  if (FUSE && active) {
+    uint16_t* sdw = sd_stage + wave * (kPeriodGroups * kGroup);
+    em = wave_encode_finish<kPeriodGroups>(xraw, p * kPeriodGroups, fa.rotate, sdw, lane, fa.metaQ,
+                                           fa.metaF, gpad);
+    wave_lds_sync();
+    wave_pack_ptq1(sdw, fa.frag + p * kPtqFragWords, 1, 0, lane);
+  }
   build_lut32(lut, lut_seed);
   __syncthreads();
+  if (FUSE && active) wait_own_stores();
 
   float acc[M];
 #pragma unroll
@@ -603,8 +709,9 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
     for (int k = 0; k < kPeriodGroups; ++k) {
       sc[k] = scale_half(sr[k], lane);
+      // fused: from the registers (other periods' meta share its cache lines)
 #pragma unroll
-      for (int m = 0; m < M; ++m) gf[k][m] = metaF[(int64_t)m * gpad + gp + k];
+      for (int m = 0; m < M; ++m) gf[k][m] = FUSE ? em.f_of(k) : metaF[(int64_t)m * gpad + gp + k];
     }
     const uint32_t* fp = frag + p * kPtqFragWords * M;
     const uint32_t lane_off = lut_lane_off(lane);
@@ -615,7 +722,8 @@ __global__ void __launch_bounds__(64 * W)
     else
       ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
   }
-  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg, rows_pad, sums, y);
+  wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg,
+                  ws.local * kTile + lane, sums, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,50 +818,47 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   p.nta = p.NT;
   p.sgb = 1;
   static const int64_t split_rest = env_int("BGG_GEMV_SPLIT_REST", 1);
-  if (split_rest && p.Sg == 1 && p.S <= kMaxSumSlices) {
+  if (split_rest && p.Sg == 1 && p.S <= kMaxSumSlices && p.NT * kTile <= kSumRows) {
     const int64_t ncu = device_cus(), r = p.NT % ncu;
     if (p.NT > ncu && r != 0 && r * p.S <= 2 * ncu) {
       p.nta = p.NT - r;
       p.sgb = p.S;
     }
   }
-  const int64_t kb = gemv_m_bucket(M);
-  // [digit words][group Q][group F][row sums]: everything before the row
-  // sums depends only on the format, K and M
-  p.off_frag = 0;
+  // [row sums][digit words][group Q][group F]: the row sums are the same for
+  // every call, the rest depends only on the format, K and M
+  p.off_sums = 0;
+  p.off_frag = kSumBytes;
   uint64_t off = align256(p.off_frag + (uint64_t)p.slots * p.frag_words_per_token * 4);
   p.off_meta_q = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
-  p.off_sums = off;
-  off = align256(off + (p.Sg > 1 || p.sgb > 1 ? (uint64_t)kb * p.rows_pad * 8 : 0));
   p.total = off;
   return p;
 }
 
 void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x, int64_t M,
-                 int rotate, uint8_t* ws, size_t ws_bytes, hipStream_t st) {
-  // the row sums: everything from their offset to the end of the workspace
-  // (a workspace sized for the largest matrix that this preparation serves)
-  uint4* zero = reinterpret_cast<uint4*>(ws + p.off_sums);
-  const int64_t nzero = (int64_t)((ws_bytes - p.off_sums) / 16);
+                 int rotate, uint8_t* ws, hipStream_t st) {
   uint32_t* frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
   int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
   if (d->format == BGG_FMT_PQ2_0)
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(64), 0, st, x, d->K, (int)M,
-                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
+                       rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
   else
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PTQ1_0>, grid, dim3(64), 0, st, x, d->K,
-                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad, zero, nzero);
+                       (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
 }
 
-// GEMV over all weight rows for tokens m0 .. m0+Mreal-1, one launch.
-template <int M>
+// GEMV over all weight rows for tokens m0 .. m0+Mreal-1 (one launch, or one
+// per kSumRows rows of split tiles).  With FUSE (one token) the kernel also
+// encodes the activations from fa.x.
+template <int M, bool FUSE>
 void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
-                 uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, hipStream_t st) {
+                 uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, const FuseArgs& fa,
+                 hipStream_t st) {
   const uint32_t* frag =
       reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
   const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
@@ -762,42 +867,55 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
   uint16_t* yg = y + m0 * d->N;
   const int Sg = (int)p.Sg;
   const dim3 block((unsigned)(64 * p.W));
-  // with one-wave slices (p.sgb > 1): nta full tiles, the rest in one-wave
-  // slices; else every tile has Sg slices
-  const int64_t t0 = 0, ntl = p.NT;
-  const int64_t nta = p.sgb > 1 ? p.nta : ntl;
-  const int sgb = (int)p.sgb;
-  static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
-  const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
-  const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
-  if (d->format == BGG_FMT_PQ2_0) {
+  // split tiles add into the row sums, which hold kSumRows rows: one launch
+  // per kSumRows / 64 tiles (one-wave slices only in a single launch)
+  const int64_t chunk = Sg > 1 ? kSumRows / kTile : p.NT;
+  for (int64_t t0 = 0; t0 < p.NT; t0 += chunk) {
+    const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
+    // with one-wave slices (p.sgb > 1): nta full tiles, the rest in one-wave
+    // slices; else every tile has Sg slices
+    const int64_t nta = p.sgb > 1 ? p.nta : ntl;
+    const int sgb = (int)p.sgb;
+    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
+    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
+    const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
+    if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
-  hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8>), grid, block, 0, st, packed, d->scale_offset,       \
+  hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8, FUSE>), grid, block, 0, st, packed, d->scale_offset, \
                      d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, yg)
-    switch (p.per_slice) {
-      case 8: BGG_PQ2(8); break;
-      case 5: BGG_PQ2(5); break;
-      case 4: BGG_PQ2(4); break;
-      default: BGG_PQ2(2); break;
-    }
+                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, fa, yg)
+      switch (p.per_slice) {
+        case 8: BGG_PQ2(8); break;
+        case 5: BGG_PQ2(5); break;
+        case 4: BGG_PQ2(4); break;
+        default: BGG_PQ2(2); break;
+      }
 #undef BGG_PQ2
-  } else {
-    // 16-wave workgroups only for the one- and two-token kernels (register
-    // budget); p.W says which one the plan was made for
-    constexpr int W16 = M >= 4 ? 8 : 16;
-    constexpr int H2 = M == 1 ? 2 : 1;
-#define BGG_PTQ1(H, WW)                                                                           \
-  hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW>), grid, block, 0, st, packed, d->scale_offset,       \
-                     d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, yg)
-    if (p.W == 16) {
-      if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
     } else {
-      if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
-    }
+      // 16-wave workgroups only for the one- and two-token kernels (register
+      // budget); p.W says which one the plan was made for
+      constexpr int W16 = M >= 4 ? 8 : 16;
+      constexpr int H2 = M == 1 ? 2 : 1;
+#define BGG_PTQ1(H, WW)                                                                           \
+  hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW, FUSE>), grid, block, 0, st, packed,                \
+                     d->scale_offset, d->chunks, p.G, d->N, Sg, Mreal, frag,                     \
+                     p.frag_words_per_token, mq, mf, p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, \
+                     light, fa, yg)
+      if (p.W == 16) {
+        if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
+      } else {
+        if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
+      }
 #undef BGG_PTQ1
+    }
   }
+}
+
+// One-launch GEMV for a single token, per format (BGG_GEMV_FUSE: bit 0
+// PQ2_0, bit 1 PTQ1_0; a cleared bit means prep kernel + GEMV kernel).
+bool gemv_fuse_enabled(int format) {
+  static const int64_t mask = env_int("BGG_GEMV_FUSE", 3);
+  return (mask >> (format == BGG_FMT_PQ2_0 ? 0 : 1)) & 1;
 }
 
 bgg_status gemv_args_check(const char* who, const bgg_weights_desc* d, int64_t M,
@@ -838,12 +956,13 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
     return fail(BGG_ERR_SHAPE, "bgg_gemv_kernel_name: M must be in 1..16 (got %lld)", (long long)M);
   const GemvPlan p = plan_gemv(d, M);
   const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
+  const char* fused = M == 1 && gemv_fuse_enabled(d->format) ? "true" : "false";
   int n;
   if (d->format == BGG_FMT_PQ2_0) {
-    n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8>", mb, (int)p.per_slice);
+    n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8, %s>", mb, (int)p.per_slice, fused);
   } else {
     const int h = (p.per_slice == 2 && mb == 1) ? 2 : 1;
-    n = snprintf(out, cap, "k_gemv_ptq1<%d, %d, %d>", mb, h, mb >= 4 ? 8 : (int)p.W);
+    n = snprintf(out, cap, "k_gemv_ptq1<%d, %d, %d, %s>", mb, h, mb >= 4 ? 8 : (int)p.W, fused);
   }
   if (n < 0 || (size_t)n >= cap)
     return fail(BGG_ERR_BUFFER, "bgg_gemv_kernel_name: %zu bytes are too few", cap);
@@ -860,7 +979,7 @@ bgg_status bgg_gemv_prepare(const bgg_weights_desc* d, const void* x_dev, int64_
   if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
     return fail(BGG_ERR_SHAPE, "bgg_gemv_prepare: unknown flags 0x%x", flags);
   launch_prep(d, p, (const uint16_t*)x_dev, M, (flags & BGG_ROTATE_INPUT) ? 1 : 0,
-              (uint8_t*)workspace, workspace_bytes, (hipStream_t)stream);
+              (uint8_t*)workspace, (hipStream_t)stream);
   return hip_check("bgg_gemv_prepare");
 }
 
@@ -879,9 +998,9 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* d, const void* packed_dev, void*
   for (int64_t m0 = 0; m0 < M; m0 += kGemvTokens) {
     const int mg = (int)(M - m0 < kGemvTokens ? M - m0 : kGemvTokens);
     switch (gemv_m_bucket(mg)) {
-      case 1: launch_gemv<1>(d, p, pk, y, m0, mg, ws, s); break;
-      case 2: launch_gemv<2>(d, p, pk, y, m0, mg, ws, s); break;
-      default: launch_gemv<4>(d, p, pk, y, m0, mg, ws, s); break;
+      case 1: launch_gemv<1, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
+      case 2: launch_gemv<2, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
+      default: launch_gemv<4, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
     }
     if ((st = hip_check("bgg_gemv_run"))) return st;
   }
@@ -896,9 +1015,31 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
   if (!packed_dev || !y_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemv: NULL buffer");
   if (!aligned16(packed_dev) || ((uintptr_t)y_dev & 1))
     return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned buffer");
-  st = bgg_gemv_prepare(d, x_dev, M, flags, workspace, workspace_bytes, stream);
+  // (the one-launch kernel wants the digit words of a block or period to
+  // fill whole 64-byte lines: a workspace aligned to 64 bytes)
+  if (M != 1 || !gemv_fuse_enabled(d->format) || ((uintptr_t)workspace & 63)) {
+    st = bgg_gemv_prepare(d, x_dev, M, flags, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return bgg_gemv_run(d, packed_dev, y_dev, M, workspace, workspace_bytes, stream);
+  }
+  // one token: a single launch that also encodes the activations
+  GemvPlan p;
+  st = gemv_args_check("bgg_ternary_gemv", d, M, workspace, workspace_bytes, &p);
   if (st) return st;
-  return bgg_gemv_run(d, packed_dev, y_dev, M, workspace, workspace_bytes, stream);
+  if (!x_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemv: NULL x");
+  if (!aligned16(x_dev)) return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned x");
+  if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
+    return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: unknown flags 0x%x", flags);
+  uint8_t* ws = (uint8_t*)workspace;
+  FuseArgs fa;
+  fa.x = (const uint16_t*)x_dev;
+  fa.frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
+  fa.metaQ = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
+  fa.metaF = reinterpret_cast<float*>(ws + p.off_meta_f);
+  fa.rotate = (flags & BGG_ROTATE_INPUT) ? 1 : 0;
+  launch_gemv<1, true>(d, p, (const uint8_t*)packed_dev, (uint16_t*)y_dev, 0, 1, ws, fa,
+                       (hipStream_t)stream);
+  return hip_check("bgg_ternary_gemv");
 }
 
 }  // extern "C"

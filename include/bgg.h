@@ -179,8 +179,15 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *               else already rotated)
  *   y_dev       device fp16 [M][N]
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
- *               bytes; its contents need no initialisation and are scratch.
- * Equivalent to bgg_gemv_prepare followed by bgg_gemv_run.
+ *               bytes, 16-byte aligned (64-byte aligned for the one-launch
+ *               path below).  Its first 2 MiB hold the row sums of split-K
+ *               launches, which must be zero when a call starts: zero-fill a
+ *               new workspace once; every GEMV call (any format, K, M or N)
+ *               leaves them zero again.  A workspace used for anything else
+ *               in between must be zero-filled again.  The rest is scratch.
+ * For M == 1 one kernel launch encodes the activations and computes y;
+ * otherwise it is bgg_gemv_prepare followed by bgg_gemv_run.  Both give the
+ * same bits.
  * Each 64-row tile is read once per group of up to four tokens (one kernel
  * launch per group), all tokens of the group at a time.  The
  * activations are carried as 15-bit integers with a power-of-two scale per
@@ -203,10 +210,7 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev
  *
  * bgg_gemv_prepare: transform (with BGG_ROTATE_INPUT) and encode the M
  * activation rows x_dev (fp16 [M][K]) into `workspace`.  What it writes
- * there depends only on the format, K and M of `desc`; it also clears the
- * workspace from the end of that data to workspace_bytes (the row sums of
- * split-K runs, which every run leaves cleared), so pass the size that the
- * largest matrix to be run needs rather than a much larger buffer.
+ * there depends only on the format, K and M of `desc`.
  *
  * bgg_gemv_run: y_dev (fp16 [M][N]) = the product of the packed matrix with
  * the activations last prepared in `workspace` (stream order).  Any matrix
@@ -221,8 +225,12 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
                         int64_t M, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The name under which a profiler lists the GEMV kernel that
- * bgg_gemv_run launches for the first group of up to four of M tokens, e.g.
- * "k_gemv_ptq1<1, 1, 8>" (host only; for matching profiles to calls).
+ * bgg_ternary_gemv launches for the first group of up to four of M tokens,
+ * e.g. "k_gemv_ptq1<1, 1, 8, true>" (host only; for matching profiles to
+ * calls).  The last template argument is true for the one-launch kernel
+ * that also encodes the activations (M == 1) and false for the kernel that
+ * reads a preparation (bgg_gemv_run launches that one, with the same other
+ * arguments).
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);

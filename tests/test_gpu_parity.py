@@ -173,6 +173,36 @@ def test_gemv_projection_full_size(env, fmt, name):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (300, 640), (100, 1152), (64, 128)])
+def test_gemv_one_launch_matches_two_step(env, fmt, N, K):
+    """For one token bgg_ternary_gemv runs a single kernel that also encodes
+    x; it must give the bits of bgg_gemv_prepare + bgg_gemv_run, call after
+    call on one workspace with a different x each time (no call may read
+    another call's encoded activations), with and without the transform."""
+    bgg, torch = env
+    say(f"gemv one-launch vs two-step {fmt} {N}x{K}")
+    T, S = gen_matrix(71, 9, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    assert bgg.bgg_gemv_kernel_name(d.desc, 1).endswith("true>")
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 1))
+    for i in range(4):
+        flags = bgg.BGG_ROTATE_INPUT if i != 2 else 0
+        x = synth.activations_f16(71, 10 + i, 1, K)
+        xd = torch.from_numpy(x).cuda()
+        y1 = torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda")
+        y2 = torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda")
+        bgg.bgg_ternary_gemv(d.desc, d.packed, xd, y1, 1, flags, ws)
+        bgg.bgg_gemv_prepare(d.desc, xd, 1, flags, ws)
+        bgg.bgg_gemv_run(d.desc, d.packed, y2, 1, ws)
+        torch.cuda.synchronize()
+        a, b = y1.cpu().numpy(), y2.cpu().numpy()
+        assert not np.isnan(a).any()
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"call {i}"
+        if i == 0 and N * K <= 1 << 20:
+            assert np.all(relerr(a, oracle_y(fmt, T, S, x)) <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_basis_vectors_bit_exact(env, fmt):
     """Rotation off and x = e_k: y_n = S[n][k/128] * T[n][k] exactly."""
     bgg, torch = env
