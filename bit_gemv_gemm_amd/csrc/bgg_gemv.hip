@@ -145,7 +145,7 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
     const float f = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
     meta.q[pass] = qsum;
     meta.f[pass] = f;
-    if (in_set && lane16 == 0 && g < gpad) {
+    if (metaQ && in_set && lane16 == 0 && g < gpad) {
       metaQ[g] = qsum;
       metaF[g] = f;
     }
@@ -383,9 +383,10 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
 
 // ---------------------------------------------------------------------------
 // One-launch GEMV for one token: every wave first encodes the activation
-// blocks of its own K slice (the same words the prep kernel writes, at the
-// same places in the workspace), then reads them back with scalar loads.
-// Workgroups that cover the same K slice write identical words.  The wave
+// blocks of its own K slice (the same words the prep kernel writes, laid out
+// the same way, in one of kFuseCopies copies in the workspace), then reads
+// them back with scalar loads.  Workgroups that cover the same K slice and
+// copy write identical words.  The wave
 // waits for its own stores (s_waitcnt vmcnt(0): stores complete in L2)
 // before its first scalar load; the scalar cache is invalidated at every
 // launch, and the digit words of a PQ2_0 group (256 bytes) or a PTQ1_0
@@ -399,11 +400,17 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
 // ---------------------------------------------------------------------------
 struct FuseArgs {
   const uint16_t* x;  // the token row, K fp16 values
-  uint32_t* frag;     // = the kernel's frag / metaQ / metaF
-  int32_t* metaQ;
+  uint32_t* frag;     // = the kernel's frag: kFuseCopies copies of the digit words
+  int32_t* metaQ;     // null: the meta stays in registers
   float* metaF;
   int rotate;
 };
+// Workgroup b writes and reads copy b % kFuseCopies of the digit words: when
+// every workgroup of the launch wrote the same lines, the scalar loads of
+// those lines waited behind the stream of identical writes from the other
+// CUs (3.5 us more for a PTQ1_0 projection).  Workgroups are dispatched to
+// the 8 XCDs in turn, so each copy is written by a few workgroups of one XCD.
+constexpr int64_t kFuseCopies = 64;
 __device__ __forceinline__ void wait_own_stores() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __builtin_amdgcn_sched_barrier(0);
@@ -441,6 +448,7 @@ __global__ void __launch_bounds__(64 * W)
         reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
     EncodeRaw<BPS> xraw;
     if (FUSE) xraw = wave_encode_load<BPS>(fa.x, G, gbeg, true, lane);
+    const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
     // Every load of the slice is issued before any is used, without branches
     // (a group past G re-reads group G-1 and gets a zero weight below).
     uint4 w[2 * BPS];
@@ -461,7 +469,7 @@ __global__ void __launch_bounds__(64 * W)
       const EncodeMeta<BPS> em =
           wave_encode_finish<BPS>(xraw, gbeg, fa.rotate, sdw, lane, fa.metaQ, fa.metaF, gpad);
       wave_lds_sync();
-      wave_pack_pq2<BPS>(sdw, fa.frag, 2 * gbeg, C, lane);
+      wave_pack_pq2<BPS>(sdw, fa.frag + fcopy, 2 * gbeg, C, lane);
       // the group meta straight from the registers: other waves' meta share
       // its cache lines, and a scalar load could cache them before they are
       // written (zero past G, like the prepared meta)
@@ -501,7 +509,7 @@ __global__ void __launch_bounds__(64 * W)
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const uint32_t* xf = frag + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
+        const uint32_t* xf = frag + fcopy + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
         int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -686,15 +694,17 @@ __global__ void __launch_bounds__(64 * W)
     for (int c = 0; c < CH; ++c) w[c] = ld_stream(tdata + (p * kPeriodChunks + part * CH + c) * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
+  const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
+  // the LUT is built while the loads are in flight (with FUSE: while x is)
+  build_lut32(lut, lut_seed);
   EncodeMeta<kPeriodGroups> em;
   if (FUSE && active) {
     uint16_t* sdw = sd_stage + wave * (kPeriodGroups * kGroup);
     em = wave_encode_finish<kPeriodGroups>(xraw, p * kPeriodGroups, fa.rotate, sdw, lane, fa.metaQ,
                                            fa.metaF, gpad);
     wave_lds_sync();
-    wave_pack_ptq1(sdw, fa.frag + p * kPtqFragWords, 1, 0, lane);
+    wave_pack_ptq1(sdw, fa.frag + fcopy + p * kPtqFragWords, 1, 0, lane);
   }
-  build_lut32(lut, lut_seed);
   __syncthreads();
   if (FUSE && active) wait_own_stores();
 
@@ -713,7 +723,7 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
       for (int m = 0; m < M; ++m) gf[k][m] = FUSE ? em.f_of(k) : metaF[(int64_t)m * gpad + gp + k];
     }
-    const uint32_t* fp = frag + p * kPtqFragWords * M;
+    const uint32_t* fp = frag + fcopy + p * kPtqFragWords * M;
     const uint32_t lane_off = lut_lane_off(lane);
     const char* lbase = reinterpret_cast<const char*>(lut);
     static_assert(H == 1 || H == 2, "one or two parts per period");
@@ -746,7 +756,7 @@ int64_t env_int(const char* name, int64_t dflt) {
 // 64-bit row sums), and the workspace layout.
 struct GemvPlan {
   int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
-  uint64_t off_frag, off_meta_q, off_meta_f, off_sums, total;
+  uint64_t off_frag, off_meta_q, off_meta_f, off_sums, off_fuse, total;
   int64_t nta, sgb;  // tiles with Sg slices; one-wave slices of the rest
 };
 
@@ -834,6 +844,10 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
+  // the one-launch kernel's copies of one token's digit words (reserved for
+  // every M, so that a workspace sized for more tokens serves fewer)
+  p.off_fuse = off;
+  off = align256(off + (uint64_t)kFuseCopies * p.frag_words_per_token * 4);
   p.total = off;
   return p;
 }
@@ -860,7 +874,8 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
                  uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, const FuseArgs& fa,
                  hipStream_t st) {
   const uint32_t* frag =
-      reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
+      FUSE ? reinterpret_cast<const uint32_t*>(ws + p.off_fuse)
+           : reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
   const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
   const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f) + m0 * p.gpad;
   unsigned long long* sums = reinterpret_cast<unsigned long long*>(ws + p.off_sums);
@@ -1033,9 +1048,9 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
   uint8_t* ws = (uint8_t*)workspace;
   FuseArgs fa;
   fa.x = (const uint16_t*)x_dev;
-  fa.frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
-  fa.metaQ = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
-  fa.metaF = reinterpret_cast<float*>(ws + p.off_meta_f);
+  fa.frag = reinterpret_cast<uint32_t*>(ws + p.off_fuse);
+  fa.metaQ = nullptr;
+  fa.metaF = nullptr;
   fa.rotate = (flags & BGG_ROTATE_INPUT) ? 1 : 0;
   launch_gemv<1, true>(d, p, (const uint8_t*)packed_dev, (uint16_t*)y_dev, 0, 1, ws, fa,
                        (hipStream_t)stream);
