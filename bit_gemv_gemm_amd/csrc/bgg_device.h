@@ -45,10 +45,39 @@ __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__flo
 // 1/sqrt(128) rounded to fp32.
 constexpr float kHadamardNorm = 0.08838834764831845f;
 
+// v of lane l ^ m within each group of 16 lanes (m = 1, 2, 4 or 8), with
+// DPP lane moves, which cost no LDS trip: m = 1, 2 are quad permutations,
+// m = 8 a rotation of the 16-lane row by 8, and m = 4 two row shifts that
+// each write only the 4-lane banks that read in their direction.
+template <int m>
+__device__ __forceinline__ int xor16_i(int v) {
+  static_assert(m == 1 || m == 2 || m == 4 || m == 8, "xor16: m in {1, 2, 4, 8}");
+  if (m == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if (m == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if (m == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  // lanes 0-3, 8-11 (banks 0, 2) read l + 4 (row_shl:4); lanes 4-7, 12-15
+  // (banks 1, 3) read l - 4 (row_shr:4)
+  const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);
+  return __builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false);
+}
+template <int m>
+__device__ __forceinline__ float xor16_f(float v) {
+  return __int_as_float(xor16_i<m>(__float_as_int(v)));
+}
+
 // Fast Walsh-Hadamard transform (Sylvester order, unnormalised) of one
 // 128-block held by 16 lanes, 8 consecutive values each (lane i of the 16
 // holds positions 8i..8i+7).  Butterflies (a, b) -> (a + b, a - b) over
 // strides 1..64, in fp32.
+template <int m>
+__device__ __forceinline__ void fwht_lane_stage(float v[8], int lane16) {
+  const float sgn = (lane16 & m) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = xor16_f<m>(v[i]);
+    v[i] = fmaf(sgn, v[i], p);  // low lane: v + p; high lane: p - v
+  }
+}
 __device__ __forceinline__ void fwht128_unscaled(float v[8], int lane16) {
 #pragma unroll
   for (int s = 1; s < 8; s <<= 1) {
@@ -60,15 +89,10 @@ __device__ __forceinline__ void fwht128_unscaled(float v[8], int lane16) {
         v[i + s] = a - b;
       }
   }
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const float sgn = (lane16 & m) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __shfl_xor(v[i], m, 16);
-      v[i] = fmaf(sgn, v[i], p);  // low lane: v + p; high lane: p - v
-    }
-  }
+  fwht_lane_stage<1>(v, lane16);
+  fwht_lane_stage<2>(v, lane16);
+  fwht_lane_stage<4>(v, lane16);
+  fwht_lane_stage<8>(v, lane16);
 }
 
 __device__ __forceinline__ void unpack8h(const uint4 u, float v[8]) {

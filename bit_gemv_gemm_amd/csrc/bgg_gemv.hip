@@ -124,8 +124,10 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+    amax = fmaxf(amax, xor16_f<1>(amax));
+    amax = fmaxf(amax, xor16_f<2>(amax));
+    amax = fmaxf(amax, xor16_f<4>(amax));
+    amax = fmaxf(amax, xor16_f<8>(amax));
     int e = 0;
     frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1): |x'| < 2^e
     int qsum = 0;
@@ -140,8 +142,10 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
       *reinterpret_cast<uint4*>(sd + gi * kGroup + lane16 * 8) =
           make_uint4(nib[0] | nib[1] << 16, nib[2] | nib[3] << 16, nib[4] | nib[5] << 16,
                      nib[6] | nib[7] << 16);
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) qsum += __shfl_xor(qsum, s, 16);
+    qsum += xor16_i<1>(qsum);
+    qsum += xor16_i<2>(qsum);
+    qsum += xor16_i<4>(qsum);
+    qsum += xor16_i<8>(qsum);
     const float f = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
     meta.q[pass] = qsum;
     meta.f[pass] = f;
@@ -697,6 +701,9 @@ __global__ void __launch_bounds__(64 * W)
   const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
   // the LUT is built while the loads are in flight (with FUSE: while x is)
   build_lut32(lut, lut_seed);
+  __syncthreads();
+  // (after the barrier: each wave goes on to its loop as soon as its own
+  // encoding is done)
   EncodeMeta<kPeriodGroups> em;
   if (FUSE && active) {
     uint16_t* sdw = sd_stage + wave * (kPeriodGroups * kGroup);
@@ -704,9 +711,8 @@ __global__ void __launch_bounds__(64 * W)
                                            fa.metaF, gpad);
     wave_lds_sync();
     wave_pack_ptq1(sdw, fa.frag + fcopy + p * kPtqFragWords, 1, 0, lane);
+    wait_own_stores();
   }
-  __syncthreads();
-  if (FUSE && active) wait_own_stores();
 
   float acc[M];
 #pragma unroll
