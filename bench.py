@@ -70,6 +70,105 @@ def measured_traffic(kernel: str):
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def decode_stack_bench(args, bgg, torch, dev, capture):
+    """The full decode step of a 64-layer stack (q, k, v, o, gate, up, down
+    per layer) at M = 1 and the small-batch sweep M = 2, 4, 8, 16, both
+    packings.  Each projection is one bgg_ternary_gemv call that transforms
+    and encodes its own x (448 calls per step).  At M = 1 a second line
+    shares each transform the way a model can: one bgg_gemv_prepare for q, k
+    and v, one for o, one for gate and up, one for down, each followed by
+    bgg_gemv_run per matrix.  Every matrix has its own device buffer; the 64
+    layers reuse layer 0's generated values (the work and the bytes streamed
+    do not depend on them).  GB/s = packed bytes of the step / median wall
+    time of one graph replay."""
+    import numpy as np
+    import synth
+    w = synth.WORKLOADS["decode_step"]
+    seed, mats = w["seed"], w["matrices"]
+    ms = [1] + list(synth.WORKLOADS["small_batch"]["m"])
+    mmax = max(ms)
+    stream = torch.cuda.current_stream()
+    xs = {k: torch.from_numpy(synth.workload_x(seed, mmax, k)).to(dev)
+          for k in sorted({m.k for m in mats})}
+    ys = {n: torch.empty((mmax, n), dtype=torch.float16, device=dev) for n in sorted({m.n for m in mats})}
+    weights = sum(m.n * m.k for m in mats)
+    res = dict(workload=f"decode step: {len(mats) // 7} layers x (q 5120->6144, k/v 5120->1024, "
+                        f"o 6144->5120, gate/up 5120->17408, down 17408->5120), "
+                        f"Hadamard transform before every projection",
+               layers=len(mats) // 7, matrices=len(mats), weights=weights, formats={})
+
+    def median_replay_us(g, reps):
+        cur = torch.cuda.current_stream()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            g.replay()
+            b.record(cur)
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(times))
+
+    for fmt in ("PQ2_0", "PTQ1_0"):
+        t0 = time.time()
+        host = {}
+        for m in mats[:7]:
+            T, S = synth.workload_matrix(m, seed)
+            d = bgg.bgg_describe(fmt, m.n, m.k)
+            host[m.name.split(".")[1]] = (d, bgg.bgg_pack_weights(d, T, S))
+            del T, S
+        calls = []
+        for m in mats:
+            d, hp = host[m.name.split(".")[1]]
+            calls.append((m, d, bgg.upload(hp, dev)))
+        del host
+        step_bytes = sum(int(d.format_bytes) for _, d, _ in calls)
+        wsb = max(bgg.bgg_gemv_workspace_size(d, mmax) for _, d, _ in calls)
+        ws = bgg.workspace(wsb, dev)
+        log(f"decode step {fmt}: {step_bytes / 1e9:.2f} GB packed in {len(calls)} buffers "
+            f"({time.time() - t0:.1f}s)")
+        per_m = {}
+        for M in ms:
+            def step(st, M=M):
+                for m, d, p in calls:
+                    bgg.bgg_ternary_gemv(d, p, xs[m.k][:M], ys[m.n][:M], M, bgg.BGG_ROTATE_INPUT,
+                                         ws, st)
+            g = capture(step)
+            us = median_replay_us(g, args.stack_replays)
+            del g
+            per_m[str(M)] = dict(us_per_step=round(us, 1), gbs=round(step_bytes / us / 1e3, 1),
+                                 frac=round(step_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                 tflops=round(2.0 * M * weights / us / 1e6, 2))
+            log(f"  M={M}: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
+
+        # M = 1 with the transform shared as a model would share it
+        groups = []  # (input width, [calls])
+        for i in range(0, len(calls), 7):
+            layer = calls[i:i + 7]
+            groups += [layer[0:3], layer[3:4], layer[4:6], layer[6:7]]
+
+        def step_shared(st):
+            for grp in groups:
+                m0, d0, _ = grp[0]
+                bgg.bgg_gemv_prepare(d0, xs[m0.k][:1], 1, bgg.BGG_ROTATE_INPUT, ws, st)
+                for m, d, p in grp:
+                    bgg.bgg_gemv_run(d, p, ys[m.n][:1], 1, ws, st)
+        g = capture(step_shared)
+        us = median_replay_us(g, args.stack_replays)
+        del g
+        shared = dict(us_per_step=round(us, 1), gbs=round(step_bytes / us / 1e3, 1),
+                      frac=round(step_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                      launches=len(groups) + len(calls))
+        log(f"  M=1 shared transform: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
+        res["formats"][fmt] = dict(packed_bytes=step_bytes, per_m=per_m, m1_shared_transform=shared)
+        del calls, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,6 +176,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=8, help="distinct device copies of the weights")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode-step", action="store_true",
+                    help="skip the 64-layer decode step and the small-batch sweep")
+    ap.add_argument("--stack-replays", type=int, default=20,
+                    help="timed graph replays per decode-step configuration (median reported)")
+    ap.add_argument("--gemm-warmup", type=int, default=40,
+                    help="untimed rotate + GEMM pairs before the timed prefill launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=100,
@@ -249,8 +354,11 @@ def main() -> int:
             x = torch.from_numpy(synth.workload_x(pw["seed"], M, mat.k)).to(dev)
             xr = torch.empty_like(x)
             y = torch.empty((M, mat.n), dtype=torch.float16, device=dev)
+            # warm-up long enough (tens of ms of matrix work) for the clocks to
+            # settle: the first launches after the GEMV part run up to 25 %
+            # slower than the steady state
             reps = 10
-            for _ in range(3):
+            for _ in range(args.gemm_warmup):
                 bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
                 bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
             torch.cuda.synchronize()
@@ -285,6 +393,11 @@ def main() -> int:
                                     peak=HBM_PEAK_GBS, unit="GB/s",
                                     frac=round(max(f["gbs"] for f in fwht) / HBM_PEAK_GBS, 4))))
         log(f"prefill {tf:.0f} TFLOP/s; " + ", ".join(f"{s['matrix']} {s['tflops']} TF" for s in shapes))
+
+    # ------------------------------------- 64-layer decode step, M = 1 .. 16
+    stack = None
+    if not args.no_decode_step:
+        stack = decode_stack_bench(args, bgg, torch, dev, capture)
 
     # ----------------------------------------------------------- CPU oracle
     cpu = None
@@ -323,6 +436,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "kernels": kernels,
         "prefill_gemm": prefill,
+        "decode_step": stack,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)
