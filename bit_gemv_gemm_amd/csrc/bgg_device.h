@@ -182,6 +182,31 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t word, uint32_t lane_off) {
   return __builtin_amdgcn_perm(word, lane_off, 0x0C0C0000u | ((4u + J) << 8));
 }
 
+// fp16 matrix-core operands (v_mfma_f32_32x32x16_f16)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Eight consecutive PQ2_0 codes (16 bits of a code word: code i in bits
+// 2i..2i+1) and a scale -> the fp16 MFMA operand (s*t_0, ..., s*t_7).
+// A nibble (c1 << 2 | c0) times 0x4001 puts c0 in bits 0-1 and c1 in bits
+// 16-17; 0x6400 | c is the fp16 1024 + c, and subtracting 1025 gives t = c-1
+// exactly; t * s is exact.
+__device__ __forceinline__ f16x8 decode8_pq2(uint32_t codes16, __half2 s2) {
+  const __half2 bias = __halves2half2(__ushort_as_half(0xE401), __ushort_as_half(0xE401));  // -1025
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t nib = (codes16 >> (4 * j)) & 0xFu;
+    uint32_t p = ((nib * 0x4001u) & 0x00030003u) | 0x64006400u;
+    __half2 h = *reinterpret_cast<__half2*>(&p);
+    h = __hmul2(__hadd2(h, bias), s2);
+    out[j] = *reinterpret_cast<uint32_t*>(&h);
+  }
+  f16x8 r;
+  __builtin_memcpy(&r, out, sizeof(r));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------

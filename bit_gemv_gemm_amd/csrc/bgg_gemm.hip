@@ -24,39 +24,18 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
-#include "bgg_internal.h"
+#include "bgg_device.h"
 
 using bgg::fail;
+using bgg::f16x8;
+using bgg::f32x16;
+using bgg::decode8_pq2;
 
 namespace {
 
 constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // halves per LDS row (+16 bytes against bank conflicts)
 constexpr int kTileRows = BGG_ROW_TILE;
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Eight consecutive PQ2_0 codes (16 bits of a code word: code i in bits
-// 2i..2i+1) and a scale -> the fp16 MFMA operand (s*t_0, ..., s*t_7).
-// A nibble (c1 << 2 | c0) times 0x4001 puts c0 in bits 0-1 and c1 in bits
-// 16-17; 0x6400 | c is the fp16 1024 + c, and subtracting 1025 gives t = c-1
-// exactly; t * s is exact.
-__device__ __forceinline__ f16x8 decode8(uint32_t codes16, __half2 s2) {
-  const __half2 bias = __halves2half2(__ushort_as_half(0xE401), __ushort_as_half(0xE401));  // -1025
-  uint32_t out[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t nib = (codes16 >> (4 * j)) & 0xFu;
-    uint32_t p = ((nib * 0x4001u) & 0x00030003u) | 0x64006400u;
-    __half2 h = *reinterpret_cast<__half2*>(&p);
-    h = __hmul2(__hadd2(h, bias), s2);
-    out[j] = *reinterpret_cast<uint32_t*>(&h);
-  }
-  f16x8 r;
-  __builtin_memcpy(&r, out, sizeof(r));
-  return r;
-}
 
 __global__ void __launch_bounds__(256, 2)
     k_gemm_pq2(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
@@ -137,7 +116,7 @@ __global__ void __launch_bounds__(256, 2)
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                        \
         const uint32_t w_ = kk == 0 ? bw[j].x : kk == 1 ? bw[j].y            \
                             : kk == 2 ? bw[j].z : bw[j].w;                   \
-        b[j] = decode8(w_ >> (16 * h), s2[j]);                               \
+        b[j] = decode8_pq2(w_ >> (16 * h), s2[j]);                               \
       }                                                                      \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                          \
           _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =           \

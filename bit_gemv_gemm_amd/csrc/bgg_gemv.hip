@@ -31,6 +31,7 @@
 //     workgroups).
 #include "bgg_device.h"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -295,9 +296,9 @@ constexpr int kMaxSumSlices = 127;  // arrivals the count field holds
 // K, M and N: kSumSlots token slots of kSumRows words.  A launch covers at
 // most kSumRows rows of split tiles.  Every launch leaves the words it used
 // at zero, so a zero-filled workspace stays ready for any GEMV call.
-constexpr int64_t kSumSlots = 4;
+constexpr int64_t kSumSlots = 16;
 constexpr int64_t kSumRows = 65536;
-constexpr uint64_t kSumBytes = (uint64_t)kSumSlots * kSumRows * 8;  // 2 MiB
+constexpr uint64_t kSumBytes = (uint64_t)kSumSlots * kSumRows * 8;  // 8 MiB
 
 __device__ __forceinline__ uint64_t sum_term(float s) {
   const double lim = (double)(kSumBias - 1);
@@ -743,6 +744,259 @@ __global__ void __launch_bounds__(64 * W)
 }
 
 // ---------------------------------------------------------------------------
+// PQ2_0 for 2..16 tokens on the matrix cores, with the same integer
+// arithmetic as the kernels above: for each 128-group the exact sum
+// p = sum t q over the group's weights, then acc = fma(s 2^(e-14), p, acc)
+// in fp32 (the rows of a token come out bit for bit as with one token).
+//
+// The VALU kernels spend dot8 work per code word per token and read the
+// weights once per four tokens; here one v_mfma_scale_f32_16x16x128_f8f6f4
+// per row block multiplies a 128-group of 16 weight rows with 16 token
+// slots (slots past M repeat the last token; their results are dropped):
+//   * B (weights) in fp4 (e2m1): a code c in {0, 1, 2} (trit c - 1) is the
+//     nibble c, whose e2m1 value is c / 2; B's block scale 2 makes it c.
+//     Two operations per 16 codes: the codes of even positions are w & 0x3..,
+//     of odd positions (w >> 2) & 0x3...
+//   * A (activations) in fp8 (e4m3): q = 1024 d0 + 32 d1 + d2 with balanced
+//     base-32 digits d in [-16, 16], each an e4m3 integer; one MFMA per
+//     digit with A's block scale 2^(e-14+10-5k) for digit k, accumulating
+//     into the same registers.  Started from -2^(e-14) sum q (written by the
+//     prep kernel), the accumulator ends at 2^(e-14) sum (c-1) q: every
+//     partial sum is a multiple of 2^(e-14) below 2^24 of them, so fp32
+//     holds it exactly.
+// Operand layouts (gfx950): B lane (col, g) holds K 32 g .. 32 g + 31 of
+// column col as nibbles, A lane (row, g) holds K 16 g + (0..15) in bytes
+// 0-15 and K 64 + 16 g + (0..15) in bytes 16-31; the scale byte of lane
+// (row, g) covers K block 32 g.  The prep kernel stores the A digits in the
+// order the B nibbles take, for each lane 32 contiguous bytes.
+//
+// Work split as the VALU kernel (wg_slot, same slices): a wave takes BPS
+// groups of one 64-row tile (row blocks rb: rows col + 16 rb), W waves of a
+// workgroup consecutive slices; the waves' 16 x 64 results are added in
+// wave order in LDS, the workgroups of a tile in the fixed-point row sums
+// (one slot per token).
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMmaSlots = 16;      // token slots of the A operand
+constexpr int kMmaRedStride = 68;  // floats per token row in LDS (64 rows + 4: no bank conflicts)
+constexpr int kMxDigits = 3;       // base-32 digits of q
+
+// Group position (0..127) of the weight that B element K (= 32 g + n, nibble n
+// of lane group g) carries: dword j = n / 8 of the lane's four holds the
+// codes of word j / 2 at even (j even) or odd (j odd) positions.
+__host__ __device__ constexpr int mx_pos_of_k(int K) {
+  return (K & ~31) + 16 * ((K >> 4) & 1) + 2 * (K & 7) + ((K >> 3) & 1);
+}
+// K of byte e of an A lane in lane group g.
+__host__ __device__ constexpr int mx_k_of_a(int g, int e) {
+  return e < 16 ? 16 * g + e : 64 + 16 * g + (e - 16);
+}
+// e4m3 byte of an integer |d| <= 16 (exact).
+__device__ __forceinline__ uint32_t e4m3_of_int(int d) {
+  const uint32_t a = (uint32_t)(d < 0 ? -d : d);
+  if (a == 0) return 0;
+  const int p = 31 - __builtin_clz(a);
+  return (d < 0 ? 0x80u : 0u) | ((uint32_t)(p + 7) << 3) | (((a << 3) >> p) - 8);
+}
+
+template <int BPS, int W>
+__global__ void __launch_bounds__(64 * W)
+    k_gemv_pq2_mx(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
+                  int64_t N, int Sg, int Mreal, const uint4* __restrict__ xa,
+                  const uint32_t* __restrict__ xs, const float* __restrict__ xc,
+                  unsigned long long* __restrict__ sums, int64_t tile0, int64_t ntl, int64_t nta,
+                  int sgb, int light_last, uint16_t* __restrict__ y) {
+  __shared__ float red[W][kMmaSlots * kMmaRedStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
+  const int64_t tile = ws.tile;
+  const int64_t gbeg =
+      ws.one ? (wave == 0 ? (int64_t)ws.wgs * BPS : G) : ((int64_t)ws.wgs * W + wave) * BPS;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (gbeg < G) {
+    // K 32 kg .. 32 kg + 31 of group g, row r: 8 bytes at chunk 2 g + kg / 2,
+    // half kg % 2 -- uint2 index ((tile C + c) 64 + r) 2 + half
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2* wsrc =
+        reinterpret_cast<const u32x2*>(packed) + ((tile * C + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
+    const uint16_t* ssrc =
+        reinterpret_cast<const uint16_t*>(packed + scale_offset) + tile * G * kTile + col;
+    // The loads of the slice are issued first, group by group (A digits,
+    // scale word, start values, weights, weight scales), with no branch
+    // between them and their use: loads complete in issue order, so group i
+    // waits only for its own loads and those of the groups before it.  The
+    // A operands of at most PRE groups are in flight (registers); those of
+    // group i + PRE are issued once group i is done.  A group past G
+    // re-reads group G - 1 and gets a zero scale.  Lanes of token slots past
+    // M load nothing and multiply zeros (their rows are dropped), so a few
+    // tokens cost few A bytes.
+    constexpr int PRE = BPS <= 5 ? BPS : 4;
+    const bool aload = col < Mreal;
+    const int aslot = aload ? col : Mreal - 1;
+    const uint4* asrc = xa + (aslot + 16 * kg) * 2;
+    uint4 a[PRE][kMxDigits][2];
+    uint32_t sa[PRE];
+    f32x4 c0[PRE];
+    u32x2 w[BPS][4];
+    uint16_t sc[BPS][4];
+#define BGG_MX_LOAD_A(SLOT, I)                                                  \
+  do {                                                                          \
+    const int64_t g_ = gbeg + (I) < G ? gbeg + (I) : G - 1;                     \
+    _Pragma("unroll") for (int k = 0; k < kMxDigits; ++k) {                    \
+      a[SLOT][k][0] = aload ? asrc[(g_ * kMxDigits + k) * 128] : make_uint4(0, 0, 0, 0); \
+      a[SLOT][k][1] = aload ? asrc[(g_ * kMxDigits + k) * 128 + 1] : make_uint4(0, 0, 0, 0); \
+    }                                                                           \
+    sa[SLOT] = xs[g_ * kMmaSlots + aslot];                                      \
+    c0[SLOT] = *reinterpret_cast<const f32x4*>(xc + g_ * kMmaSlots + 4 * kg);   \
+  } while (0)
+#pragma unroll
+    for (int i = 0; i < BPS; ++i) {
+      const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
+      if (i < PRE) BGG_MX_LOAD_A(i, i);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        w[i][rb] = __builtin_nontemporal_load(wsrc + g * (4 * kTile) + rb * 32);
+        sc[i][rb] = ssrc[g * kTile + 16 * rb];
+      }
+    }
+    // keep the scheduler from sinking the loads towards their uses
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < BPS; ++i) {
+      constexpr int kPre = PRE;
+      const int slot = i % kPre;
+      i32x8 A[kMxDigits];
+#pragma unroll
+      for (int k = 0; k < kMxDigits; ++k) {
+        A[k] = i32x8{(int)a[slot][k][0].x, (int)a[slot][k][0].y, (int)a[slot][k][0].z,
+                     (int)a[slot][k][0].w, (int)a[slot][k][1].x, (int)a[slot][k][1].y,
+                     (int)a[slot][k][1].z, (int)a[slot][k][1].w};
+      }
+      const uint32_t sac = sa[slot];
+      const f32x4 cc = c0[slot];
+      if (i + PRE < BPS) BGG_MX_LOAD_A(slot, i + PRE);
+      const bool live = gbeg + i < G;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const uint32_t lo = w[i][rb].x, hi = w[i][rb].y;
+        const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                         (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+        f32x4 ag = cc;
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, ag, 0, 4, 0, (int)sac, 0, 128);
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, ag, 0, 4, 1, (int)sac, 0, 128);
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, ag, 0, 4, 2, (int)sac, 0, 128);
+        const float s = live ? h2f(sc[i][rb]) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s, ag[e], acc[rb][e]);
+      }
+    }
+#undef BGG_MX_LOAD_A
+  }
+  // D layout: lane holds weight row 16 rb + col and token slots 4 kg + e
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      red[wave][(4 * kg + e) * kMmaRedStride + 16 * rb + col] = acc[rb][e];
+  __syncthreads();
+  for (int it = threadIdx.x; it < kMmaSlots * kTile; it += 64 * W) {
+    const int t = it >> 6, r = it & 63;
+    if (t >= Mreal) break;  // t only grows with it
+    float v = red[0][t * kMmaRedStride + r];
+#pragma unroll
+    for (int q = 1; q < W; ++q) v += red[q][t * kMmaRedStride + r];
+    const int64_t row = tile * kTile + r;
+    if (ws.Sg == 1) {
+      if (row < N) y[(int64_t)t * N + row] = f2h(v);
+      continue;
+    }
+    unsigned long long* word = &sums[(int64_t)t * kSumRows + ws.local * kTile + r];
+    const uint64_t term = sum_term(v);
+    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)(old >> kSumCountShift) == ws.Sg - 1) {
+      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)ws.Sg * (int64_t)kSumBias;
+      if (row < N) y[(int64_t)t * N + row] = f2h((float)((double)tot * 0x1p-30));
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Activations for the matrix-core kernel.  Per 128-group and token slot
+// (slots past M repeat token M - 1): the same x', e and q as the encoding
+// above; q's three base-32 digits as e4m3 bytes in the A operand order
+// (xa: per group and digit, 64 lanes x 32 bytes), the scale bytes
+// 127 + e - 14 + 10 - 5 k of digit k (xs: one word per group and slot) and
+// -2^(e-14) sum q (xc).  grid: G blocks of 256 threads, 16 lanes per slot.
+__global__ void __launch_bounds__(256)
+    k_gemv_prep_mx(const uint16_t* __restrict__ x, int64_t K, int M, int rotate,
+                   uint32_t* __restrict__ xa, uint32_t* __restrict__ xs, float* __restrict__ xc) {
+  __shared__ int16_t qs[kMmaSlots][kGroup];
+  const int64_t blk = blockIdx.x;
+  const int t = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int src = t < M ? t : M - 1;
+  float v[8];
+  load8h(x + (int64_t)src * K + blk * kGroup + 8 * l16, v);
+  if (rotate) {
+    fwht128_unscaled(v, l16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, xor16_f<1>(amax));
+  amax = fmaxf(amax, xor16_f<2>(amax));
+  amax = fmaxf(amax, xor16_f<4>(amax));
+  amax = fmaxf(amax, xor16_f<8>(amax));
+  int e = 0;
+  frexpf(amax, &e);
+  int qsum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = amax > 0.0f ? (int)rintf(ldexpf(v[j], 14 - e)) : 0;
+    qs[t][8 * l16 + j] = (int16_t)q;
+    qsum += q;
+  }
+  qsum += xor16_i<1>(qsum);
+  qsum += xor16_i<2>(qsum);
+  qsum += xor16_i<4>(qsum);
+  qsum += xor16_i<8>(qsum);
+  if (l16 == 0) {
+    const int eb = amax > 0.0f ? e : 0;
+    xs[blk * kMmaSlots + t] = (uint32_t)(123 + eb) | ((uint32_t)(118 + eb) << 8) |
+                              ((uint32_t)(113 + eb) << 16) | (127u << 24);
+    xc[blk * kMmaSlots + t] = amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
+  }
+  __syncthreads();
+  // 3 digits x 64 lanes x 8 words per group
+  for (int it = threadIdx.x; it < kMxDigits * 64 * 8; it += 256) {
+    const int k = it >> 9, l = (it >> 3) & 63, dd = it & 7;
+    const int tt = l & 15, ga = l >> 4;
+    uint32_t word = 0;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int q = qs[tt][mx_pos_of_k(mx_k_of_a(ga, 4 * dd + bb))];
+      const int d2 = ((q + 16) & 31) - 16;
+      const int r = (q - d2) >> 5;
+      const int d1 = ((r + 16) & 31) - 16;
+      const int d0 = (r - d1) >> 5;
+      const int d = k == 0 ? d0 : k == 1 ? d1 : d2;
+      word |= e4m3_of_int(d) << (8 * bb);
+    }
+    xa[((blk * kMxDigits + k) * 64 + l) * 8 + dd] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // plan and launch
 // ---------------------------------------------------------------------------
 // Token slots of the prepared activations: padding tokens are zero.
@@ -764,7 +1018,16 @@ struct GemvPlan {
   int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
   uint64_t off_frag, off_meta_q, off_meta_f, off_sums, off_fuse, total;
   int64_t nta, sgb;  // tiles with Sg slices; one-wave slices of the rest
+  bool mma;          // PQ2_0 with several tokens: the matrix-core kernel
 };
+
+// The fewest PQ2_0 tokens that run on the matrix-core kernel (fewer: the
+// VALU kernels, up to four tokens per pass; both give the same bits).  Two
+// tokens measured faster on the VALU kernel (one pass, little dot8 work).
+int64_t gemv_mma_min_tokens() {
+  static const int64_t m = env_int("BGG_GEMV_MMA_MIN", 3);
+  return m < 2 ? 2 : m;
+}
 
 // Compute units of the current device (cached per device).
 int64_t device_cus() {
@@ -790,6 +1053,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   p.rows_pad = p.NT * kTile;
   p.slots = gemv_m_slots(M);
   p.W = 8;
+  p.mma = d->format == BGG_FMT_PQ2_0 && M >= gemv_mma_min_tokens();
   if (d->format == BGG_FMT_PQ2_0) {
     p.gpad = p.G;
     p.units = p.G;
@@ -843,11 +1107,20 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   }
   // [row sums][digit words][group Q][group F]: the row sums are the same for
   // every call, the rest depends only on the format, K and M
+  // (for several PQ2_0 tokens the frag region also holds the matrix-core
+  // kernel's A digits, and the group-Q region its scale words and start
+  // values)
+  uint64_t frag_bytes = (uint64_t)p.slots * p.frag_words_per_token * 4;
+  uint64_t meta_q_bytes = (uint64_t)p.slots * p.gpad * 4;
+  if (d->format == BGG_FMT_PQ2_0 && M >= 2) {
+    frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
+    meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 8);
+  }
   p.off_sums = 0;
   p.off_frag = kSumBytes;
-  uint64_t off = align256(p.off_frag + (uint64_t)p.slots * p.frag_words_per_token * 4);
+  uint64_t off = align256(p.off_frag + frag_bytes);
   p.off_meta_q = off;
-  off = align256(off + (uint64_t)p.slots * p.gpad * 4);
+  off = align256(off + meta_q_bytes);
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
   // the one-launch kernel's copies of one token's digit words (reserved for
@@ -863,6 +1136,13 @@ void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x
   uint32_t* frag = reinterpret_cast<uint32_t*>(ws + p.off_frag);
   int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
+  if (p.mma) {
+    uint32_t* xs = reinterpret_cast<uint32_t*>(ws + p.off_meta_q);
+    hipLaunchKernelGGL(k_gemv_prep_mx, dim3((unsigned)p.G), dim3(256), 0, st, x, d->K, (int)M,
+                       rotate, reinterpret_cast<uint32_t*>(ws + p.off_frag), xs,
+                       reinterpret_cast<float*>(xs + p.G * kMmaSlots));
+    return;
+  }
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
   if (d->format == BGG_FMT_PQ2_0)
     hipLaunchKernelGGL(k_gemv_prep<BGG_FMT_PQ2_0>, grid, dim3(64), 0, st, x, d->K, (int)M,
@@ -932,6 +1212,38 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
   }
 }
 
+// The matrix-core GEMV for 2..16 PQ2_0 tokens (one launch, or one per
+// kSumRows rows of split tiles); the plan's work split is the VALU kernel's.
+void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
+                     uint16_t* y, int Mreal, uint8_t* ws, hipStream_t st) {
+  const uint4* xa = reinterpret_cast<const uint4*>(ws + p.off_frag);
+  const uint32_t* xs = reinterpret_cast<const uint32_t*>(ws + p.off_meta_q);
+  const float* xc = reinterpret_cast<const float*>(xs + p.G * kMmaSlots);
+  unsigned long long* sums = reinterpret_cast<unsigned long long*>(ws + p.off_sums);
+  const int Sg = (int)p.Sg;
+  const dim3 block(64 * 8);
+  const int64_t chunk = Sg > 1 ? kSumRows / kTile : p.NT;
+  for (int64_t t0 = 0; t0 < p.NT; t0 += chunk) {
+    const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
+    const int64_t nta = p.sgb > 1 ? p.nta : ntl;
+    const int sgb = (int)p.sgb;
+    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
+    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
+    const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
+#define BGG_MMA(BPS)                                                                           \
+  hipLaunchKernelGGL((k_gemv_pq2_mx<BPS, 8>), grid, block, 0, st, packed, d->scale_offset,    \
+                     d->chunks, p.G, d->N, Sg, Mreal, xa, xs, xc, sums, t0, ntl, nta, sgb,    \
+                     light, y)
+    switch (p.per_slice) {
+      case 8: BGG_MMA(8); break;
+      case 5: BGG_MMA(5); break;
+      case 4: BGG_MMA(4); break;
+      default: BGG_MMA(2); break;
+    }
+#undef BGG_MMA
+  }
+}
+
 // One-launch GEMV for a single token, per format (BGG_GEMV_FUSE: bit 0
 // PQ2_0, bit 1 PTQ1_0; a cleared bit means prep kernel + GEMV kernel).
 bool gemv_fuse_enabled(int format) {
@@ -979,7 +1291,9 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
   const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
   const char* fused = M == 1 && gemv_fuse_enabled(d->format) ? "true" : "false";
   int n;
-  if (d->format == BGG_FMT_PQ2_0) {
+  if (p.mma) {
+    n = snprintf(out, cap, "k_gemv_pq2_mx<%d, 8>", (int)p.per_slice);
+  } else if (d->format == BGG_FMT_PQ2_0) {
     n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8, %s>", mb, (int)p.per_slice, fused);
   } else {
     const int h = (p.per_slice == 2 && mb == 1) ? 2 : 1;
@@ -1016,6 +1330,10 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* d, const void* packed_dev, void*
   const uint8_t* pk = (const uint8_t*)packed_dev;
   uint8_t* ws = (uint8_t*)workspace;
   uint16_t* y = (uint16_t*)y_dev;
+  if (p.mma) {
+    launch_gemv_mma(d, p, pk, y, (int)M, ws, s);
+    return hip_check("bgg_gemv_run");
+  }
   for (int64_t m0 = 0; m0 < M; m0 += kGemvTokens) {
     const int mg = (int)(M - m0 < kGemvTokens ? M - m0 : kGemvTokens);
     switch (gemv_m_bucket(mg)) {

@@ -180,7 +180,7 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *   y_dev       device fp16 [M][N]
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
  *               bytes, 16-byte aligned (64-byte aligned for the one-launch
- *               path below).  Its first 2 MiB hold the row sums of split-K
+ *               path below).  Its first 8 MiB hold the row sums of split-K
  *               launches, which must be zero when a call starts: zero-fill a
  *               new workspace once; every GEMV call (any format, K, M or N)
  *               leaves them zero again.  A workspace used for anything else
@@ -188,15 +188,19 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * For M == 1 one kernel launch encodes the activations and computes y;
  * otherwise it is bgg_gemv_prepare followed by bgg_gemv_run.  Both give the
  * same bits.
- * Each 64-row tile is read once per group of up to four tokens (one kernel
- * launch per group), all tokens of the group at a time.  The
- * activations are carried as 15-bit integers with a power-of-two scale per
- * 128-block (absolute error at most 2^-14 of the block's largest |x'|), the
- * trit products are exact integer sums, and each group's sum is scaled and
- * accumulated in fp32 in a fixed order; where K is split over workgroups
- * their partial rows are added as 64-bit fixed-point integers (resolution
- * 2^-30, magnitude below 2^19), whose sum does not depend on the order.  y
- * is rounded to fp16 once, and the same inputs always give bit-identical y.
+ * Arithmetic.  The activations are carried as 15-bit integers q with a
+ * power-of-two scale per 128-block (absolute error at most 2^-14 of the
+ * block's largest |x'|); each group's trit sum p = sum t q is exact, and is
+ * scaled and accumulated in fp32 in a fixed order.  PTQ1_0 (any M) and
+ * PQ2_0 with one or two tokens read each 64-row tile once per group of up
+ * to four tokens (one kernel launch per group); PQ2_0 with 3..16 tokens
+ * reads it once for all tokens (one launch, matrix cores), with the same
+ * sums and fp32 steps, so a token's y does not depend on the other tokens
+ * or on M.
+ * Where K is split over workgroups their partial rows are added as 64-bit
+ * fixed-point integers (resolution 2^-30, magnitude below 2^19), whose sum
+ * does not depend on the order.  y is rounded to fp16 once, and the same
+ * inputs always give bit-identical y.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER,
  * BGG_ERR_HIP.
  */
@@ -230,7 +234,8 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
  * calls).  The last template argument is true for the one-launch kernel
  * that also encodes the activations (M == 1) and false for the kernel that
  * reads a preparation (bgg_gemv_run launches that one, with the same other
- * arguments).
+ * arguments).  PQ2_0 with 3..16 tokens names the matrix-core kernel, e.g.
+ * "k_gemv_pq2_mx<5, 8>", which covers all M tokens in one launch.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);

@@ -182,9 +182,9 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_hadamard_rotate(None, None, 1, 128, None) == 1
     # shape errors are reported before any device work
     assert lib.bgg_hadamard_rotate(16, 16, 1, 100, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 0, 1, 16, 1 << 23, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, 1 << 23, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 23, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 0, 1, 16, 1 << 24, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, 1 << 24, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 24, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
     dp = bgg.bgg_describe("PTQ1_0", 64, 128)

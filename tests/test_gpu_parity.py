@@ -281,41 +281,33 @@ def test_gemv_zero_weights_and_repeat_calls(env, fmt):
     assert np.array_equal(y_a[:1], y_b)
 
 
-def test_gemv_decode_step_shapes_sampled(env):
-    """Every projection shape of the 64-layer decode step at full size
-    (first and last layer), both packings; outputs of 96 sampled rows per
-    matrix checked against the oracle, which regenerates just those rows."""
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152)])
+def test_gemv_pq2_tokens_do_not_mix(env, N, K):
+    """PQ2_0 with 3..16 tokens runs on the matrix cores with 16 token slots
+    and the integer arithmetic of the one-token kernel (two tokens: the VALU
+    kernel): a token's y must not depend on the other tokens or on M, and
+    must equal its one-token y bit for bit; M = 16 must match the oracle."""
     bgg, torch = env
-    w = synth.WORKLOADS["decode_step"]
-    rng = np.random.default_rng(0)
-    for mat in [m for m in w["matrices"] if m.name.startswith(("L0.", "L63."))]:
-        T, S = synth.workload_matrix(mat, w["seed"])
-        x = synth.workload_x(w["seed"], 1, mat.k)
-        rows = np.sort(rng.choice(mat.n, 96, replace=False))
-        for fmt in FMTS:
-            say(f"decode-step {fmt} {mat.name} N={mat.n} K={mat.k}")
-            y = Dev(bgg, torch, fmt, T, S).gemv(x)
-            ref = oracle.matvec(T[rows], S[rows], oracle.rotate(x))
-            full_scale = np.max(np.abs(y.astype(np.float64)))
-            err = np.max(np.abs(y[:, rows].astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30)
-            assert err <= TOL and full_scale > 0
-
-
-@pytest.mark.parametrize("M", [2, 4, 8, 16])
-def test_gemv_small_batch_full_shapes(env, M):
-    """Small-batch decode at the decode step's gate/up and down shapes."""
-    bgg, torch = env
-    w = synth.WORKLOADS["small_batch"]
-    for mat in [m for m in w["matrices"] if m.name in ("L0.gate", "L0.down")]:
-        T, S = synth.workload_matrix(mat, w["seed"])
-        x = synth.workload_x(w["seed"], M, mat.k)
-        rows = np.arange(0, mat.n, 37)
-        xr = oracle.rotate(x)
-        ref = oracle.matvec(T[rows], S[rows], xr)
-        for fmt in FMTS:
-            say(f"small-batch {fmt} M={M} {mat.name}")
-            y = Dev(bgg, torch, fmt, T, S).gemv(x)
-            assert np.all(relerr(y[:, rows], ref) <= TOL)
+    say(f"gemv pq2 tokens do not mix {N}x{K}")
+    T, S = gen_matrix(101, 3, N, K)
+    d = Dev(bgg, torch, "PQ2_0", T, S)
+    x = synth.activations_f16(101, 4, 16, K)
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
+    assert bgg.bgg_gemv_kernel_name(d.desc, 3).startswith("k_gemv_pq2_mx<")
+    assert bgg.bgg_gemv_kernel_name(d.desc, 2).startswith("k_gemv_pq2<")
+    y16 = d.gemv(x, ws=ws)
+    ref = oracle_y("PQ2_0", T, S, x)
+    assert np.all(relerr(y16, ref) <= TOL)
+    for M in (2, 3, 7, 15):
+        yM = d.gemv(x[16 - M:], ws=ws)
+        assert np.array_equal(yM.view(np.uint16), y16[16 - M:].view(np.uint16)), f"M={M}"
+    for m in (0, 5, 15):
+        y1 = d.gemv(x[m:m + 1], ws=ws)
+        assert np.array_equal(y1[0].view(np.uint16), y16[m].view(np.uint16)), f"token {m}"
+    # the same token in every slot
+    xs = np.repeat(x[5:6], 16, axis=0)
+    ys = d.gemv(xs, ws=ws)
+    assert np.all(ys.view(np.uint16) == y16[5].view(np.uint16))
 
 
 # ---------------------------------------------------------------------------
