@@ -158,11 +158,23 @@ __device__ __forceinline__ uint32_t ptq1_trit_nibbles(uint32_t b) {
   return t;
 }
 __device__ __forceinline__ uint32_t lut_lane_off(int lane) { return (uint32_t)(lane & 31) * 4u; }
+// The same five trits as codes c = t + 1 in 2-bit fields (code i in bits
+// 2i..2i+1): the PQ2_0 code form, ten bits per byte.
+__device__ __forceinline__ uint32_t ptq1_codes10(uint32_t b) {
+  const uint32_t c = ptq1_entry(b);
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) r |= ((c >> (4 * i)) & 3u) << (2 * i);
+  return r;
+}
 // Built in two steps: the first 256 threads each decode one byte value into
 // seed[], then (after a barrier) every thread copies entries out, 16 bytes
 // per store.  Needs blockDim.x >= 256; the caller synchronises afterwards.
+// CODES: entries in the 2-bit code form instead of trit nibbles.
+template <bool CODES = false>
 __device__ __forceinline__ void build_lut32(uint32_t* lut, uint32_t* seed) {
-  if (threadIdx.x < 256) seed[threadIdx.x] = ptq1_trit_nibbles(threadIdx.x);
+  if (threadIdx.x < 256)
+    seed[threadIdx.x] = CODES ? ptq1_codes10(threadIdx.x) : ptq1_trit_nibbles(threadIdx.x);
   __syncthreads();
   constexpr int kQuads = kLutCopies32 / 4, kRowQuads = kLutRowBytes / 16;
   for (int i = threadIdx.x; i < 256 * kQuads; i += blockDim.x) {

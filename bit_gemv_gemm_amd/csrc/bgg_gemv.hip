@@ -930,6 +930,185 @@ __global__ void __launch_bounds__(64 * W)
   }
 }
 
+// ---------------------------------------------------------------------------
+// PTQ1_0 for several tokens on the matrix cores.  A wave takes one period
+// (five groups, 128 row bytes) of one 64-row tile, as the VALU kernel with
+// one part per period does, and gives the same bits:
+//   1. each lane decodes its own row's 128 bytes through the LUT (entries in
+//      the 2-bit code form, ten bits per byte) into the PQ2_0 code layout --
+//      16 bytes are 80 positions, exactly five 32-bit words -- and stores
+//      the 40 words of the period in LDS;
+//   2. the MFMA loop of k_gemv_pq2_mx reads each lane's operand words (K
+//      32 kg .. 32 kg + 31 of a group, rows col + 16 rb) from there.
+// LDS: the LUT (64 KiB), the waves' code words (44 words per row), and the
+// final reduction, which reuses the code words' space.
+// ---------------------------------------------------------------------------
+constexpr int kPtqCodeStride = 44;  // words per row in LDS: 40 + 4 against bank conflicts
+
+template <int W>
+__global__ void __launch_bounds__(64 * W)
+    k_gemv_ptq1_mx(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
+                   int64_t N, int Sg, int Mreal, const uint4* __restrict__ xa,
+                   const uint32_t* __restrict__ xs, const float* __restrict__ xc,
+                   unsigned long long* __restrict__ sums, int64_t tile0, int64_t ntl, int64_t nta,
+                   int sgb, int light_last, uint16_t* __restrict__ y) {
+  static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
+  static_assert(kMmaSlots * kMmaRedStride <= kTile * kPtqCodeStride, "red fits in a wave's codes");
+  constexpr int PRE = 2;  // groups whose A operands are in flight
+  __shared__ uint32_t lut[256 * kLutRowBytes / 4];
+  __shared__ uint32_t lut_seed[256];
+  __shared__ __attribute__((aligned(16))) uint32_t codes[W][kTile * kPtqCodeStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+  const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
+  const int64_t tile = ws.tile;
+  const int64_t P = ceil_div(G, kPeriodGroups);
+  const int64_t p = ws.one ? (wave == 0 ? ws.wgs : P) : (int64_t)ws.wgs * W + wave;
+  const bool active = p < P;
+  const int64_t g0 = p * kPeriodGroups;
+
+  // Loads first, before the LUT is built: the row's 8 chunks of the period
+  // (past the row they read the next tile's bytes or the buffer's zero
+  // slack; those positions are in groups past G, which get a zero scale),
+  // the weight scales, and the A operands of the first PRE groups.
+  const bool aload = col < Mreal;
+  const int aslot = aload ? col : Mreal - 1;
+  const uint4* asrc = xa + (aslot + 16 * kg) * 2;
+  uint4 wch[kPeriodChunks];
+  uint16_t sc[kPeriodGroups][4];
+  uint4 a[PRE][kMxDigits][2];
+  uint32_t sa[PRE];
+  f32x4 c0[PRE];
+#define BGG_MX_LOAD_A(SLOT, I)                                                  \
+  do {                                                                          \
+    const int64_t g_ = g0 + (I) < G ? g0 + (I) : G - 1;                         \
+    _Pragma("unroll") for (int k = 0; k < kMxDigits; ++k) {                    \
+      a[SLOT][k][0] = aload ? asrc[(g_ * kMxDigits + k) * 128] : make_uint4(0, 0, 0, 0); \
+      a[SLOT][k][1] = aload ? asrc[(g_ * kMxDigits + k) * 128 + 1] : make_uint4(0, 0, 0, 0); \
+    }                                                                           \
+    sa[SLOT] = xs[g_ * kMmaSlots + aslot];                                      \
+    c0[SLOT] = *reinterpret_cast<const f32x4*>(xc + g_ * kMmaSlots + 4 * kg);   \
+  } while (0)
+  if (active) {
+    const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
+#pragma unroll
+    for (int c = 0; c < kPeriodChunks; ++c) wch[c] = ld_stream(tdata + (p * kPeriodChunks + c) * kTile);
+    const uint16_t* ssrc =
+        reinterpret_cast<const uint16_t*>(packed + scale_offset) + tile * G * kTile + col;
+#pragma unroll
+    for (int gi = 0; gi < kPeriodGroups; ++gi) {
+      const int64_t g = g0 + gi < G ? g0 + gi : G - 1;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) sc[gi][rb] = ssrc[g * kTile + 16 * rb];
+    }
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) BGG_MX_LOAD_A(i, i);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  build_lut32<true>(lut, lut_seed);
+  __syncthreads();
+
+  uint32_t* cw = codes[wave];
+  if (active) {
+    // 1. decode: chunk c (bytes 16c .. 16c+15 of the period) -> words
+    //    5c .. 5c+4 (byte j's ten code bits at bit 10 j of the 160)
+    const uint32_t lane_off = lut_lane_off(lane);
+    const char* lbase = reinterpret_cast<const char*>(lut);
+#pragma unroll
+    for (int c = 0; c < kPeriodChunks; ++c) {
+      const uint32_t wd[4] = {wch[c].x, wch[c].y, wch[c].z, wch[c].w};
+      uint32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[4 * q + 0] = *reinterpret_cast<const uint32_t*>(lbase + lut_addr<0>(wd[q], lane_off));
+        v[4 * q + 1] = *reinterpret_cast<const uint32_t*>(lbase + lut_addr<1>(wd[q], lane_off));
+        v[4 * q + 2] = *reinterpret_cast<const uint32_t*>(lbase + lut_addr<2>(wd[q], lane_off));
+        v[4 * q + 3] = *reinterpret_cast<const uint32_t*>(lbase + lut_addr<3>(wd[q], lane_off));
+      }
+      uint32_t o[5];
+      o[0] = v[0] | (v[1] << 10) | (v[2] << 20) | (v[3] << 30);
+      o[1] = (v[3] >> 2) | (v[4] << 8) | (v[5] << 18) | (v[6] << 28);
+      o[2] = (v[6] >> 4) | (v[7] << 6) | (v[8] << 16) | (v[9] << 26);
+      o[3] = (v[9] >> 6) | (v[10] << 4) | (v[11] << 14) | (v[12] << 24);
+      o[4] = (v[12] >> 8) | (v[13] << 2) | (v[14] << 12) | (v[15] << 22);
+#pragma unroll
+      for (int d = 0; d < 5; ++d) cw[lane * kPtqCodeStride + 5 * c + d] = o[d];
+    }
+  }
+  wave_lds_sync();  // a wave reads only its own code words
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (active) {
+    // 2. per group: 3 MFMAs per row block, then acc += s * (2^(e-14) p)
+#pragma unroll
+    for (int gi = 0; gi < kPeriodGroups; ++gi) {
+      const int slot = gi % PRE;
+      i32x8 A[kMxDigits];
+#pragma unroll
+      for (int k = 0; k < kMxDigits; ++k) {
+        A[k] = i32x8{(int)a[slot][k][0].x, (int)a[slot][k][0].y, (int)a[slot][k][0].z,
+                     (int)a[slot][k][0].w, (int)a[slot][k][1].x, (int)a[slot][k][1].y,
+                     (int)a[slot][k][1].z, (int)a[slot][k][1].w};
+      }
+      const uint32_t sac = sa[slot];
+      const f32x4 cc = c0[slot];
+      if (gi + PRE < kPeriodGroups) BGG_MX_LOAD_A(slot, gi + PRE);
+      const bool live = g0 + gi < G;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 wv = *reinterpret_cast<const u32x2*>(
+            &cw[(col + 16 * rb) * kPtqCodeStride + 8 * gi + 2 * kg]);
+        const uint32_t lo = wv.x, hi = wv.y;
+        const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                         (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+        f32x4 ag = cc;
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, ag, 0, 4, 0, (int)sac, 0, 128);
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, ag, 0, 4, 1, (int)sac, 0, 128);
+        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, ag, 0, 4, 2, (int)sac, 0, 128);
+        const float s = live ? h2f(sc[gi][rb]) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s, ag[e], acc[rb][e]);
+      }
+    }
+  }
+#undef BGG_MX_LOAD_A
+  // every wave is done with its code words before they become red
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(codes[0]);
+  constexpr int kRedWave = kTile * kPtqCodeStride;  // floats between waves' red rows
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      red[wave * kRedWave + (4 * kg + e) * kMmaRedStride + 16 * rb + col] = acc[rb][e];
+  __syncthreads();
+  for (int it = threadIdx.x; it < kMmaSlots * kTile; it += 64 * W) {
+    const int t = it >> 6, r = it & 63;
+    if (t >= Mreal) break;  // t only grows with it
+    float v = red[t * kMmaRedStride + r];
+#pragma unroll
+    for (int q = 1; q < W; ++q) v += red[q * kRedWave + t * kMmaRedStride + r];
+    const int64_t row = tile * kTile + r;
+    if (ws.Sg == 1) {
+      if (row < N) y[(int64_t)t * N + row] = f2h(v);
+      continue;
+    }
+    unsigned long long* word = &sums[(int64_t)t * kSumRows + ws.local * kTile + r];
+    const uint64_t term = sum_term(v);
+    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)(old >> kSumCountShift) == ws.Sg - 1) {
+      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)ws.Sg * (int64_t)kSumBias;
+      if (row < N) y[(int64_t)t * N + row] = f2h((float)((double)tot * 0x1p-30));
+      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Activations for the matrix-core kernel.  Per 128-group and token slot
 // (slots past M repeat token M - 1): the same x', e and q as the encoding
 // above; q's three base-32 digits as e4m3 bytes in the A operand order
@@ -1021,11 +1200,15 @@ struct GemvPlan {
   bool mma;          // PQ2_0 with several tokens: the matrix-core kernel
 };
 
-// The fewest PQ2_0 tokens that run on the matrix-core kernel (fewer: the
-// VALU kernels, up to four tokens per pass; both give the same bits).  Two
-// tokens measured faster on the VALU kernel (one pass, little dot8 work).
-int64_t gemv_mma_min_tokens() {
-  static const int64_t m = env_int("BGG_GEMV_MMA_MIN", 3);
+// The fewest tokens that run on the matrix-core kernels (fewer: the VALU
+// kernels, up to four tokens per pass; both give the same bits).  PQ2_0 with
+// two tokens measured faster on the VALU kernel (one pass, little dot8
+// work); PTQ1_0's VALU kernel spends a LUT lookup and dot8 work per byte
+// and token.
+int64_t gemv_mma_min_tokens(int format) {
+  static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 3);
+  static const int64_t ptq1 = env_int("BGG_GEMV_PTQ1_MMA_MIN", 2);
+  const int64_t m = format == BGG_FMT_PQ2_0 ? pq2 : ptq1;
   return m < 2 ? 2 : m;
 }
 
@@ -1053,7 +1236,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   p.rows_pad = p.NT * kTile;
   p.slots = gemv_m_slots(M);
   p.W = 8;
-  p.mma = d->format == BGG_FMT_PQ2_0 && M >= gemv_mma_min_tokens();
+  p.mma = M >= gemv_mma_min_tokens(d->format);
   if (d->format == BGG_FMT_PQ2_0) {
     p.gpad = p.G;
     p.units = p.G;
@@ -1085,7 +1268,9 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     p.gpad = P * kPeriodGroups;
     p.frag_words_per_token = P * kPtqFragWords;
     static const int64_t ptq1_w = env_int("BGG_GEMV_PTQ1_W", 8) >= 16 ? 16 : 8;
-    p.W = gemv_m_bucket(M) >= 4 ? 8 : ptq1_w;  // every token group of this M runs with p.W
+    // (every token group of this M runs with p.W; the matrix-core kernel
+    // with 8)
+    p.W = p.mma || gemv_m_bucket(M) >= 4 ? 8 : ptq1_w;
     p.per_slice = 1;
     while (p.per_slice < 2 && gemv_m_bucket(M) == 1 && p.NT * P * p.per_slice < ptq1_target)
       p.per_slice *= 2;
@@ -1107,12 +1292,12 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   }
   // [row sums][digit words][group Q][group F]: the row sums are the same for
   // every call, the rest depends only on the format, K and M
-  // (for several PQ2_0 tokens the frag region also holds the matrix-core
-  // kernel's A digits, and the group-Q region its scale words and start
+  // (for several tokens the frag region also holds the matrix-core
+  // kernels' A digits, and the group-Q region their scale words and start
   // values)
   uint64_t frag_bytes = (uint64_t)p.slots * p.frag_words_per_token * 4;
   uint64_t meta_q_bytes = (uint64_t)p.slots * p.gpad * 4;
-  if (d->format == BGG_FMT_PQ2_0 && M >= 2) {
+  if (M >= 2) {
     frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
     meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 8);
   }
@@ -1212,8 +1397,8 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
   }
 }
 
-// The matrix-core GEMV for 2..16 PQ2_0 tokens (one launch, or one per
-// kSumRows rows of split tiles); the plan's work split is the VALU kernel's.
+// The matrix-core GEMV for several tokens (one launch, or one per kSumRows
+// rows of split tiles); the plan's work split is the VALU kernels'.
 void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
                      uint16_t* y, int Mreal, uint8_t* ws, hipStream_t st) {
   const uint4* xa = reinterpret_cast<const uint4*>(ws + p.off_frag);
@@ -1230,6 +1415,12 @@ void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t
     static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
     const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
     const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
+    if (d->format == BGG_FMT_PTQ1_0) {
+      hipLaunchKernelGGL((k_gemv_ptq1_mx<8>), grid, block, 0, st, packed, d->scale_offset,
+                         d->chunks, p.G, d->N, Sg, Mreal, xa, xs, xc, sums, t0, ntl, nta, sgb,
+                         light, y);
+      continue;
+    }
 #define BGG_MMA(BPS)                                                                           \
   hipLaunchKernelGGL((k_gemv_pq2_mx<BPS, 8>), grid, block, 0, st, packed, d->scale_offset,    \
                      d->chunks, p.G, d->N, Sg, Mreal, xa, xs, xc, sums, t0, ntl, nta, sgb,    \
@@ -1291,7 +1482,9 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
   const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
   const char* fused = M == 1 && gemv_fuse_enabled(d->format) ? "true" : "false";
   int n;
-  if (p.mma) {
+  if (p.mma && d->format == BGG_FMT_PTQ1_0) {
+    n = snprintf(out, cap, "k_gemv_ptq1_mx<8>");
+  } else if (p.mma) {
     n = snprintf(out, cap, "k_gemv_pq2_mx<%d, 8>", (int)p.per_slice);
   } else if (d->format == BGG_FMT_PQ2_0) {
     n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8, %s>", mb, (int)p.per_slice, fused);

@@ -281,29 +281,37 @@ def test_gemv_zero_weights_and_repeat_calls(env, fmt):
     assert np.array_equal(y_a[:1], y_b)
 
 
-@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152)])
-def test_gemv_pq2_tokens_do_not_mix(env, N, K):
-    """PQ2_0 with 3..16 tokens runs on the matrix cores with 16 token slots
-    and the integer arithmetic of the one-token kernel (two tokens: the VALU
-    kernel): a token's y must not depend on the other tokens or on M, and
-    must equal its one-token y bit for bit; M = 16 must match the oracle."""
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152), (200, 5248)])
+def test_gemv_tokens_do_not_mix(env, fmt, N, K):
+    """Several tokens run on the matrix cores with 16 token slots and the
+    integer arithmetic of the VALU kernels (PQ2_0 with two tokens: the VALU
+    kernel): a token's y must not depend on the other tokens or on M (bit
+    for bit), must equal its one-token y bit for bit where the one-token
+    kernel splits K the same way (PQ2_0 always; PTQ1_0 when it takes whole
+    periods), and M = 16 must match the oracle."""
     bgg, torch = env
-    say(f"gemv pq2 tokens do not mix {N}x{K}")
+    say(f"gemv tokens do not mix {fmt} {N}x{K}")
     T, S = gen_matrix(101, 3, N, K)
-    d = Dev(bgg, torch, "PQ2_0", T, S)
+    d = Dev(bgg, torch, fmt, T, S)
     x = synth.activations_f16(101, 4, 16, K)
     ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
-    assert bgg.bgg_gemv_kernel_name(d.desc, 3).startswith("k_gemv_pq2_mx<")
-    assert bgg.bgg_gemv_kernel_name(d.desc, 2).startswith("k_gemv_pq2<")
+    mx = "k_gemv_pq2_mx<" if fmt == "PQ2_0" else "k_gemv_ptq1_mx<"
+    assert bgg.bgg_gemv_kernel_name(d.desc, 3).startswith(mx)
     y16 = d.gemv(x, ws=ws)
-    ref = oracle_y("PQ2_0", T, S, x)
+    ref = oracle_y(fmt, T, S, x)
     assert np.all(relerr(y16, ref) <= TOL)
     for M in (2, 3, 7, 15):
         yM = d.gemv(x[16 - M:], ws=ws)
         assert np.array_equal(yM.view(np.uint16), y16[16 - M:].view(np.uint16)), f"M={M}"
+    one = bgg.bgg_gemv_kernel_name(d.desc, 1)
+    same_split = fmt == "PQ2_0" or one.startswith("k_gemv_ptq1<1, 1,")
     for m in (0, 5, 15):
         y1 = d.gemv(x[m:m + 1], ws=ws)
-        assert np.array_equal(y1[0].view(np.uint16), y16[m].view(np.uint16)), f"token {m}"
+        if same_split:
+            assert np.array_equal(y1[0].view(np.uint16), y16[m].view(np.uint16)), f"token {m}"
+        else:
+            assert relerr(y1[0], y16[m].astype(np.float64)) <= TOL
     # the same token in every slot
     xs = np.repeat(x[5:6], 16, axis=0)
     ys = d.gemv(xs, ws=ws)
