@@ -79,8 +79,9 @@ def decode_stack_bench(args, bgg, torch, dev, capture):
     and v, one for o, one for gate and up, one for down, each followed by
     bgg_gemv_run per matrix.  Every matrix has its own device buffer; the 64
     layers reuse layer 0's generated values (the work and the bytes streamed
-    do not depend on them).  GB/s = packed bytes of the step / median wall
-    time of one graph replay."""
+    do not depend on them).  A third set of lines packs q, k, v and gate, up
+    as one matrix each (four calls per layer), for every M.  GB/s = packed
+    bytes of the step / median wall time of one graph replay."""
     import numpy as np
     import synth
     w = synth.WORKLOADS["decode_step"]
@@ -163,8 +164,49 @@ def decode_stack_bench(args, bgg, torch, dev, capture):
                       frac=round(step_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
                       launches=len(groups) + len(calls))
         log(f"  M=1 shared transform: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
-        res["formats"][fmt] = dict(packed_bytes=step_bytes, per_m=per_m, m1_shared_transform=shared)
-        del calls, ws
+        del calls
+        torch.cuda.empty_cache()
+
+        # Grouped projections: the rows of q, k and v packed as one matrix
+        # (N = 8192), those of gate and up as another (N = 34816), so a layer
+        # is four calls; each call transforms its input once.  The same
+        # weights and packed bytes up to the padding of the groups' rows.
+        t0 = time.time()
+        byname = {m.name.split(".")[1]: m for m in mats[:7]}
+        gdefs = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+                 ("down", ("down",))]
+        ghost = {}
+        for gname, parts in gdefs:
+            Ts, Ss = zip(*(synth.workload_matrix(byname[q], seed) for q in parts))
+            T, S = np.concatenate(Ts), np.concatenate(Ss)
+            d = bgg.bgg_describe(fmt, T.shape[0], T.shape[1])
+            ghost[gname] = (d, bgg.bgg_pack_weights(d, T, S))
+            del Ts, Ss, T, S
+        gcalls = [(ghost[gname][0], bgg.upload(ghost[gname][1], dev))
+                  for _ in range(len(mats) // 7) for gname, _ in gdefs]
+        del ghost
+        gbytes = sum(int(d.format_bytes) for d, _ in gcalls)
+        gys = {int(d.N): torch.empty((mmax, int(d.N)), dtype=torch.float16, device=dev)
+               for d, _ in gcalls}
+        wsb = max(bgg.bgg_gemv_workspace_size(d, mmax) for d, _ in gcalls)
+        ws = bgg.workspace(wsb, dev)
+        log(f"  grouped: {gbytes / 1e9:.2f} GB packed in {len(gcalls)} buffers ({time.time() - t0:.1f}s)")
+        grouped = {}
+        for M in ms:
+            def step_grouped(st, M=M):
+                for d, p in gcalls:
+                    bgg.bgg_ternary_gemv(d, p, xs[int(d.K)][:M], gys[int(d.N)][:M], M,
+                                         bgg.BGG_ROTATE_INPUT, ws, st)
+            g = capture(step_grouped)
+            us = median_replay_us(g, args.stack_replays)
+            del g
+            grouped[str(M)] = dict(us_per_step=round(us, 1), gbs=round(gbytes / us / 1e3, 1),
+                                   frac=round(gbytes / us / 1e3 / HBM_PEAK_GBS, 4))
+            log(f"  grouped M={M}: {us:.0f} us per step, {gbytes / us / 1e3:.0f} GB/s")
+        res["formats"][fmt] = dict(packed_bytes=step_bytes, per_m=per_m, m1_shared_transform=shared,
+                                   grouped=dict(packed_bytes=gbytes, launches=len(gcalls),
+                                                per_m=grouped))
+        del gcalls, gys, ws
         torch.cuda.empty_cache()
     return res
 
