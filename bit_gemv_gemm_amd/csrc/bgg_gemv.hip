@@ -801,6 +801,39 @@ __device__ __forceinline__ uint32_t e4m3_of_int(int d) {
   return (d < 0 ? 0x80u : 0u) | ((uint32_t)(p + 7) << 3) | (((a << 3) >> p) - 8);
 }
 
+// One 128-group for the lane's four row blocks: B operands from the code
+// words (lo: K 32 kg .. +15, hi: K 32 kg + 16 .. +31 of the group), the
+// three digit MFMAs issued digit by digit across the row blocks (four
+// independent accumulators, so no MFMA waits for the one before it), then
+// acc[rb] += s[rb] * (2^(e-14) p) per row block.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void mx_group(const i32x8 (&A)[kMxDigits], uint32_t sa, f32x4 c0,
+                                         const u32x2 (&wv)[4], const float (&s)[4],
+                                         f32x4 (&acc)[4]) {
+  i32x8 B[4];
+  f32x4 ag[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const uint32_t lo = wv[rb].x, hi = wv[rb].y;
+    B[rb] = i32x8{(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                  (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+    ag[rb] = c0;
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B[rb], ag[rb], 0, 4, 0, (int)sa, 0, 128);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B[rb], ag[rb], 0, 4, 1, (int)sa, 0, 128);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B[rb], ag[rb], 0, 4, 2, (int)sa, 0, 128);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s[rb], ag[rb][e], acc[rb][e]);
+}
+
 template <int BPS, int W>
 __global__ void __launch_bounds__(64 * W)
     k_gemv_pq2_mx(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
@@ -824,81 +857,68 @@ __global__ void __launch_bounds__(64 * W)
   if (gbeg < G) {
     // K 32 kg .. 32 kg + 31 of group g, row r: 8 bytes at chunk 2 g + kg / 2,
     // half kg % 2 -- uint2 index ((tile C + c) 64 + r) 2 + half
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2* wsrc =
         reinterpret_cast<const u32x2*>(packed) + ((tile * C + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
     const uint16_t* ssrc =
         reinterpret_cast<const uint16_t*>(packed + scale_offset) + tile * G * kTile + col;
-    // The loads of the slice are issued first, group by group (A digits,
-    // scale word, start values, weights, weight scales), with no branch
-    // between them and their use: loads complete in issue order, so group i
-    // waits only for its own loads and those of the groups before it.  The
-    // A operands of at most PRE groups are in flight (registers); those of
-    // group i + PRE are issued once group i is done.  A group past G
-    // re-reads group G - 1 and gets a zero scale.  Lanes of token slots past
-    // M load nothing and multiply zeros (their rows are dropped), so a few
-    // tokens cost few A bytes.
-    constexpr int PRE = BPS <= 5 ? BPS : 4;
+    // The slice runs in batches of NB groups (all BPS groups, or two halves
+    // of eight: the registers hold one batch).  A batch's loads are issued
+    // first, group by group (A digits, scale word, start values, weights,
+    // weight scales), with no branch between them and their use: loads
+    // complete in issue order, so group i waits only for its own loads and
+    // those of the groups before it.  A group past G re-reads group G - 1
+    // and gets a zero scale.  Lanes of token slots past M load no A bytes
+    // and multiply zeros (their rows are dropped), so a few tokens cost few
+    // A bytes.
+    constexpr int NB = BPS <= 5 ? BPS : BPS / 2;
+    static_assert(BPS % NB == 0, "whole batches");
     const bool aload = col < Mreal;
     const int aslot = aload ? col : Mreal - 1;
     const uint4* asrc = xa + (aslot + 16 * kg) * 2;
-    uint4 a[PRE][kMxDigits][2];
-    uint32_t sa[PRE];
-    f32x4 c0[PRE];
-    u32x2 w[BPS][4];
-    uint16_t sc[BPS][4];
-#define BGG_MX_LOAD_A(SLOT, I)                                                  \
-  do {                                                                          \
-    const int64_t g_ = gbeg + (I) < G ? gbeg + (I) : G - 1;                     \
-    _Pragma("unroll") for (int k = 0; k < kMxDigits; ++k) {                    \
-      a[SLOT][k][0] = aload ? asrc[(g_ * kMxDigits + k) * 128] : make_uint4(0, 0, 0, 0); \
-      a[SLOT][k][1] = aload ? asrc[(g_ * kMxDigits + k) * 128 + 1] : make_uint4(0, 0, 0, 0); \
-    }                                                                           \
-    sa[SLOT] = xs[g_ * kMmaSlots + aslot];                                      \
-    c0[SLOT] = *reinterpret_cast<const f32x4*>(xc + g_ * kMmaSlots + 4 * kg);   \
-  } while (0)
+    // (a loop, not unrolled: the second batch's loads must not move above
+    // the first batch's work)
+#pragma unroll 1
+    for (int b0 = 0; b0 < BPS; b0 += NB) {
+      __builtin_amdgcn_sched_barrier(0);
+      uint4 a[NB][kMxDigits][2];
+      uint32_t sa[NB];
+      f32x4 c0[NB];
+      u32x2 w[NB][4];
+      uint16_t sc[NB][4];
 #pragma unroll
-    for (int i = 0; i < BPS; ++i) {
-      const int64_t g = gbeg + i < G ? gbeg + i : G - 1;
-      if (i < PRE) BGG_MX_LOAD_A(i, i);
+      for (int i = 0; i < NB; ++i) {
+        const int64_t g = gbeg + b0 + i < G ? gbeg + b0 + i : G - 1;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        w[i][rb] = __builtin_nontemporal_load(wsrc + g * (4 * kTile) + rb * 32);
-        sc[i][rb] = ssrc[g * kTile + 16 * rb];
+        for (int k = 0; k < kMxDigits; ++k) {
+          a[i][k][0] = aload ? asrc[(g * kMxDigits + k) * 128] : make_uint4(0, 0, 0, 0);
+          a[i][k][1] = aload ? asrc[(g * kMxDigits + k) * 128 + 1] : make_uint4(0, 0, 0, 0);
+        }
+        sa[i] = xs[g * kMmaSlots + aslot];
+        c0[i] = *reinterpret_cast<const f32x4*>(xc + g * kMmaSlots + 4 * kg);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          w[i][rb] = __builtin_nontemporal_load(wsrc + g * (4 * kTile) + rb * 32);
+          sc[i][rb] = ssrc[g * kTile + 16 * rb];
+        }
+      }
+      // keep the scheduler from sinking the loads towards their uses
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        i32x8 A[kMxDigits];
+#pragma unroll
+        for (int k = 0; k < kMxDigits; ++k) {
+          A[k] = i32x8{(int)a[i][k][0].x, (int)a[i][k][0].y, (int)a[i][k][0].z,
+                       (int)a[i][k][0].w, (int)a[i][k][1].x, (int)a[i][k][1].y,
+                       (int)a[i][k][1].z, (int)a[i][k][1].w};
+        }
+        const bool live = gbeg + b0 + i < G;
+        float s[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) s[rb] = live ? h2f(sc[i][rb]) : 0.0f;
+        mx_group(A, sa[i], c0[i], w[i], s, acc);
       }
     }
-    // keep the scheduler from sinking the loads towards their uses
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < BPS; ++i) {
-      constexpr int kPre = PRE;
-      const int slot = i % kPre;
-      i32x8 A[kMxDigits];
-#pragma unroll
-      for (int k = 0; k < kMxDigits; ++k) {
-        A[k] = i32x8{(int)a[slot][k][0].x, (int)a[slot][k][0].y, (int)a[slot][k][0].z,
-                     (int)a[slot][k][0].w, (int)a[slot][k][1].x, (int)a[slot][k][1].y,
-                     (int)a[slot][k][1].z, (int)a[slot][k][1].w};
-      }
-      const uint32_t sac = sa[slot];
-      const f32x4 cc = c0[slot];
-      if (i + PRE < BPS) BGG_MX_LOAD_A(slot, i + PRE);
-      const bool live = gbeg + i < G;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const uint32_t lo = w[i][rb].x, hi = w[i][rb].y;
-        const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                         (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
-        f32x4 ag = cc;
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, ag, 0, 4, 0, (int)sac, 0, 128);
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, ag, 0, 4, 1, (int)sac, 0, 128);
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, ag, 0, 4, 2, (int)sac, 0, 128);
-        const float s = live ? h2f(sc[i][rb]) : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s, ag[e], acc[rb][e]);
-      }
-    }
-#undef BGG_MX_LOAD_A
   }
   // D layout: lane holds weight row 16 rb + col and token slots 4 kg + e
 #pragma unroll
@@ -1057,22 +1077,14 @@ __global__ void __launch_bounds__(64 * W)
       const f32x4 cc = c0[slot];
       if (gi + PRE < kPeriodGroups) BGG_MX_LOAD_A(slot, gi + PRE);
       const bool live = g0 + gi < G;
+      u32x2 wv[4];
+      float s[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 wv = *reinterpret_cast<const u32x2*>(
-            &cw[(col + 16 * rb) * kPtqCodeStride + 8 * gi + 2 * kg]);
-        const uint32_t lo = wv.x, hi = wv.y;
-        const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                         (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
-        f32x4 ag = cc;
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, ag, 0, 4, 0, (int)sac, 0, 128);
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, ag, 0, 4, 1, (int)sac, 0, 128);
-        ag = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, ag, 0, 4, 2, (int)sac, 0, 128);
-        const float s = live ? h2f(sc[gi][rb]) : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s, ag[e], acc[rb][e]);
+        wv[rb] = *reinterpret_cast<const u32x2*>(&cw[(col + 16 * rb) * kPtqCodeStride + 8 * gi + 2 * kg]);
+        s[rb] = live ? h2f(sc[gi][rb]) : 0.0f;
       }
+      mx_group(A, sac, cc, wv, s, acc);
     }
   }
 #undef BGG_MX_LOAD_A
@@ -1209,7 +1221,7 @@ int64_t gemv_mma_min_tokens(int format) {
   static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 3);
   static const int64_t ptq1 = env_int("BGG_GEMV_PTQ1_MMA_MIN", 2);
   const int64_t m = format == BGG_FMT_PQ2_0 ? pq2 : ptq1;
-  return m < 2 ? 2 : m;
+  return m < 1 ? 1 : m;
 }
 
 // Compute units of the current device (cached per device).
@@ -1272,7 +1284,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     // with 8)
     p.W = p.mma || gemv_m_bucket(M) >= 4 ? 8 : ptq1_w;
     p.per_slice = 1;
-    while (p.per_slice < 2 && gemv_m_bucket(M) == 1 && p.NT * P * p.per_slice < ptq1_target)
+    while (p.per_slice < 2 && !p.mma && gemv_m_bucket(M) == 1 && p.NT * P * p.per_slice < ptq1_target)
       p.per_slice *= 2;
     p.units = P * p.per_slice;
     p.S = p.units;
@@ -1292,15 +1304,13 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   }
   // [row sums][digit words][group Q][group F]: the row sums are the same for
   // every call, the rest depends only on the format, K and M
-  // (for several tokens the frag region also holds the matrix-core
-  // kernels' A digits, and the group-Q region their scale words and start
-  // values)
+  // (the frag region also holds the matrix-core kernels' A digits, and the
+  // group-Q region their scale words and start values: reserved for every
+  // M, so that the size does not depend on which kernel runs)
   uint64_t frag_bytes = (uint64_t)p.slots * p.frag_words_per_token * 4;
   uint64_t meta_q_bytes = (uint64_t)p.slots * p.gpad * 4;
-  if (M >= 2) {
-    frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
-    meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 8);
-  }
+  frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
+  meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 8);
   p.off_sums = 0;
   p.off_frag = kSumBytes;
   uint64_t off = align256(p.off_frag + frag_bytes);
@@ -1480,7 +1490,8 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
     return fail(BGG_ERR_SHAPE, "bgg_gemv_kernel_name: M must be in 1..16 (got %lld)", (long long)M);
   const GemvPlan p = plan_gemv(d, M);
   const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
-  const char* fused = M == 1 && gemv_fuse_enabled(d->format) ? "true" : "false";
+  const char* fused =
+      M == 1 && gemv_fuse_enabled(d->format) && !p.mma ? "true" : "false";
   int n;
   if (p.mma && d->format == BGG_FMT_PTQ1_0) {
     n = snprintf(out, cap, "k_gemv_ptq1_mx<8>");
@@ -1549,7 +1560,8 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
     return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned buffer");
   // (the one-launch kernel wants the digit words of a block or period to
   // fill whole 64-byte lines: a workspace aligned to 64 bytes)
-  if (M != 1 || !gemv_fuse_enabled(d->format) || ((uintptr_t)workspace & 63)) {
+  if (M != 1 || !gemv_fuse_enabled(d->format) || ((uintptr_t)workspace & 63) ||
+      M >= gemv_mma_min_tokens(d->format)) {
     st = bgg_gemv_prepare(d, x_dev, M, flags, workspace, workspace_bytes, stream);
     if (st) return st;
     return bgg_gemv_run(d, packed_dev, y_dev, M, workspace, workspace_bytes, stream);

@@ -282,7 +282,8 @@ def test_gemv_zero_weights_and_repeat_calls(env, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152), (200, 5248)])
+@pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152), (200, 5248),
+                                 (8192, 6144)])
 def test_gemv_tokens_do_not_mix(env, fmt, N, K):
     """Several tokens run on the matrix cores with 16 token slots and the
     integer arithmetic of the VALU kernels (PQ2_0 with two tokens: the VALU
@@ -298,6 +299,9 @@ def test_gemv_tokens_do_not_mix(env, fmt, N, K):
     ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
     mx = "k_gemv_pq2_mx<" if fmt == "PQ2_0" else "k_gemv_ptq1_mx<"
     assert bgg.bgg_gemv_kernel_name(d.desc, 3).startswith(mx)
+    if fmt == "PQ2_0" and (N, K) == (8192, 6144):
+        # eight groups per wave: the kernel runs them as two batches of four
+        assert bgg.bgg_gemv_kernel_name(d.desc, 3) == "k_gemv_pq2_mx<8, 8>"
     y16 = d.gemv(x, ws=ws)
     ref = oracle_y(fmt, T, S, x)
     assert np.all(relerr(y16, ref) <= TOL)
