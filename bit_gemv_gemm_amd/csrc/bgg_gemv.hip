@@ -1121,18 +1121,24 @@ __global__ void __launch_bounds__(64 * W)
   }
 }
 
-// Activations for the matrix-core kernel.  Per 128-group and token slot
-// (slots past M repeat token M - 1): the same x', e and q as the encoding
-// above; q's three base-32 digits as e4m3 bytes in the A operand order
-// (xa: per group and digit, 64 lanes x 32 bytes), the scale bytes
-// 127 + e - 14 + 10 - 5 k of digit k (xs: one word per group and slot) and
-// -2^(e-14) sum q (xc).  grid: G blocks of 256 threads, 16 lanes per slot.
-__global__ void __launch_bounds__(256)
+// Activations for the matrix-core kernels.  Per 128-group and token slot:
+// the same x', e and q as the encoding above; q's three base-32 digits as
+// e4m3 bytes in the A operand order (xa: per group and digit, 64 lanes x 32
+// bytes), the scale bytes 127 + e - 14 + 10 - 5 k of digit k (xs: one word
+// per group and slot) and -2^(e-14) sum q (xc).  Only the slots below M
+// rounded up to four are written (slots past M-1 repeat token M - 1): the
+// GEMV's lanes of slots past M load nothing, and their rows are dropped.
+// grid: (G, ceil(M / 4)) blocks of 64 threads, four slots of one group per
+// block, 16 lanes per slot.
+constexpr int kPrepMxSlots = 4;
+__global__ void __launch_bounds__(64)
     k_gemv_prep_mx(const uint16_t* __restrict__ x, int64_t K, int M, int rotate,
                    uint32_t* __restrict__ xa, uint32_t* __restrict__ xs, float* __restrict__ xc) {
-  __shared__ int16_t qs[kMmaSlots][kGroup];
+  // the e4m3 bytes of every digit, slot and group position
+  __shared__ uint8_t dig[kMxDigits][kPrepMxSlots][kGroup];
   const int64_t blk = blockIdx.x;
-  const int t = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int ts = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int t = (int)blockIdx.y * kPrepMxSlots + ts;
   const int src = t < M ? t : M - 1;
   float v[8];
   load8h(x + (int64_t)src * K + blk * kGroup + 8 * l16, v);
@@ -1151,12 +1157,22 @@ __global__ void __launch_bounds__(256)
   int e = 0;
   frexpf(amax, &e);
   int qsum = 0;
+  uint32_t b[kMxDigits][2] = {{0, 0}, {0, 0}, {0, 0}};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int q = amax > 0.0f ? (int)rintf(ldexpf(v[j], 14 - e)) : 0;
-    qs[t][8 * l16 + j] = (int16_t)q;
     qsum += q;
+    const int d2 = ((q + 16) & 31) - 16;
+    const int r = (q - d2) >> 5;
+    const int d1 = ((r + 16) & 31) - 16;
+    const int d0 = (r - d1) >> 5;
+    b[0][j >> 2] |= e4m3_of_int(d0) << (8 * (j & 3));
+    b[1][j >> 2] |= e4m3_of_int(d1) << (8 * (j & 3));
+    b[2][j >> 2] |= e4m3_of_int(d2) << (8 * (j & 3));
   }
+#pragma unroll
+  for (int k = 0; k < kMxDigits; ++k)
+    *reinterpret_cast<uint2*>(&dig[k][ts][8 * l16]) = make_uint2(b[k][0], b[k][1]);
   qsum += xor16_i<1>(qsum);
   qsum += xor16_i<2>(qsum);
   qsum += xor16_i<4>(qsum);
@@ -1168,21 +1184,20 @@ __global__ void __launch_bounds__(256)
     xc[blk * kMmaSlots + t] = amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
   }
   __syncthreads();
-  // 3 digits x 64 lanes x 8 words per group
-  for (int it = threadIdx.x; it < kMxDigits * 64 * 8; it += 256) {
-    const int k = it >> 9, l = (it >> 3) & 63, dd = it & 7;
-    const int tt = l & 15, ga = l >> 4;
+  // this block's words: 3 digits x 4 lane groups x 4 slots x 8 words; word
+  // dd of lane (slot tt, lane group ga) holds A bytes e = 4 dd .. 4 dd + 3,
+  // i.e. the digits at the group positions that the B nibbles of those K
+  // carry
+#pragma unroll
+  for (int it0 = 0; it0 < kMxDigits * 4 * kPrepMxSlots * 8; it0 += 64) {
+    const int it = it0 + threadIdx.x;
+    const int k = it >> 7, ga = (it >> 5) & 3, tl = (it >> 3) & 3, dd = it & 7;
+    const uint8_t* row = dig[k][tl];
     uint32_t word = 0;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int q = qs[tt][mx_pos_of_k(mx_k_of_a(ga, 4 * dd + bb))];
-      const int d2 = ((q + 16) & 31) - 16;
-      const int r = (q - d2) >> 5;
-      const int d1 = ((r + 16) & 31) - 16;
-      const int d0 = (r - d1) >> 5;
-      const int d = k == 0 ? d0 : k == 1 ? d1 : d2;
-      word |= e4m3_of_int(d) << (8 * bb);
-    }
+    for (int bb = 0; bb < 4; ++bb)
+      word |= (uint32_t)row[mx_pos_of_k(mx_k_of_a(ga, 4 * dd + bb))] << (8 * bb);
+    const int l = 16 * ga + (int)blockIdx.y * kPrepMxSlots + tl;
     xa[((blk * kMxDigits + k) * 64 + l) * 8 + dd] = word;
   }
 }
@@ -1213,12 +1228,12 @@ struct GemvPlan {
 };
 
 // The fewest tokens that run on the matrix-core kernels (fewer: the VALU
-// kernels, up to four tokens per pass; both give the same bits).  PQ2_0 with
-// two tokens measured faster on the VALU kernel (one pass, little dot8
-// work); PTQ1_0's VALU kernel spends a LUT lookup and dot8 work per byte
-// and token.
+// kernels, up to four tokens per pass; both give the same bits).  From two
+// tokens on they measured faster for both packings (the VALU kernels spend
+// dot8 work per packed word or byte and token); one token stays on the
+// VALU kernels, whose one-launch form also encodes the activations.
 int64_t gemv_mma_min_tokens(int format) {
-  static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 3);
+  static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 2);
   static const int64_t ptq1 = env_int("BGG_GEMV_PTQ1_MMA_MIN", 2);
   const int64_t m = format == BGG_FMT_PQ2_0 ? pq2 : ptq1;
   return m < 1 ? 1 : m;
@@ -1333,7 +1348,8 @@ void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   if (p.mma) {
     uint32_t* xs = reinterpret_cast<uint32_t*>(ws + p.off_meta_q);
-    hipLaunchKernelGGL(k_gemv_prep_mx, dim3((unsigned)p.G), dim3(256), 0, st, x, d->K, (int)M,
+    hipLaunchKernelGGL(k_gemv_prep_mx, dim3((unsigned)p.G, (unsigned)ceil_div(M, kPrepMxSlots)),
+                       dim3(64), 0, st, x, d->K, (int)M,
                        rotate, reinterpret_cast<uint32_t*>(ws + p.off_frag), xs,
                        reinterpret_cast<float*>(xs + p.G * kMmaSlots));
     return;

@@ -191,12 +191,12 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * Arithmetic.  The activations are carried as 15-bit integers q with a
  * power-of-two scale per 128-block (absolute error at most 2^-14 of the
  * block's largest |x'|); each group's trit sum p = sum t q is exact, and is
- * scaled and accumulated in fp32 in a fixed order.  PTQ1_0 (any M) and
- * PQ2_0 with one or two tokens read each 64-row tile once per group of up
- * to four tokens (one kernel launch per group); PQ2_0 with 3..16 tokens
- * reads it once for all tokens (one launch, matrix cores), with the same
- * sums and fp32 steps, so a token's y does not depend on the other tokens
- * or on M.
+ * scaled and accumulated in fp32 in a fixed order.  One token: one
+ * pass over the weights on the vector ALUs.  2..16 tokens: one pass for all
+ * of them on the matrix cores, with the same sums and fp32 steps, so a
+ * token's y does not depend on the other tokens or on M (PTQ1_0 at M == 1
+ * may split a 640-weight period between two waves, whose partial sums then
+ * round differently in the last bits).
  * Where K is split over workgroups their partial rows are added as 64-bit
  * fixed-point integers (resolution 2^-30, magnitude below 2^19), whose sum
  * does not depend on the order.  y is rounded to fp16 once, and the same
@@ -234,8 +234,9 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
  * calls).  The last template argument is true for the one-launch kernel
  * that also encodes the activations (M == 1) and false for the kernel that
  * reads a preparation (bgg_gemv_run launches that one, with the same other
- * arguments).  PQ2_0 with 3..16 tokens names the matrix-core kernel, e.g.
- * "k_gemv_pq2_mx<5, 8>", which covers all M tokens in one launch.
+ * arguments).  2..16 tokens name the matrix-core kernel, e.g.
+ * "k_gemv_pq2_mx<5, 8>" or "k_gemv_ptq1_mx<8>", which covers all M tokens
+ * in one launch.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);

@@ -286,9 +286,8 @@ def test_gemv_zero_weights_and_repeat_calls(env, fmt):
                                  (8192, 6144)])
 def test_gemv_tokens_do_not_mix(env, fmt, N, K):
     """Several tokens run on the matrix cores with 16 token slots and the
-    integer arithmetic of the VALU kernels (PQ2_0 with two tokens: the VALU
-    kernel): a token's y must not depend on the other tokens or on M (bit
-    for bit), must equal its one-token y bit for bit where the one-token
+    integer arithmetic of the VALU kernels: a token's y must not depend on
+    the other tokens or on M (bit for bit), must equal its one-token y bit for bit where the one-token
     kernel splits K the same way (PQ2_0 always; PTQ1_0 when it takes whole
     periods), and M = 16 must match the oracle."""
     bgg, torch = env
@@ -298,7 +297,7 @@ def test_gemv_tokens_do_not_mix(env, fmt, N, K):
     x = synth.activations_f16(101, 4, 16, K)
     ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
     mx = "k_gemv_pq2_mx<" if fmt == "PQ2_0" else "k_gemv_ptq1_mx<"
-    assert bgg.bgg_gemv_kernel_name(d.desc, 3).startswith(mx)
+    assert bgg.bgg_gemv_kernel_name(d.desc, 2).startswith(mx)
     if fmt == "PQ2_0" and (N, K) == (8192, 6144):
         # eight groups per wave: the kernel runs them as two batches of four
         assert bgg.bgg_gemv_kernel_name(d.desc, 3) == "k_gemv_pq2_mx<8, 8>"
