@@ -172,7 +172,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // L = 0..3, which sit next to each other (one 16-byte store).
 template <int NG>
 __device__ __forceinline__ void wave_pack_pq2(const uint16_t* sd, uint32_t* __restrict__ out,
-                                              int64_t c0, int64_t C, int lane) {
+                                              int64_t c0, int64_t C, int lane,
+                                              int64_t cout0 = 0) {
 #pragma unroll
   for (int it0 = 0; it0 < NG * 16; it0 += 64) {
     const int it = it0 + lane;
@@ -186,11 +187,20 @@ __device__ __forceinline__ void wave_pack_pq2(const uint16_t* sd, uint32_t* __re
 #pragma unroll
         for (int L = 0; L < 4; ++L) wd[L] |= ((v >> (4 * L)) & 15u) << (4 * n);
       }
-      *reinterpret_cast<uint4*>(out + c * kPqFragWords + d * 8 + par * 4) =
+      *reinterpret_cast<uint4*>(out + (c - cout0) * kPqFragWords + d * 8 + par * 4) =
           make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
   }
 }
+
+// Where word i of a wave's PTQ1_0 digit words sits: contiguous (global
+// workspace), or (HOLES) in the unused upper halves of the LUT's 256-byte
+// rows, 32 words per row -- the one-launch kernel keeps them in LDS there.
+template <bool HOLES>
+__device__ __forceinline__ int ptq1_word(int i) {
+  return HOLES ? (i >> 5) * (kLutRowBytes / 4) + (i & 31) : i;
+}
+constexpr int kPtqHoleRows = (kPtqFragWords + 31) / 32;  // LUT rows per wave
 
 // PTQ1_0 digit words of one period (528 words per token) from sd.  Word
 // (byte jb, L), jb < 128: nibble i = digit L of q at period position
@@ -201,6 +211,7 @@ __device__ __forceinline__ void wave_pack_pq2(const uint16_t* sd, uint32_t* __re
 // the words one wave needs for a few consecutive bytes are contiguous.
 // Lane jb packs the four words of byte jb (and the upper four of a
 // straddling byte), two bytes per lane.
+template <bool HOLES = false>
 __device__ __forceinline__ void wave_pack_ptq1(const uint16_t* sd, uint32_t* __restrict__ out,
                                                int b, int slot, int lane) {
 #pragma unroll
@@ -222,9 +233,10 @@ __device__ __forceinline__ void wave_pack_ptq1(const uint16_t* sd, uint32_t* __r
           lo[L] |= nib;
       }
     }
-    *reinterpret_cast<uint4*>(out + (jb * b + slot) * 4) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(out + ptq1_word<HOLES>((jb * b + slot) * 4)) =
+        make_uint4(lo[0], lo[1], lo[2], lo[3]);
     if ((5 * jb + 4) / kGroup != first_group)  // bytes 25, 51, 76, 102: s = first_group
-      *reinterpret_cast<uint4*>(out + ((kPeriodBytes + first_group) * b + slot) * 4) =
+      *reinterpret_cast<uint4*>(out + ptq1_word<HOLES>(((kPeriodBytes + first_group) * b + slot) * 4)) =
           make_uint4(hi[0], hi[1], hi[2], hi[3]);
   }
 }
@@ -388,24 +400,21 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
 
 // ---------------------------------------------------------------------------
 // One-launch GEMV for one token: every wave first encodes the activation
-// blocks of its own K slice (the same words the prep kernel writes, laid out
-// the same way, in one of kFuseCopies copies in the workspace), then reads
-// them back with scalar loads.  Workgroups that cover the same K slice and
-// copy write identical words.  The wave
-// waits for its own stores (s_waitcnt vmcnt(0): stores complete in L2)
-// before its first scalar load; the scalar cache is invalidated at every
-// launch, and the digit words of a PQ2_0 group (256 bytes) or a PTQ1_0
-// period (2112 bytes) fill whole 64-byte lines, so a line is only read after
-// it was written and cannot hold another call's words.  The per-block meta
-// (4 bytes per block, many blocks to a line) is taken from the registers of
-// the lanes that computed it instead.  The writes
-// go through their own pointers so that the compiler, which cannot see that
-// they reach the memory the scalar loads read, keeps those loads scalar;
-// the wait and a scheduling barrier keep them after the stores.
+// blocks of its own K slice (the same digit words the prep kernel writes,
+// laid out the same way) into LDS and reads them from there: PQ2_0 into a
+// per-wave array, PTQ1_0 into the unused upper halves of the LUT's rows.
+// No global round trip: a wait for the wave's own global stores
+// (s_waitcnt vmcnt(0)) would also wait for every weight load issued before
+// them.  The per-block meta comes from the registers of the lanes that
+// computed it.  (A PTQ1_0 workgroup of 16 waves has too few LUT rows; its
+// waves store the words to one of kFuseCopies copies in the workspace, wait
+// for those stores and read them back with scalar loads: the scalar cache
+// is invalidated at every launch and a period's words fill whole 64-byte
+// lines, so no line is read before it is written.)
 // ---------------------------------------------------------------------------
 struct FuseArgs {
   const uint16_t* x;  // the token row, K fp16 values
-  uint32_t* frag;     // = the kernel's frag: kFuseCopies copies of the digit words
+  uint32_t* frag;     // kFuseCopies copies of the digit words (16-wave PTQ1_0 only)
   int32_t* metaQ;     // null: the meta stays in registers
   float* metaF;
   int rotate;
@@ -436,6 +445,9 @@ __global__ void __launch_bounds__(64 * W)
   static_assert(!FUSE || M == 1, "the one-launch GEMV is for one token");
   __shared__ float red[W][M][64];
   __shared__ __attribute__((aligned(16))) uint16_t sd_stage[FUSE ? W * BPS * kGroup : 8];
+  // one-launch: each wave's digit words stay in LDS (chunks of its slice)
+  constexpr int kWaveFrag = 2 * BPS * kPqFragWords;
+  __shared__ __attribute__((aligned(16))) uint32_t wfrag[FUSE ? W * kWaveFrag : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
@@ -453,7 +465,7 @@ __global__ void __launch_bounds__(64 * W)
         reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
     EncodeRaw<BPS> xraw;
     if (FUSE) xraw = wave_encode_load<BPS>(fa.x, G, gbeg, true, lane);
-    const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
+    uint32_t* wf = wfrag + (FUSE ? wave * kWaveFrag : 0);
     // Every load of the slice is issued before any is used, without branches
     // (a group past G re-reads group G-1 and gets a zero weight below).
     uint4 w[2 * BPS];
@@ -474,16 +486,14 @@ __global__ void __launch_bounds__(64 * W)
       const EncodeMeta<BPS> em =
           wave_encode_finish<BPS>(xraw, gbeg, fa.rotate, sdw, lane, fa.metaQ, fa.metaF, gpad);
       wave_lds_sync();
-      wave_pack_pq2<BPS>(sdw, fa.frag + fcopy, 2 * gbeg, C, lane);
-      // the group meta straight from the registers: other waves' meta share
-      // its cache lines, and a scalar load could cache them before they are
-      // written (zero past G, like the prepared meta)
+      wave_pack_pq2<BPS>(sdw, wf, 2 * gbeg, C, lane, 2 * gbeg);
+      // the group meta straight from the registers
 #pragma unroll
       for (int i = 0; i < BPS; ++i) {
         gf[i][0] = em.f_of(i);
         gq[i][0] = em.q_of(i);
       }
-      wait_own_stores();
+      wave_lds_sync();
     } else {
 #pragma unroll
       for (int i = 0; i < BPS; ++i)
@@ -514,13 +524,22 @@ __global__ void __launch_bounds__(64 * W)
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const uint32_t* xf = frag + fcopy + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
+        const uint32_t* xf = FUSE ? wf + (2 * (g - gbeg)) * kPqFragWords
+                                  : frag + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
         int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+        // one-launch: the group's 64 digit words from LDS, all reads issued
+        // before the first use (a read takes far longer than its four dot8)
+        uint4 fl[FUSE ? 16 : 1];
+        if (FUSE) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) fl[q] = reinterpret_cast<const uint4*>(xf)[q];
+        }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            const uint32_t* f = xf + c * kPqFragWords + d * 8;
+            const uint32_t* f =
+                FUSE ? reinterpret_cast<const uint32_t*>(&fl[c * 8 + d * 2]) : xf + c * kPqFragWords + d * 8;
             const int e = (int)E[c * 4 + d], o = (int)O[c * 4 + d];
             a0 = __builtin_amdgcn_sdot8(e, (int)f[0], a0, false);
             a1 = __builtin_amdgcn_sdot8(e, (int)f[1], a1, false);
@@ -568,7 +587,7 @@ __device__ __forceinline__ void ptq1_close(int (&a)[M][4], float (&acc)[M], cons
 // computed, then both are awaited.  Without the explicit wait the compiler
 // waits for everything at the first use of batch b, i.e. right after issuing
 // batch b+1, and the scalar-load latency is paid once per batch.
-template <int M, int H, int PART>
+template <int M, int H, int PART, bool HOLES>
 __device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (&sc)[kPeriodGroups],
                                           const float (&gf)[kPeriodGroups][M],
                                           const uint32_t* __restrict__ fp, const char* lbase, uint32_t lane_off, float (&acc)[M]) {
@@ -602,13 +621,14 @@ __device__ __forceinline__ void ptq1_part(const uint4 (&w)[8 / H], const float (
 #pragma unroll
       for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int L = 0; L < 4; ++L) fr[buf][j][m][L] = fp[(jb * M + m) * 4 + L];
+        for (int L = 0; L < 4; ++L) fr[buf][j][m][L] = fp[ptq1_word<HOLES>((jb * M + m) * 4 + L)];
       const int k_first = (5 * jb) / kGroup;
       if ((5 * jb + 4) / kGroup != k_first) {
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-          for (int L = 0; L < 4; ++L) up[buf][m][L] = fp[(kPeriodBytes * M + k_first * M + m) * 4 + L];
+          for (int L = 0; L < 4; ++L)
+            up[buf][m][L] = fp[ptq1_word<HOLES>((kPeriodBytes * M + k_first * M + m) * 4 + L)];
       }
     }
   };
@@ -700,6 +720,10 @@ __global__ void __launch_bounds__(64 * W)
   }
   __builtin_amdgcn_sched_barrier(0);
   const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
+  // one-launch: the wave's digit words in LDS, in the unused upper halves
+  // of LUT rows wave * kPtqHoleRows .. (when the workgroup's waves fit)
+  constexpr bool kHoles = FUSE && W * kPtqHoleRows <= 256;
+  uint32_t* holes = lut + wave * kPtqHoleRows * (kLutRowBytes / 4) + kLutRowBytes / 8;
   // the LUT is built while the loads are in flight (with FUSE: while x is)
   build_lut32(lut, lut_seed);
   __syncthreads();
@@ -711,8 +735,13 @@ __global__ void __launch_bounds__(64 * W)
     em = wave_encode_finish<kPeriodGroups>(xraw, p * kPeriodGroups, fa.rotate, sdw, lane, fa.metaQ,
                                            fa.metaF, gpad);
     wave_lds_sync();
-    wave_pack_ptq1(sdw, fa.frag + fcopy + p * kPtqFragWords, 1, 0, lane);
-    wait_own_stores();
+    if (kHoles) {
+      wave_pack_ptq1<true>(sdw, holes, 1, 0, lane);
+      wave_lds_sync();
+    } else {
+      wave_pack_ptq1(sdw, fa.frag + fcopy + p * kPtqFragWords, 1, 0, lane);
+      wait_own_stores();
+    }
   }
 
   float acc[M];
@@ -730,14 +759,14 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
       for (int m = 0; m < M; ++m) gf[k][m] = FUSE ? em.f_of(k) : metaF[(int64_t)m * gpad + gp + k];
     }
-    const uint32_t* fp = frag + fcopy + p * kPtqFragWords * M;
+    const uint32_t* fp = kHoles ? holes : frag + fcopy + p * kPtqFragWords * M;
     const uint32_t lane_off = lut_lane_off(lane);
     const char* lbase = reinterpret_cast<const char*>(lut);
     static_assert(H == 1 || H == 2, "one or two parts per period");
     if (H == 1 || part == 0)
-      ptq1_part<M, H, 0>(w, sc, gf, fp, lbase, lane_off, acc);
+      ptq1_part<M, H, 0, kHoles>(w, sc, gf, fp, lbase, lane_off, acc);
     else
-      ptq1_part<M, H, H - 1>(w, sc, gf, fp, lbase, lane_off, acc);
+      ptq1_part<M, H, H - 1, kHoles>(w, sc, gf, fp, lbase, lane_off, acc);
   }
   wg_finish<M, W>(acc, red, wave, lane, tile * kTile + lane, N, Mreal, ws.Sg,
                   ws.local * kTile + lane, sums, y);
