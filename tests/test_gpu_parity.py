@@ -321,6 +321,69 @@ def test_gemv_tokens_do_not_mix(env, fmt, N, K):
     assert np.all(ys.view(np.uint16) == y16[5].view(np.uint16))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K,M", [(1, 128, 16), (1, 640, 2), (65, 256, 5), (64, 128, 16),
+                                   (4097, 640, 2), (130, 1152, 16), (300, 5248, 9)])
+def test_gemv_matrix_core_edges(env, fmt, N, K, M):
+    """Matrix-core GEMV edge shapes: one row, one 128-group, ragged tiles
+    (65 rows; 4097 rows = 64 tiles and one row), K not a multiple of the
+    PTQ1_0 period (5248 = 8 periods and one group); every output checked.
+    With a single output per token the per-row bar would divide by one dot
+    product, which can nearly cancel (-9e-5 for one token here); such
+    shapes are held to the same bar pooled over all tokens."""
+    bgg, torch = env
+    say(f"gemv matrix-core edges {fmt} N={N} K={K} M={M}")
+    T, S = gen_matrix(111, 5, N, K)
+    x = synth.activations_f16(111, 6, M, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    assert "_mx<" in bgg.bgg_gemv_kernel_name(d.desc, M)
+    y = d.gemv(x)
+    assert not np.isnan(y).any()
+    ref = oracle_y(fmt, T, S, x)
+    if N < 64:
+        assert np.max(np.abs(y - ref)) <= TOL * np.max(np.abs(ref))
+    else:
+        assert np.all(relerr(y, ref) <= TOL)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_matrix_core_every_token_count(env, fmt):
+    """Every M from 2 to 16 on one shape, each against the oracle, one
+    workspace for all calls (sized for 16 tokens)."""
+    bgg, torch = env
+    N, K = 257, 1408
+    say(f"gemv matrix-core M=2..16 {fmt}")
+    T, S = gen_matrix(121, 7, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
+    x = synth.activations_f16(121, 8, 16, K)
+    ref = oracle_y(fmt, T, S, x)
+    for M in range(2, 17):
+        y = d.gemv(x[:M], ws=ws)
+        assert np.all(relerr(y, ref[:M]) <= TOL), f"M={M}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_workspace_shared_across_shapes(env, fmt):
+    """One zero-filled workspace serves calls of different K, N and M in any
+    order (the split-K row sums are left at zero by every launch)."""
+    bgg, torch = env
+    say(f"gemv shared workspace {fmt}")
+    shapes = [(5120, 17408), (17408, 5120), (300, 640), (6144, 5120)]
+    devs = []
+    for i, (N, K) in enumerate(shapes):
+        T, S = gen_matrix(131, 10 + i, N, K)
+        devs.append((Dev(bgg, torch, fmt, T, S), T, S))
+    ws = bgg.workspace(max(bgg.bgg_gemv_workspace_size(d.desc, 16) for d, _, _ in devs))
+    for M in (1, 16, 3, 1, 2):
+        for d, T, S in devs:
+            x = synth.activations_f16(131, 20 + M, M, d.K)
+            y = d.gemv(x, ws=ws)
+            rows = np.arange(0, d.N, 97)
+            ref = oracle.matvec(T[rows], S[rows], oracle.rotate(x))
+            assert np.all(relerr(y[:, rows], ref) <= TOL), f"M={M} {d.N}x{d.K}"
+
+
 # ---------------------------------------------------------------------------
 # prompt GEMM
 # ---------------------------------------------------------------------------
