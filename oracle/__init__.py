@@ -10,9 +10,13 @@ rows).  What each function follows on the source pages is stated in oracle.c:
 * ``sylvester(n)``       explicit Sylvester Hadamard matrix, entries +-1;
 * ``rotate(x)``          x' = blockdiag(H_128/sqrt(128)) x, dense mat-vecs, fp64;
 * ``pack / unpack``      canonical PQ2_0 (2-bit slot, code t+1) and PTQ1_0
-                         (5 trits per byte, little-endian base 3 of t+1);
-* ``format_bytes``       bytes of a packed matrix incl. one fp16 per 128;
-* ``matvec(T, S, xr)``   y = sum_k S[n][k/128] T[n][k] xr[m][k] in fp64;
+                         (5 trits per byte, little-endian base 3 of t+1), and
+                         the sister formats Q1_0 (one sign bit per weight) and
+                         Q2_0_g64 (the PQ2_0 stream);
+* ``scale_group(fmt)``   weights per fp16 scale: 128, or 64 for Q2_0_g64;
+* ``format_bytes``       bytes of a packed matrix incl. its fp16 scales;
+* ``matvec(T, S, xr)``   y = sum_k S[n][k/group] T[n][k] xr[m][k] in fp64
+                         (group = K / scales per row);
 * ``linear(...)``        unpack + rotate + matvec from the stored form.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
@@ -28,8 +32,10 @@ import numpy as np
 
 PQ2_0 = 1
 PTQ1_0 = 2
+Q1_0 = 3
+Q2_0_G64 = 4
 BLOCK = 128
-FORMATS = {"PQ2_0": PQ2_0, "PTQ1_0": PTQ1_0}
+FORMATS = {"PQ2_0": PQ2_0, "PTQ1_0": PTQ1_0, "Q1_0": Q1_0, "Q2_0_G64": Q2_0_G64}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -57,6 +63,10 @@ def configure(lib):
     lib.oracle_row_bytes.restype = i64
     lib.oracle_format_bytes.argtypes = [ci, i64, i64]
     lib.oracle_format_bytes.restype = i64
+    lib.oracle_scale_group.argtypes = [ci]
+    lib.oracle_scale_group.restype = i64
+    lib.oracle_matvec_group.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp]
+    lib.oracle_matvec_group.restype = ci
     lib.oracle_pack.argtypes = [ci, vp, i64, i64, vp]
     lib.oracle_unpack.argtypes = [ci, vp, i64, i64, vp]
     lib.oracle_matvec.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -139,6 +149,10 @@ def row_bytes(fmt, K: int) -> int:
     return int(_load().oracle_row_bytes(_fmt(fmt), K))
 
 
+def scale_group(fmt) -> int:
+    return int(_load().oracle_scale_group(_fmt(fmt)))
+
+
 def format_bytes(fmt, N: int, K: int) -> int:
     return int(_load().oracle_format_bytes(_fmt(fmt), N, K))
 
@@ -165,8 +179,9 @@ def unpack(fmt, packed, K: int) -> np.ndarray:
 
 
 def matvec(T, S, xr) -> np.ndarray:
-    """fp64 [M, N] = products of ternary rows T [N, K] with scales S (fp16
-    [N, K/128]) and rotated activations xr (fp64 [M, K])."""
+    """fp64 [M, N] = products of weight rows T [N, K] with scales S (fp16
+    [N, K/group]: K/128 scales per row, or K/64) and rotated activations xr
+    (fp64 [M, K])."""
     T = np.ascontiguousarray(T, dtype=np.int8)
     Sb = _f16bits(S)
     xr = np.ascontiguousarray(xr, dtype=np.float64)
@@ -174,10 +189,16 @@ def matvec(T, S, xr) -> np.ndarray:
         xr = xr[None, :]
     N, K = T.shape
     M = xr.shape[0]
-    assert Sb.shape == (N, K // BLOCK) and xr.shape[1] == K
+    assert Sb.shape[0] == N and Sb.shape[1] >= 1 and K % Sb.shape[1] == 0 and xr.shape[1] == K
+    group = K // Sb.shape[1]
     y = np.empty((M, N), dtype=np.float64)
-    _check(_load().oracle_matvec(T.ctypes.data, Sb.ctypes.data, xr.ctypes.data, M, N, K,
-                                 y.ctypes.data), "matvec")
+    if group == BLOCK:
+        rc = _load().oracle_matvec(T.ctypes.data, Sb.ctypes.data, xr.ctypes.data, M, N, K,
+                                   y.ctypes.data)
+    else:
+        rc = _load().oracle_matvec_group(T.ctypes.data, Sb.ctypes.data, xr.ctypes.data, M, N, K,
+                                         group, y.ctypes.data)
+    _check(rc, "matvec")
     return y
 
 
@@ -191,7 +212,7 @@ def linear(fmt, packed, S, x, rotate: bool = True) -> np.ndarray:
         xb = xb[None, :]
     N = packed.shape[0]
     M, K = xb.shape
-    assert packed.shape[1] == row_bytes(fmt, K) and Sb.shape == (N, K // BLOCK)
+    assert packed.shape[1] == row_bytes(fmt, K) and Sb.shape == (N, K // scale_group(fmt))
     y = np.empty((M, N), dtype=np.float64)
     _check(_load().oracle_linear(_fmt(fmt), packed.ctypes.data, Sb.ctypes.data, xb.ctypes.data,
                                  M, N, K, 1 if rotate else 0, y.ctypes.data), "linear")

@@ -30,6 +30,14 @@
  *   - PTQ1_0: row byte j = sum_i (t_{5j+i} + 1) * 3^i, a continuous stream of
  *     ceil(K/5) bytes per row, trits past K padded with t = 0; bytes 243..255
  *     are invalid.
+ *   - the sister formats the third page names by their effective bits per
+ *     weight only ([C] opening summary: 1-bit weights {-1, +1} with an FP16
+ *     group scale at about 1.125 bits per weight; section 后端支持现状: a
+ *     ternary "Q2_0_g64" file form).  Read here as Q1_0: bit i of row byte j
+ *     is weight 8j+i, 1 for +1 and 0 for -1, one FP16 scale per 128 weights
+ *     (1 + 16/128 = 1.125 bits); Q2_0_g64: the PQ2_0 row stream with one
+ *     FP16 scale per 64 weights (2 + 16/64 = 2.25 bits).  The activation
+ *     transform keeps its 128-blocks for every format.
  *
  * All floating point is fp64; fp16 inputs are decoded exactly.
  */
@@ -40,6 +48,8 @@
 
 #define ORACLE_PQ2_0 1
 #define ORACLE_PTQ1_0 2
+#define ORACLE_Q1_0 3
+#define ORACLE_Q2_0_G64 4
 #define BLOCK 128
 
 /* IEEE 754 binary16 -> double: sign, 5-bit exponent (bias 15), 10-bit
@@ -99,32 +109,49 @@ int oracle_rotate(const uint16_t* x, int64_t M, int64_t K, double* xr) {
 
 /* Bytes of one packed row (canonical layout). [A] packing, [C] */
 int64_t oracle_row_bytes(int fmt, int64_t K) {
-  if (fmt == ORACLE_PQ2_0) return (K + 3) / 4;
+  if (fmt == ORACLE_PQ2_0 || fmt == ORACLE_Q2_0_G64) return (K + 3) / 4;
   if (fmt == ORACLE_PTQ1_0) return (K + 4) / 5;
+  if (fmt == ORACLE_Q1_0) return (K + 7) / 8;
   return -1;
 }
 
-/* Bytes of a whole N x K matrix: packed trits plus one fp16 per 128. [A] */
+/* Weights that share one fp16 scale: 128 [A method], 64 for Q2_0_g64. */
+int64_t oracle_scale_group(int fmt) {
+  if (fmt == ORACLE_PQ2_0 || fmt == ORACLE_PTQ1_0 || fmt == ORACLE_Q1_0) return BLOCK;
+  if (fmt == ORACLE_Q2_0_G64) return 64;
+  return -1;
+}
+
+/* Bytes of a whole N x K matrix: packed weights plus one fp16 per scale
+ * group. [A] */
 int64_t oracle_format_bytes(int fmt, int64_t N, int64_t K) {
-  int64_t rb = oracle_row_bytes(fmt, K);
-  if (rb < 0 || K % BLOCK) return -1;
-  return N * rb + N * (K / BLOCK) * 2;
+  int64_t rb = oracle_row_bytes(fmt, K), group = oracle_scale_group(fmt);
+  if (rb < 0 || group < 0 || K % BLOCK) return -1;
+  return N * rb + N * (K / group) * 2;
 }
 
 /* Canonical packing of trits T[N][K] into out[N][row_bytes]. Returns 0, or
- * -1 for a bad format, -3 for a value outside {-1,0,1}. */
+ * -1 for a bad format, -3 for a value outside {-1,0,1} (outside {-1,1} for
+ * Q1_0). */
 int oracle_pack(int fmt, const int8_t* T, int64_t N, int64_t K, uint8_t* out) {
   int64_t rb = oracle_row_bytes(fmt, K);
   if (rb < 0) return -1;
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t j = 0; j < rb; ++j) {
       unsigned byte = 0;
-      if (fmt == ORACLE_PQ2_0) {
+      if (fmt == ORACLE_PQ2_0 || fmt == ORACLE_Q2_0_G64) {
         for (int i = 0; i < 4; ++i) {
           int64_t k = 4 * j + i;
           int t = k < K ? T[n * K + k] : 0;
           if (t < -1 || t > 1) return -3;
           byte |= (unsigned)(t + 1) << (2 * i);
+        }
+      } else if (fmt == ORACLE_Q1_0) {
+        for (int i = 0; i < 8; ++i) {
+          int64_t k = 8 * j + i;
+          int t = k < K ? T[n * K + k] : -1;
+          if (t != -1 && t != 1) return -3;
+          if (t == 1) byte |= 1u << i;
         }
       } else {
         unsigned pow3 = 1;
@@ -150,7 +177,12 @@ int oracle_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, int8_t* 
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t j = 0; j < rb; ++j) {
       unsigned byte = packed[n * rb + j];
-      if (fmt == ORACLE_PQ2_0) {
+      if (fmt == ORACLE_Q1_0) {
+        for (int i = 0; i < 8; ++i) {
+          int64_t k = 8 * j + i;
+          if (k < K) T[n * K + k] = (int8_t)(((byte >> i) & 1u) ? 1 : -1);
+        }
+      } else if (fmt == ORACLE_PQ2_0 || fmt == ORACLE_Q2_0_G64) {
         for (int i = 0; i < 4; ++i) {
           unsigned code = (byte >> (2 * i)) & 3u;
           if (code == 3) return -4;
@@ -171,22 +203,30 @@ int oracle_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, int8_t* 
   return 0;
 }
 
-/* y[m][n] = sum_k S[n][k/128] * T[n][k] * xr[m][k] in fp64; S is fp16.
- * xr holds activations already in rotated coordinates. [A] */
-int oracle_matvec(const int8_t* T, const uint16_t* S, const double* xr, int64_t M, int64_t N,
-                  int64_t K, double* y) {
-  if (K % BLOCK) return -1;
-  const int64_t G = K / BLOCK;
+/* y[m][n] = sum_k S[n][k/group] * T[n][k] * xr[m][k] in fp64; S is fp16
+ * with K/group scales per row.  xr holds activations already in rotated
+ * coordinates. [A] */
+int oracle_matvec_group(const int8_t* T, const uint16_t* S, const double* xr, int64_t M,
+                        int64_t N, int64_t K, int64_t group, double* y) {
+  if (group < 1 || K % group) return -1;
+  const int64_t G = K / group;
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t m = 0; m < M; ++m) {
       double acc = 0.0;
       for (int64_t k = 0; k < K; ++k)
-        acc += oracle_f16_to_f64(S[n * G + k / BLOCK]) * (double)T[n * K + k] * xr[m * K + k];
+        acc += oracle_f16_to_f64(S[n * G + k / group]) * (double)T[n * K + k] * xr[m * K + k];
       y[m * N + n] = acc;
     }
   }
   return 0;
+}
+
+/* The same with one scale per 128 weights [A method paragraph]. */
+int oracle_matvec(const int8_t* T, const uint16_t* S, const double* xr, int64_t M, int64_t N,
+                  int64_t K, double* y) {
+  if (K % BLOCK) return -1;
+  return oracle_matvec_group(T, S, xr, M, N, K, BLOCK, y);
 }
 
 /* The whole layer from the stored form: unpack the canonical bytes, rotate
@@ -205,7 +245,7 @@ int oracle_linear(int fmt, const uint8_t* packed, const uint16_t* S, const uint1
     else
       for (int64_t i = 0; i < M * K; ++i) xr[i] = oracle_f16_to_f64(x[i]);
   }
-  if (!rc) rc = oracle_matvec(T, S, xr, M, N, K, y);
+  if (!rc) rc = oracle_matvec_group(T, S, xr, M, N, K, oracle_scale_group(fmt), y);
   free(T);
   free(xr);
   return rc;

@@ -278,6 +278,75 @@ def pin_sylvester_row_closed_form():
             assert abs(y[0, n] - want) <= 1e-12 * (1 + abs(want))
 
 
+# --------------------------------------------------------------------------
+# sister formats: Q1_0 (one sign bit per weight, a scale per 128) and
+# Q2_0_g64 (the PQ2_0 stream, a scale per 64)
+# --------------------------------------------------------------------------
+def _rand_signs(n, k):
+    return RNG.choice(np.array([-1, 1], np.int8), size=(n, k))
+
+
+def pin_q1_exhaustive():
+    vals = np.array(np.meshgrid(*([[-1, 1]] * 8), indexing="ij")).reshape(8, -1).T.astype(np.int8)
+    P = oracle.pack("Q1_0", vals)              # one byte per row of 8 signs
+    assert P.shape == (256, 1)
+    assert sorted(P[:, 0].tolist()) == list(range(256))   # a bijection onto 0..255
+    assert np.array_equal(oracle.unpack("Q1_0", P, 8), vals)
+    assert oracle.pack("Q1_0", np.ones((1, 8), np.int8))[0, 0] == 0xFF
+    assert oracle.pack("Q1_0", -np.ones((1, 8), np.int8))[0, 0] == 0x00
+    for i in range(8):                         # weight i is bit i, 1 for +1
+        t = -np.ones((1, 8), np.int8)
+        t[0, i] = 1
+        assert oracle.pack("Q1_0", t)[0, 0] == 1 << i
+    with pytest.raises(oracle.OracleError):    # no zero weight in a 1-bit format
+        oracle.pack("Q1_0", np.zeros((1, 8), np.int8))
+
+
+def pin_sister_formats_sizes_and_streams():
+    for K in (128, 5120, 17408):
+        # 1 + 16/128: the effective bits per weight printed for 1-bit Bonsai
+        assert oracle.bits_per_weight("Q1_0", 64, K) == GOLDEN["one_bit_bits_per_weight"]["value"]
+        assert oracle.bits_per_weight("Q2_0_G64", 64, K) == 2.0 + 16.0 / 64.0
+    assert oracle.scale_group("Q1_0") == 128 and oracle.scale_group("Q2_0_G64") == 64
+    assert oracle.scale_group("PQ2_0") == GOLDEN["group"]["value"]
+    T = _rand_trits(4, 640)
+    assert np.array_equal(oracle.pack("Q2_0_G64", T), oracle.pack("PQ2_0", T))
+    assert np.array_equal(oracle.unpack("Q2_0_G64", oracle.pack("PQ2_0", T), 640), T)
+    for K in (1, 7, 8, 9, 129, 640):
+        T = _rand_signs(3, K)
+        P = oracle.pack("Q1_0", T)
+        assert P.shape[1] == math.ceil(K / 8)
+        assert np.array_equal(oracle.unpack("Q1_0", P, K), T)
+
+
+def pin_matvec_group64():
+    M, N, K = 2, 3, 256
+    T = _rand_trits(N, K)
+    S = RNG.uniform(0.005, 0.05, size=(N, K // 64)).astype(np.float16)
+    xr = RNG.standard_normal((M, K))
+    y = oracle.matvec(T, S, xr)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(float(S[n, k // 64]) * int(T[n, k]) * xr[m, k] for k in range(K))
+            assert abs(y[m, n] - acc) <= 1e-12 * (1 + abs(acc))
+    for k in (0, 63, 64, 127, 128, 255):       # a basis vector picks its 64-group's scale
+        e = np.zeros((1, K))
+        e[0, k] = 1.0
+        assert np.array_equal(oracle.matvec(T, S, e)[0], S[:, k // 64].astype(np.float64) * T[:, k])
+
+
+def pin_linear_sister_formats():
+    for fmt, group in (("Q1_0", 128), ("Q2_0_G64", 64)):
+        for (M, N, K) in ((1, 5, 128), (3, 7, 640)):
+            T = _rand_signs(N, K) if fmt == "Q1_0" else _rand_trits(N, K)
+            S = RNG.uniform(0.005, 0.05, size=(N, K // group)).astype(np.float16)
+            x = _rand_f16((M, K))
+            Wst = S.astype(np.float64).repeat(group, axis=1) * T
+            want = x.astype(np.float64) @ (Wst @ _hhat_blockdiag(K)).T
+            got = oracle.linear(fmt, oracle.pack(fmt, T), S, x)
+            assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -294,9 +363,13 @@ MUTANTS = {
     "rotate_no_norm": ("xr[m * K + b * BLOCK + r] = acc * norm;", "xr[m * K + b * BLOCK + r] = acc;"),
     "rotate_block_offset": ("blk[i] = oracle_f16_to_f64(x[m * K + b * BLOCK + i]);",
                             "blk[i] = oracle_f16_to_f64(x[m * K + b + i]);"),
-    "scale_index": ("S[n * G + k / BLOCK]", "S[n * G + k % G]"),
-    "dropped_scale": ("acc += oracle_f16_to_f64(S[n * G + k / BLOCK]) * (double)T[n * K + k] * xr[m * K + k];",
+    "scale_index": ("S[n * G + k / group]", "S[n * G + k % G]"),
+    "dropped_scale": ("acc += oracle_f16_to_f64(S[n * G + k / group]) * (double)T[n * K + k] * xr[m * K + k];",
                       "acc += (double)T[n * K + k] * xr[m * K + k];"),
+    "q1_bit_order": ("if (t == 1) byte |= 1u << i;", "if (t == 1) byte |= 0x80u >> i;"),
+    "q1_sign": ("T[n * K + k] = (int8_t)(((byte >> i) & 1u) ? 1 : -1);",
+                "T[n * K + k] = (int8_t)(((byte >> i) & 1u) ? -1 : 1);"),
+    "group64_scale": ("if (fmt == ORACLE_Q2_0_G64) return 64;", "if (fmt == ORACLE_Q2_0_G64) return 128;"),
     "pq2_code_sign": ("T[n * K + k] = (int8_t)((int)code - 1);", "T[n * K + k] = (int8_t)(1 - (int)code);"),
     "pq2_slot_shift": ("byte |= (unsigned)(t + 1) << (2 * i);", "byte |= (unsigned)(t + 1) << i;"),
     "ptq1_digit_order": ("int64_t k = 5 * j + i;\n          if (k < K) T[n * K + k] = (int8_t)((int)digit - 1);",
