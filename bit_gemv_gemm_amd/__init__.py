@@ -31,7 +31,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 BGG_FMT_PQ2_0 = 1
 BGG_FMT_PTQ1_0 = 2
-FORMATS = {"PQ2_0": BGG_FMT_PQ2_0, "PTQ1_0": BGG_FMT_PTQ1_0}
+BGG_FMT_Q1_0 = 3
+BGG_FMT_Q2_0_G64 = 4
+FORMATS = {"PQ2_0": BGG_FMT_PQ2_0, "PTQ1_0": BGG_FMT_PTQ1_0, "Q1_0": BGG_FMT_Q1_0,
+           "Q2_0_G64": BGG_FMT_Q2_0_G64}
 BGG_ROTATE_INPUT = 1
 BGG_GROUP = 128
 BGG_ROW_TILE = 64
@@ -50,7 +53,8 @@ class bgg_weights_desc(ctypes.Structure):
                 ("row_tiles", ctypes.c_int64), ("row_bytes", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("trit_bytes", ctypes.c_uint64),
                 ("scale_offset", ctypes.c_uint64), ("scale_bytes", ctypes.c_uint64),
-                ("total_bytes", ctypes.c_uint64), ("format_bytes", ctypes.c_uint64)]
+                ("total_bytes", ctypes.c_uint64), ("format_bytes", ctypes.c_uint64),
+                ("scale_group", ctypes.c_int64), ("scales", ctypes.c_int64)]
 
     def __repr__(self):
         return "bgg_weights_desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -143,7 +147,7 @@ def bgg_describe(fmt, N: int, K: int) -> bgg_weights_desc:
 def bgg_pack_weights(desc: bgg_weights_desc, trits, scales) -> np.ndarray:
     """Host int8 trits [N][K] and fp16 scales [N][K/128] -> packed bytes (host)."""
     t, tp = _host_ptr(trits, np.int8, (desc.N, desc.K))
-    s, sp = _host_ptr(scales, np.uint16, (desc.N, desc.groups))
+    s, sp = _host_ptr(scales, np.uint16, (desc.N, desc.scales))
     out = np.empty(desc.total_bytes, dtype=np.uint8)
     _ok(_lib.bgg_pack_weights(ctypes.byref(desc), tp, sp, out.ctypes.data), "bgg_pack_weights")
     return out
@@ -151,7 +155,7 @@ def bgg_pack_weights(desc: bgg_weights_desc, trits, scales) -> np.ndarray:
 
 def bgg_repack_canonical(desc: bgg_weights_desc, canonical, scales) -> np.ndarray:
     c, cp = _host_ptr(canonical, np.uint8, (desc.N, desc.row_bytes))
-    s, sp = _host_ptr(scales, np.uint16, (desc.N, desc.groups))
+    s, sp = _host_ptr(scales, np.uint16, (desc.N, desc.scales))
     out = np.empty(desc.total_bytes, dtype=np.uint8)
     _ok(_lib.bgg_repack_canonical(ctypes.byref(desc), cp, sp, out.ctypes.data), "bgg_repack_canonical")
     return out
@@ -197,7 +201,7 @@ def bgg_unpack_weights(desc, packed_dev, trits_dev, scales_dev, stream=None) -> 
     _ok(_lib.bgg_unpack_weights(
         ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
         _dev_ptr(trits_dev, desc.N * desc.K, "trits"),
-        _dev_ptr(scales_dev, desc.N * desc.groups * 2, "scales"), _stream(stream)),
+        _dev_ptr(scales_dev, desc.N * desc.scales * 2, "scales"), _stream(stream)),
         "bgg_unpack_weights")
 
 

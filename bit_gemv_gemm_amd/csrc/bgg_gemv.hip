@@ -863,13 +863,91 @@ __device__ __forceinline__ void mx_group(const i32x8 (&A)[kMxDigits], uint32_t s
     for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s[rb], ag[rb][e], acc[rb][e]);
 }
 
-template <int BPS, int W>
-__global__ void __launch_bounds__(64 * W)
-    k_gemv_pq2_mx(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
-                  int64_t N, int Sg, int Mreal, const uint4* __restrict__ xa,
-                  const uint32_t* __restrict__ xs, const float* __restrict__ xc,
-                  unsigned long long* __restrict__ sums, int64_t tile0, int64_t ntl, int64_t nta,
-                  int sgb, int light_last, uint16_t* __restrict__ y) {
+// Q1_0: one 32-bit word of sign bits (K 32 kg .. +31 of the group, bit i =
+// K 32 kg + i) -> four B words of fp4 nibbles in natural K order: nibble n
+// of word j = bit 8 j + n, as the nibble value 0 or 1 (e2m1 0 or 0.5; B's
+// block scale 4 makes it 0 or 2, so 2 b - 1 = the weight after the -sum q
+// start).  Each byte's bits are moved to the nibbles' low bits in three
+// shift-or-mask steps.
+__device__ __forceinline__ uint32_t q1_spread8(uint32_t b) {
+  uint32_t x = (b | (b << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+__device__ __forceinline__ void mx_group_q1(const i32x8 (&A)[kMxDigits], uint32_t sa, f32x4 c0,
+                                            const uint32_t (&wv)[4], const float (&s)[4],
+                                            f32x4 (&acc)[4]) {
+  i32x8 B[4];
+  f32x4 ag[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const uint32_t w = wv[rb];
+    B[rb] = i32x8{(int)q1_spread8(w & 0xFFu), (int)q1_spread8((w >> 8) & 0xFFu),
+                  (int)q1_spread8((w >> 16) & 0xFFu), (int)q1_spread8(w >> 24), 0, 0, 0, 0};
+    ag[rb] = c0;
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B[rb], ag[rb], 0, 4, 0, (int)sa, 0, 129);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B[rb], ag[rb], 0, 4, 1, (int)sa, 0, 129);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B[rb], ag[rb], 0, 4, 2, (int)sa, 0, 129);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s[rb], ag[rb][e], acc[rb][e]);
+}
+// Q2_0_g64: the PQ2_0 operands, but a scale per 64 weights: lane groups 0-1
+// hold the group's first 64 weights (chunk 2 g), 2-3 the second; each half
+// is summed by its own MFMAs (B zero in the other half's lanes) from its
+// own start value -2^(e-14) sum q over the half, and takes its own scale.
+__device__ __forceinline__ void mx_group_g64(const i32x8 (&A)[kMxDigits], uint32_t sa,
+                                             const f32x4 (&c0)[2], const u32x2 (&wv)[4],
+                                             const float (&s)[2][4], bool upper, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool mine = (h == 1) == upper;
+    i32x8 B[4];
+    f32x4 ag[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      // (the other half's lanes feed nibble 0, the value 0)
+      const uint32_t lo = mine ? wv[rb].x : 0u, hi = mine ? wv[rb].y : 0u;
+      B[rb] = i32x8{(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                    (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+      ag[rb] = c0[h];
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B[rb], ag[rb], 0, 4, 0, (int)sa, 0, 128);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B[rb], ag[rb], 0, 4, 1, (int)sa, 0, 128);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      ag[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B[rb], ag[rb], 0, 4, 2, (int)sa, 0, 128);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[rb][e] = fmaf(s[h][rb], ag[rb][e], acc[rb][e]);
+  }
+}
+
+template <int FMT, int BPS, int W>
+__device__ __forceinline__ void mx_gemv_body(const uint8_t* __restrict__ packed,
+                                             uint64_t scale_offset, int64_t C, int64_t G,
+                                             int64_t N, int Sg, int Mreal,
+                                             const uint4* __restrict__ xa,
+                                             const uint32_t* __restrict__ xs,
+                                             const float* __restrict__ xc,
+                                             const float* __restrict__ xh,
+                                             unsigned long long* __restrict__ sums, int64_t tile0,
+                                             int64_t ntl, int64_t nta, int sgb, int light_last,
+                                             uint16_t* __restrict__ y) {
+  constexpr bool kQ1 = FMT == BGG_FMT_Q1_0, kG64 = FMT == BGG_FMT_Q2_0_G64;
   __shared__ float red[W][kMmaSlots * kMmaRedStride];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -884,14 +962,20 @@ __global__ void __launch_bounds__(64 * W)
   for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (gbeg < G) {
-    // K 32 kg .. 32 kg + 31 of group g, row r: 8 bytes at chunk 2 g + kg / 2,
-    // half kg % 2 -- uint2 index ((tile C + c) 64 + r) 2 + half
+    // PQ2_0 / Q2_0_g64: K 32 kg .. 32 kg + 31 of group g, row r: 8 bytes at
+    // chunk 2 g + kg / 2, half kg % 2 -- uint2 index ((tile C + c) 64 + r) 2
+    // + half.  Q1_0: the group is chunk g; word kg -- dword index
+    // ((tile C + g) 64 + r) 4 + kg.
     const u32x2* wsrc =
         reinterpret_cast<const u32x2*>(packed) + ((tile * C + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
+    const uint32_t* wsrc1 = reinterpret_cast<const uint32_t*>(packed) + ((tile * C) * kTile + col) * 4 + kg;
+    // scales per row: G (one per group), or 2 G for Q2_0_g64
+    constexpr int kSc = kG64 ? 2 : 1;
     const uint16_t* ssrc =
-        reinterpret_cast<const uint16_t*>(packed + scale_offset) + tile * G * kTile + col;
+        reinterpret_cast<const uint16_t*>(packed + scale_offset) + tile * (kSc * G) * kTile + col;
     // The slice runs in batches of NB groups (all BPS groups, or two halves
-    // of eight: the registers hold one batch).  A batch's loads are issued
+    // of eight; Q2_0_g64, with two start values and two scales per group
+    // and row, batches of two: the registers hold one batch).  A batch's loads are issued
     // first, group by group (A digits, scale word, start values, weights,
     // weight scales), with no branch between them and their use: loads
     // complete in issue order, so group i waits only for its own loads and
@@ -899,7 +983,7 @@ __global__ void __launch_bounds__(64 * W)
     // and gets a zero scale.  Lanes of token slots past M load no A bytes
     // and multiply zeros (their rows are dropped), so a few tokens cost few
     // A bytes.
-    constexpr int NB = BPS <= 5 ? BPS : BPS / 2;
+    constexpr int NB = kG64 ? (BPS >= 8 ? 2 : BPS) : BPS <= 5 ? BPS : BPS / 2;
     static_assert(BPS % NB == 0, "whole batches");
     const bool aload = col < Mreal;
     const int aslot = aload ? col : Mreal - 1;
@@ -911,9 +995,10 @@ __global__ void __launch_bounds__(64 * W)
       __builtin_amdgcn_sched_barrier(0);
       uint4 a[NB][kMxDigits][2];
       uint32_t sa[NB];
-      f32x4 c0[NB];
+      f32x4 c0[NB][kSc];
       u32x2 w[NB][4];
-      uint16_t sc[NB][4];
+      uint32_t w1[NB][4];
+      uint16_t sc[NB][kSc][4];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int64_t g = gbeg + b0 + i < G ? gbeg + b0 + i : G - 1;
@@ -923,11 +1008,21 @@ __global__ void __launch_bounds__(64 * W)
           a[i][k][1] = aload ? asrc[(g * kMxDigits + k) * 128 + 1] : make_uint4(0, 0, 0, 0);
         }
         sa[i] = xs[g * kMmaSlots + aslot];
-        c0[i] = *reinterpret_cast<const f32x4*>(xc + g * kMmaSlots + 4 * kg);
+        if constexpr (kG64) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            c0[i][h] = *reinterpret_cast<const f32x4*>(xh + (g * 2 + h) * kMmaSlots + 4 * kg);
+        } else {
+          c0[i][0] = *reinterpret_cast<const f32x4*>(xc + g * kMmaSlots + 4 * kg);
+        }
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          w[i][rb] = __builtin_nontemporal_load(wsrc + g * (4 * kTile) + rb * 32);
-          sc[i][rb] = ssrc[g * kTile + 16 * rb];
+          if constexpr (kQ1)
+            w1[i][rb] = __builtin_nontemporal_load(wsrc1 + g * (4 * kTile) + rb * 64);
+          else
+            w[i][rb] = __builtin_nontemporal_load(wsrc + g * (4 * kTile) + rb * 32);
+#pragma unroll
+          for (int h = 0; h < kSc; ++h) sc[i][h][rb] = ssrc[(g * kSc + h) * kTile + 16 * rb];
         }
       }
       // keep the scheduler from sinking the loads towards their uses
@@ -942,10 +1037,22 @@ __global__ void __launch_bounds__(64 * W)
                        (int)a[i][k][1].z, (int)a[i][k][1].w};
         }
         const bool live = gbeg + b0 + i < G;
-        float s[4];
+        if constexpr (kG64) {
+          float s2[2][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) s[rb] = live ? h2f(sc[i][rb]) : 0.0f;
-        mx_group(A, sa[i], c0[i], w[i], s, acc);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) s2[h][rb] = live ? h2f(sc[i][h][rb]) : 0.0f;
+          mx_group_g64(A, sa[i], c0[i], w[i], s2, kg >= 2, acc);
+        } else {
+          float s[4];
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) s[rb] = live ? h2f(sc[i][0][rb]) : 0.0f;
+          if constexpr (kQ1)
+            mx_group_q1(A, sa[i], c0[i][0], w1[i], s, acc);
+          else
+            mx_group(A, sa[i], c0[i][0], w[i], s, acc);
+        }
       }
     }
   }
@@ -978,6 +1085,30 @@ __global__ void __launch_bounds__(64 * W)
     }
   }
 }
+
+#define BGG_MX_PARAMS                                                                         \
+  const uint8_t *__restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G, int64_t N,  \
+      int Sg, int Mreal, const uint4 *__restrict__ xa, const uint32_t *__restrict__ xs,        \
+      const float *__restrict__ xc, const float *__restrict__ xh,                              \
+      unsigned long long *__restrict__ sums, int64_t tile0, int64_t ntl, int64_t nta, int sgb, \
+      int light_last, uint16_t *__restrict__ y
+#define BGG_MX_ARGS \
+  packed, scale_offset, C, G, N, Sg, Mreal, xa, xs, xc, xh, sums, tile0, ntl, nta, sgb, light_last, y
+// one kernel per format, so that a profiler names them apart
+template <int BPS, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_pq2_mx(BGG_MX_PARAMS) {
+  mx_gemv_body<BGG_FMT_PQ2_0, BPS, W>(BGG_MX_ARGS);
+}
+template <int BPS, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_q1_mx(BGG_MX_PARAMS) {
+  mx_gemv_body<BGG_FMT_Q1_0, BPS, W>(BGG_MX_ARGS);
+}
+template <int BPS, int W>
+__global__ void __launch_bounds__(64 * W) k_gemv_q2g64_mx(BGG_MX_PARAMS) {
+  mx_gemv_body<BGG_FMT_Q2_0_G64, BPS, W>(BGG_MX_ARGS);
+}
+#undef BGG_MX_PARAMS
+#undef BGG_MX_ARGS
 
 // ---------------------------------------------------------------------------
 // PTQ1_0 for several tokens on the matrix cores.  A wave takes one period
@@ -1154,15 +1285,19 @@ __global__ void __launch_bounds__(64 * W)
 // the same x', e and q as the encoding above; q's three base-32 digits as
 // e4m3 bytes in the A operand order (xa: per group and digit, 64 lanes x 32
 // bytes), the scale bytes 127 + e - 14 + 10 - 5 k of digit k (xs: one word
-// per group and slot) and -2^(e-14) sum q (xc).  Only the slots below M
-// rounded up to four are written (slots past M-1 repeat token M - 1): the
-// GEMV's lanes of slots past M load nothing, and their rows are dropped.
-// grid: (G, ceil(M / 4)) blocks of 64 threads, four slots of one group per
-// block, 16 lanes per slot.
+// per group and slot) and -2^(e-14) sum q (xc), and with xh the same over
+// each 64-weight half (xh[group][half][slot], for Q2_0_g64).  Only the
+// slots below M rounded up to four are written (slots past M-1 repeat token
+// M - 1): the GEMV's lanes of slots past M load nothing, and their rows are
+// dropped.  NATURAL: the B nibbles carry K in natural order (Q1_0), else in
+// the PQ2_0 word order (mx_pos_of_k).  grid: (G, ceil(M / 4)) blocks of 64
+// threads, four slots of one group per block, 16 lanes per slot.
 constexpr int kPrepMxSlots = 4;
+template <bool NATURAL>
 __global__ void __launch_bounds__(64)
     k_gemv_prep_mx(const uint16_t* __restrict__ x, int64_t K, int M, int rotate,
-                   uint32_t* __restrict__ xa, uint32_t* __restrict__ xs, float* __restrict__ xc) {
+                   uint32_t* __restrict__ xa, uint32_t* __restrict__ xs, float* __restrict__ xc,
+                   float* __restrict__ xh) {
   // the e4m3 bytes of every digit, slot and group position
   __shared__ uint8_t dig[kMxDigits][kPrepMxSlots][kGroup];
   const int64_t blk = blockIdx.x;
@@ -1205,6 +1340,10 @@ __global__ void __launch_bounds__(64)
   qsum += xor16_i<1>(qsum);
   qsum += xor16_i<2>(qsum);
   qsum += xor16_i<4>(qsum);
+  // lanes 0-7 (positions 0-63) and 8-15 (64-127) now hold their half's sum
+  if (xh && (l16 & 7) == 0)
+    xh[(blk * 2 + (l16 >> 3)) * kMmaSlots + t] =
+        amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
   qsum += xor16_i<8>(qsum);
   if (l16 == 0) {
     const int eb = amax > 0.0f ? e : 0;
@@ -1224,8 +1363,10 @@ __global__ void __launch_bounds__(64)
     const uint8_t* row = dig[k][tl];
     uint32_t word = 0;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      word |= (uint32_t)row[mx_pos_of_k(mx_k_of_a(ga, 4 * dd + bb))] << (8 * bb);
+    for (int bb = 0; bb < 4; ++bb) {
+      const int kk = mx_k_of_a(ga, 4 * dd + bb);
+      word |= (uint32_t)row[NATURAL ? kk : mx_pos_of_k(kk)] << (8 * bb);
+    }
     const int l = 16 * ga + (int)blockIdx.y * kPrepMxSlots + tl;
     xa[((blk * kMxDigits + k) * 64 + l) * 8 + dd] = word;
   }
@@ -1264,6 +1405,8 @@ struct GemvPlan {
 int64_t gemv_mma_min_tokens(int format) {
   static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 2);
   static const int64_t ptq1 = env_int("BGG_GEMV_PTQ1_MMA_MIN", 2);
+  // the sister formats have only the matrix-core kernels
+  if (format == BGG_FMT_Q1_0 || format == BGG_FMT_Q2_0_G64) return 1;
   const int64_t m = format == BGG_FMT_PQ2_0 ? pq2 : ptq1;
   return m < 1 ? 1 : m;
 }
@@ -1293,16 +1436,18 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   p.slots = gemv_m_slots(M);
   p.W = 8;
   p.mma = M >= gemv_mma_min_tokens(d->format);
-  if (d->format == BGG_FMT_PQ2_0) {
+  if (d->format != BGG_FMT_PTQ1_0) {
     p.gpad = p.G;
     p.units = p.G;
     p.frag_words_per_token = (d->K / 64) * kPqFragWords;
     // one workgroup per tile (no partial rows) when that still fills the
     // chip: the smallest groups-per-wave with all of K in 8 waves
+    // (Q2_0_g64 has no five-group slices: its batches hold two groups)
     const int64_t one_wg[] = {2, 4, 5, 8};
     p.per_slice = 0;
     for (int64_t b : one_wg)
-      if (ceil_div(p.units, b) <= p.W && p.NT * p.W >= min_single) {
+      if (ceil_div(p.units, b) <= p.W && p.NT * p.W >= min_single &&
+          !(b == 5 && d->format == BGG_FMT_Q2_0_G64)) {
         p.per_slice = b;
         break;
       }
@@ -1354,7 +1499,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   uint64_t frag_bytes = (uint64_t)p.slots * p.frag_words_per_token * 4;
   uint64_t meta_q_bytes = (uint64_t)p.slots * p.gpad * 4;
   frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
-  meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 8);
+  meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 16);
   p.off_sums = 0;
   p.off_frag = kSumBytes;
   uint64_t off = align256(p.off_frag + frag_bytes);
@@ -1376,11 +1521,18 @@ void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x
   int32_t* mq = reinterpret_cast<int32_t*>(ws + p.off_meta_q);
   float* mf = reinterpret_cast<float*>(ws + p.off_meta_f);
   if (p.mma) {
+    // [xs: G x 16 words][xc: G x 16][xh: G x 2 x 16 (Q2_0_g64)]
     uint32_t* xs = reinterpret_cast<uint32_t*>(ws + p.off_meta_q);
-    hipLaunchKernelGGL(k_gemv_prep_mx, dim3((unsigned)p.G, (unsigned)ceil_div(M, kPrepMxSlots)),
-                       dim3(64), 0, st, x, d->K, (int)M,
-                       rotate, reinterpret_cast<uint32_t*>(ws + p.off_frag), xs,
-                       reinterpret_cast<float*>(xs + p.G * kMmaSlots));
+    float* xc = reinterpret_cast<float*>(xs + p.G * kMmaSlots);
+    float* xh = d->format == BGG_FMT_Q2_0_G64 ? xc + p.G * kMmaSlots : nullptr;
+    uint32_t* xa = reinterpret_cast<uint32_t*>(ws + p.off_frag);
+    const dim3 grid((unsigned)p.G, (unsigned)ceil_div(M, kPrepMxSlots));
+    if (d->format == BGG_FMT_Q1_0)
+      hipLaunchKernelGGL(k_gemv_prep_mx<true>, grid, dim3(64), 0, st, x, d->K, (int)M, rotate, xa,
+                         xs, xc, xh);
+    else
+      hipLaunchKernelGGL(k_gemv_prep_mx<false>, grid, dim3(64), 0, st, x, d->K, (int)M, rotate,
+                         xa, xs, xc, xh);
     return;
   }
   const dim3 grid((unsigned)ceil_div(p.gpad, kPrepGroups), (unsigned)p.slots);
@@ -1459,6 +1611,7 @@ void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t
   const uint4* xa = reinterpret_cast<const uint4*>(ws + p.off_frag);
   const uint32_t* xs = reinterpret_cast<const uint32_t*>(ws + p.off_meta_q);
   const float* xc = reinterpret_cast<const float*>(xs + p.G * kMmaSlots);
+  const float* xh = d->format == BGG_FMT_Q2_0_G64 ? xc + p.G * kMmaSlots : nullptr;
   unsigned long long* sums = reinterpret_cast<unsigned long long*>(ws + p.off_sums);
   const int Sg = (int)p.Sg;
   const dim3 block(64 * 8);
@@ -1476,17 +1629,29 @@ void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t
                          light, y);
       continue;
     }
-#define BGG_MMA(BPS)                                                                           \
-  hipLaunchKernelGGL((k_gemv_pq2_mx<BPS, 8>), grid, block, 0, st, packed, d->scale_offset,    \
-                     d->chunks, p.G, d->N, Sg, Mreal, xa, xs, xc, sums, t0, ntl, nta, sgb,    \
-                     light, y)
-    switch (p.per_slice) {
-      case 8: BGG_MMA(8); break;
-      case 5: BGG_MMA(5); break;
-      case 4: BGG_MMA(4); break;
-      default: BGG_MMA(2); break;
+#define BGG_MMA_ONE(KERN, BPS)                                                                 \
+  hipLaunchKernelGGL((KERN<BPS, 8>), grid, block, 0, st, packed, d->scale_offset, d->chunks,    \
+                     p.G, d->N, Sg, Mreal, xa, xs, xc, xh, sums, t0, ntl, nta, sgb, light, y)
+#define BGG_MMA(KERN)                          \
+  switch (p.per_slice) {                       \
+    case 8: BGG_MMA_ONE(KERN, 8); break;       \
+    case 5: BGG_MMA_ONE(KERN, 5); break;       \
+    case 4: BGG_MMA_ONE(KERN, 4); break;       \
+    default: BGG_MMA_ONE(KERN, 2); break;      \
+  }
+    if (d->format == BGG_FMT_Q1_0) {
+      BGG_MMA(k_gemv_q1_mx);
+    } else if (d->format == BGG_FMT_Q2_0_G64) {
+      switch (p.per_slice) {  // (never 5)
+        case 8: BGG_MMA_ONE(k_gemv_q2g64_mx, 8); break;
+        case 4: BGG_MMA_ONE(k_gemv_q2g64_mx, 4); break;
+        default: BGG_MMA_ONE(k_gemv_q2g64_mx, 2); break;
+      }
+    } else {
+      BGG_MMA(k_gemv_pq2_mx);
     }
 #undef BGG_MMA
+#undef BGG_MMA_ONE
   }
 }
 
@@ -1541,7 +1706,10 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
   if (p.mma && d->format == BGG_FMT_PTQ1_0) {
     n = snprintf(out, cap, "k_gemv_ptq1_mx<8>");
   } else if (p.mma) {
-    n = snprintf(out, cap, "k_gemv_pq2_mx<%d, 8>", (int)p.per_slice);
+    const char* kn = d->format == BGG_FMT_Q1_0       ? "k_gemv_q1_mx"
+                     : d->format == BGG_FMT_Q2_0_G64 ? "k_gemv_q2g64_mx"
+                                                     : "k_gemv_pq2_mx";
+    n = snprintf(out, cap, "%s<%d, 8>", kn, (int)p.per_slice);
   } else if (d->format == BGG_FMT_PQ2_0) {
     n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8, %s>", mb, (int)p.per_slice, fused);
   } else {

@@ -4,7 +4,11 @@
 // Packings follow allhereai.com/news/1346 (packing paragraph: PTQ1_0 compact
 // trits, PQ2_0 one trit per 2-bit slot) and wmrh.cn/news/471187 (section
 // 关键机制: five trits per byte); the per-128 fp16 scale follows the method
-// paragraph of the first page.
+// paragraph of the first page.  The sister formats Q1_0 (1-bit, about 1.125
+// bits per weight: opening summary of the second page) and Q2_0_g64 (named
+// in its section 后端支持现状) are laid out as this library reads them: a
+// sign bit per weight with a scale per 128, and the PQ2_0 stream with a
+// scale per 64.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -59,15 +63,30 @@ static inline uint8_t pq2_byte(const int8_t* t, int64_t k0, int64_t K) {
   return (uint8_t)v;
 }
 
+// Eight signs (bit i = weight k0+i, 1 for +1); weights past K are -1.
+static inline uint8_t q1_byte(const int8_t* t, int64_t k0, int64_t K) {
+  unsigned v = 0;
+  for (int i = 0; i < 8; ++i)
+    if (k0 + i < K && t[k0 + i] == 1) v |= 1u << i;
+  return (uint8_t)v;
+}
+
 static inline bool f16_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
 
-static inline uint8_t zero_byte(int32_t fmt) { return fmt == BGG_FMT_PQ2_0 ? 0x55 : 121; }
+static inline bool pq2_stream(int32_t fmt) { return fmt == BGG_FMT_PQ2_0 || fmt == BGG_FMT_Q2_0_G64; }
+
+// The byte of padding rows and columns: zero trits, or all -1 (Q1_0 has no
+// zero weight; its padding rows have zero scales).
+static inline uint8_t zero_byte(int32_t fmt) {
+  return pq2_stream(fmt) ? 0x55 : fmt == BGG_FMT_PTQ1_0 ? 121 : 0x00;
+}
 
 extern "C" {
 
 bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* out) {
   if (!out) return fail(BGG_ERR_NULL, "bgg_describe: out is NULL");
-  if (format != BGG_FMT_PQ2_0 && format != BGG_FMT_PTQ1_0)
+  if (format != BGG_FMT_PQ2_0 && format != BGG_FMT_PTQ1_0 && format != BGG_FMT_Q1_0 &&
+      format != BGG_FMT_Q2_0_G64)
     return fail(BGG_ERR_FORMAT, "bgg_describe: unknown format %d", (int)format);
   if (N < 1 || K < BGG_GROUP || K % BGG_GROUP != 0 || N > (int64_t(1) << 31) ||
       K > (int64_t(1) << 28))
@@ -83,13 +102,15 @@ bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* 
   d.K = K;
   d.groups = K / BGG_GROUP;
   d.row_tiles = (N + BGG_ROW_TILE - 1) / BGG_ROW_TILE;
-  d.row_bytes = format == BGG_FMT_PQ2_0 ? (K + 3) / 4 : (K + 4) / 5;
+  d.row_bytes = pq2_stream(format) ? (K + 3) / 4 : format == BGG_FMT_PTQ1_0 ? (K + 4) / 5 : K / 8;
   d.chunks = (d.row_bytes + BGG_CHUNK - 1) / BGG_CHUNK;
   d.trit_bytes = (uint64_t)d.row_tiles * d.chunks * BGG_ROW_TILE * BGG_CHUNK;
   d.scale_offset = (d.trit_bytes + 255) & ~uint64_t(255);
-  d.scale_bytes = (uint64_t)d.row_tiles * d.groups * BGG_ROW_TILE * 2;
+  d.scale_group = format == BGG_FMT_Q2_0_G64 ? 64 : BGG_GROUP;
+  d.scales = K / d.scale_group;
+  d.scale_bytes = (uint64_t)d.row_tiles * d.scales * BGG_ROW_TILE * 2;
   d.total_bytes = d.scale_offset + d.scale_bytes + BGG_READ_SLACK;
-  d.format_bytes = (uint64_t)N * d.row_bytes + (uint64_t)N * d.groups * 2;
+  d.format_bytes = (uint64_t)N * d.row_bytes + (uint64_t)N * d.scales * 2;
   *out = d;
   clear_error();
   return BGG_OK;
@@ -102,7 +123,7 @@ bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* 
 static void place_rows(const bgg_weights_desc* d, uint8_t* dst,
                        void (*row_stream)(const void*, int64_t, uint8_t*), const void* ctx,
                        const uint16_t* scales) {
-  const int64_t C = d->chunks, G = d->groups;
+  const int64_t C = d->chunks, G = d->scales;
   const int64_t padded_row = C * BGG_CHUNK;
   const int64_t rows = d->row_tiles * BGG_ROW_TILE;
   uint16_t* sdst = reinterpret_cast<uint16_t*>(dst + d->scale_offset);
@@ -146,10 +167,12 @@ struct TritCtx {
 static void trit_row_stream(const void* p, int64_t r, uint8_t* out) {
   const TritCtx* c = static_cast<const TritCtx*>(p);
   const int8_t* t = c->trits + r * c->K;
-  if (c->fmt == BGG_FMT_PQ2_0)
+  if (pq2_stream(c->fmt))
     for (int64_t j = 0; j < c->row_bytes; ++j) out[j] = pq2_byte(t, 4 * j, c->K);
-  else
+  else if (c->fmt == BGG_FMT_PTQ1_0)
     for (int64_t j = 0; j < c->row_bytes; ++j) out[j] = ptq1_byte(t, 5 * j, c->K);
+  else
+    for (int64_t j = 0; j < c->row_bytes; ++j) out[j] = q1_byte(t, 8 * j, c->K);
 }
 
 struct CanonCtx {
@@ -167,10 +190,12 @@ bgg_status bgg_pack_weights(const bgg_weights_desc* d, const int8_t* trits,
   bgg_status st = check_desc(d);
   if (st) return st;
   if (!trits || !scales || !packed) return fail(BGG_ERR_NULL, "bgg_pack_weights: NULL buffer");
-  const int64_t NK = d->N * d->K, NG = d->N * d->groups;
+  const int64_t NK = d->N * d->K, NG = d->N * d->scales;
+  const int lo = -1, hi = 1;
+  const bool signs = d->format == BGG_FMT_Q1_0;  // {-1, +1} only
   for (int64_t i = 0; i < NK; ++i)
-    if (trits[i] < -1 || trits[i] > 1)
-      return fail(BGG_ERR_TRIT, "bgg_pack_weights: trit %d at row %lld col %lld", (int)trits[i],
+    if (trits[i] < lo || trits[i] > hi || (signs && trits[i] == 0))
+      return fail(BGG_ERR_TRIT, "bgg_pack_weights: weight %d at row %lld col %lld", (int)trits[i],
                   (long long)(i / d->K), (long long)(i % d->K));
   for (int64_t i = 0; i < NG; ++i)
     if (!f16_finite(scales[i]))
@@ -183,6 +208,7 @@ bgg_status bgg_pack_weights(const bgg_weights_desc* d, const int8_t* trits,
 
 static bool canonical_byte_ok(int32_t fmt, uint8_t b) {
   if (fmt == BGG_FMT_PTQ1_0) return b < 243;
+  if (fmt == BGG_FMT_Q1_0) return true;
   for (int i = 0; i < 4; ++i)
     if (((b >> (2 * i)) & 3) == 3) return false;
   return true;
@@ -194,7 +220,7 @@ bgg_status bgg_repack_canonical(const bgg_weights_desc* d, const uint8_t* canoni
   if (st) return st;
   if (!canonical || !scales || !packed)
     return fail(BGG_ERR_NULL, "bgg_repack_canonical: NULL buffer");
-  const int64_t nb = d->N * d->row_bytes, NG = d->N * d->groups;
+  const int64_t nb = d->N * d->row_bytes, NG = d->N * d->scales;
   for (int64_t i = 0; i < nb; ++i)
     if (!canonical_byte_ok(d->format, canonical[i]))
       return fail(BGG_ERR_PACKED_BYTE, "bgg_repack_canonical: invalid byte 0x%02x at row %lld",
@@ -213,7 +239,7 @@ bgg_status bgg_validate_packed(const bgg_weights_desc* d, const void* packed) {
   if (st) return st;
   if (!packed) return fail(BGG_ERR_NULL, "bgg_validate_packed: NULL buffer");
   const uint8_t* p = static_cast<const uint8_t*>(packed);
-  const int64_t C = d->chunks, G = d->groups, rows = d->row_tiles * BGG_ROW_TILE;
+  const int64_t C = d->chunks, G = d->scales, rows = d->row_tiles * BGG_ROW_TILE;
   const uint8_t zb = zero_byte(d->format);
   for (int64_t r = 0; r < rows; ++r) {
     const int64_t t = r / BGG_ROW_TILE, l = r % BGG_ROW_TILE;

@@ -1,6 +1,7 @@
-// Device unpack: packed device layout -> int8 trits [N][K] and fp16 scales
-// [N][K/128], through the same decoders the products use (PQ2_0 nibble
-// spreading, PTQ1_0 base-3 LUT in LDS).  For checking; not on the hot path.
+// Device unpack: packed device layout -> int8 weights [N][K] and fp16 scales
+// [N][K/scale_group], through the same decoders the products use (PQ2_0 and
+// Q2_0_g64 nibble spreading, PTQ1_0 base-3 LUT in LDS, Q1_0 bits).  For
+// checking; not on the hot path.
 //
 // Packings: allhereai.com/news/1346, packing paragraph (PQ2_0 one trit per
 // 2-bit slot, PTQ1_0 compact); wmrh.cn/news/471187, section 关键机制 (five
@@ -29,7 +30,13 @@ __global__ void __launch_bounds__(256)
     const uint4 ch = reinterpret_cast<const uint4*>(packed)[tc * kTile + l];
     const uint32_t cw[4] = {ch.x, ch.y, ch.z, ch.w};
     int8_t* out = trits + row * K;
-    if (FMT == BGG_FMT_PQ2_0) {
+    if (FMT == BGG_FMT_Q1_0) {
+#pragma unroll
+      for (int b = 0; b < 128; ++b) {
+        const int64_t k = c * 128 + b;
+        if (k < K) out[k] = (int8_t)(((cw[b >> 5] >> (b & 31)) & 1u) ? 1 : -1);
+      }
+    } else if (FMT == BGG_FMT_PQ2_0 || FMT == BGG_FMT_Q2_0_G64) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t E = pq2_even(cw[d]), O = pq2_odd(cw[d]);
@@ -75,13 +82,16 @@ extern "C" bgg_status bgg_unpack_weights(const bgg_weights_desc* d, const void* 
   if (!aligned16(packed_dev)) return fail(BGG_ERR_BUFFER, "bgg_unpack_weights: packed misaligned");
   const int64_t threads = d->row_tiles * d->chunks * kTile;
   const dim3 grid((unsigned)ceil_div(threads, 256));
-  if (d->format == BGG_FMT_PQ2_0)
-    hipLaunchKernelGGL(k_unpack<BGG_FMT_PQ2_0>, grid, dim3(256), 0, (hipStream_t)stream,
-                       (const uint8_t*)packed_dev, d->scale_offset, d->row_tiles, d->chunks,
-                       d->groups, d->N, d->K, trits_dev, scales_dev);
-  else
-    hipLaunchKernelGGL(k_unpack<BGG_FMT_PTQ1_0>, grid, dim3(256), 0, (hipStream_t)stream,
-                       (const uint8_t*)packed_dev, d->scale_offset, d->row_tiles, d->chunks,
-                       d->groups, d->N, d->K, trits_dev, scales_dev);
+#define BGG_UNPACK(F)                                                                       \
+  hipLaunchKernelGGL(k_unpack<F>, grid, dim3(256), 0, (hipStream_t)stream,                \
+                     (const uint8_t*)packed_dev, d->scale_offset, d->row_tiles, d->chunks, \
+                     d->scales, d->N, d->K, trits_dev, scales_dev)
+  switch (d->format) {
+    case BGG_FMT_PQ2_0: BGG_UNPACK(BGG_FMT_PQ2_0); break;
+    case BGG_FMT_PTQ1_0: BGG_UNPACK(BGG_FMT_PTQ1_0); break;
+    case BGG_FMT_Q1_0: BGG_UNPACK(BGG_FMT_Q1_0); break;
+    default: BGG_UNPACK(BGG_FMT_Q2_0_G64); break;
+  }
+#undef BGG_UNPACK
   return hip_check("bgg_unpack_weights");
 }

@@ -51,8 +51,14 @@ extern "C" {
  * on every call, so a buffer packed one way cannot be run the other way (the
  * silent-garbage hazard of [A runtime paragraph]). */
 typedef enum {
-  BGG_FMT_PQ2_0 = 1,  /* one trit per 2-bit slot: code t+1 in {0,1,2}; 2.125 bits/weight */
-  BGG_FMT_PTQ1_0 = 2  /* five trits per byte, base 3 of t+1; 8/5 + 16/128 = 1.725 bits/weight */
+  BGG_FMT_PQ2_0 = 1,   /* one trit per 2-bit slot: code t+1 in {0,1,2}; 2.125 bits/weight */
+  BGG_FMT_PTQ1_0 = 2,  /* five trits per byte, base 3 of t+1; 8/5 + 16/128 = 1.725 bits/weight */
+  /* Sister formats, named on [C] (opening summary: 1-bit weights {-1, +1}
+   * with an FP16 group scale at about 1.125 bits per weight; section
+   * 后端支持现状: a ternary "Q2_0_g64" file form); their layouts are this
+   * library's reading: */
+  BGG_FMT_Q1_0 = 3,    /* one sign bit per weight (1 = +1, 0 = -1); 1 + 16/128 = 1.125 bits/weight */
+  BGG_FMT_Q2_0_G64 = 4 /* the PQ2_0 row stream with one FP16 scale per 64; 2 + 16/64 = 2.25 */
 } bgg_format;
 
 typedef enum {
@@ -83,7 +89,7 @@ enum {
 #define BGG_READ_SLACK 8192 /* zero bytes after the scales of a packed buffer (see below) */
 
 #define BGG_DESC_MAGIC 0x57474742u /* "BGGW" */
-#define BGG_DESC_VERSION 2u
+#define BGG_DESC_VERSION 3u
 
 /*
  * Descriptor of a packed weight matrix W [N out][K in].  Host struct, filled
@@ -91,14 +97,16 @@ enum {
  *
  * Device layout of the packed buffer (total_bytes):
  *   trit region, at offset 0: rows in tiles of 64; the bytes of each row in
- *     the format's canonical row stream (PQ2_0: row byte j holds trits
- *     4j..4j+3, trit 4j+i in bits 2i..2i+1 as t+1; PTQ1_0: row byte j =
- *     sum_i (t_{5j+i}+1) 3^i, trits past K are 0), cut into 16-byte chunks.
+ *     the format's canonical row stream (PQ2_0 and Q2_0_G64: row byte j
+ *     holds trits 4j..4j+3, trit 4j+i in bits 2i..2i+1 as t+1; PTQ1_0: row
+ *     byte j = sum_i (t_{5j+i}+1) 3^i, trits past K are 0; Q1_0: bit i of
+ *     row byte j is weight 8j+i, 1 for +1), cut into 16-byte chunks.
  *     Chunk c of row 64*t + l sits at byte ((t*chunks + c)*64 + l)*16, so the
  *     64 rows of a tile read chunk c with one coalesced 1 KiB load.  Rows
  *     past N hold zero trits, bytes past the row stream hold zero trits.
- *   scale region, at scale_offset: fp16 scale of row 64*t + l, group g at
- *     byte scale_offset + ((t*groups + g)*64 + l)*2; rows past N hold 0.
+ *   scale region, at scale_offset: fp16 scale s (weights s*scale_group ..)
+ *     of row 64*t + l at byte scale_offset + ((t*scales + s)*64 + l)*2;
+ *     rows past N hold 0.
  *   slack, at scale_offset + scale_bytes: BGG_READ_SLACK zero bytes.  The
  *     kernels read whole work units without bounds checks, up to seven
  *     chunks past a tile's last chunk and four groups past its last scale;
@@ -112,15 +120,17 @@ typedef struct bgg_weights_desc {
   int32_t row_tile;      /* BGG_ROW_TILE */
   int64_t N;             /* output rows */
   int64_t K;             /* input columns, a multiple of 128 */
-  int64_t groups;        /* K / 128 */
+  int64_t groups;        /* K / 128: blocks of the activation transform */
   int64_t row_tiles;     /* ceil(N / 64) */
-  int64_t row_bytes;     /* canonical packed bytes per row: ceil(K/4) or ceil(K/5) */
+  int64_t row_bytes;     /* canonical packed bytes per row: ceil(K/4), ceil(K/5) or K/8 */
   int64_t chunks;        /* ceil(row_bytes / 16) */
   uint64_t trit_bytes;   /* row_tiles * chunks * 1024 */
   uint64_t scale_offset; /* trit_bytes rounded up to 256 */
-  uint64_t scale_bytes;  /* row_tiles * groups * 128 */
+  uint64_t scale_bytes;  /* row_tiles * scales * 128 */
   uint64_t total_bytes;  /* scale_offset + scale_bytes + BGG_READ_SLACK */
-  uint64_t format_bytes; /* N*row_bytes + N*groups*2: the format's own size, no padding */
+  uint64_t format_bytes; /* N*row_bytes + N*scales*2: the format's own size, no padding */
+  int64_t scale_group;   /* weights per fp16 scale: 128, or 64 for Q2_0_G64 */
+  int64_t scales;        /* scales per row: K / scale_group */
 } bgg_weights_desc;
 
 /* Fill *out for a format and shape.  Host only, no side effects.
@@ -129,8 +139,9 @@ bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* 
 
 /* Pack trits and scales into the device layout (a0 of the path: offline,
  * once per matrix) [A method and packing paragraphs; C].
- *   trits   host int8 [N][K], row-major, values in {-1,0,1} (rotated coordinates)
- *   scales  host fp16 bits [N][K/128], row-major
+ *   trits   host int8 [N][K], row-major, values in {-1,0,1} ({-1,1} for Q1_0),
+ *           rotated coordinates
+ *   scales  host fp16 bits [N][K/scale_group], row-major
  *   packed  host buffer of desc->total_bytes; every byte is written
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_TRIT, BGG_ERR_SCALE (nothing
  * useful is left in packed after an error). */
@@ -140,7 +151,7 @@ bgg_status bgg_pack_weights(const bgg_weights_desc* desc, const int8_t* trits,
 /* Lay out canonical row-stream bytes (the format's file form) in the device
  * layout without decoding them.
  *   canonical  host uint8 [N][desc->row_bytes]
- *   scales     host fp16 bits [N][K/128]
+ *   scales     host fp16 bits [N][K/scale_group]
  *   packed     host buffer of desc->total_bytes
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_PACKED_BYTE, BGG_ERR_SCALE. */
 bgg_status bgg_repack_canonical(const bgg_weights_desc* desc, const uint8_t* canonical,
@@ -154,7 +165,7 @@ bgg_status bgg_validate_packed(const bgg_weights_desc* desc, const void* packed)
 /* Decode a packed device buffer back to trits and scales with the same
  * device decoders the products use (for checking; not on the hot path).
  *   packed_dev  device, desc->total_bytes
- *   trits_dev   device int8 [N][K]; scales_dev device fp16 bits [N][K/128]
+ *   trits_dev   device int8 [N][K]; scales_dev device fp16 bits [N][K/scale_group]
  * Invalid codes decode as t = 0.  Errors: BGG_ERR_NULL, BGG_ERR_DESC,
  * BGG_ERR_BUFFER, BGG_ERR_HIP. */
 bgg_status bgg_unpack_weights(const bgg_weights_desc* desc, const void* packed_dev,

@@ -10,8 +10,9 @@ ternary model on the source pages; no trained weights exist here):
 
 * trits   i.i.d., P(-1) = P(+1) = 0.31, P(0) = 0.38 (a 62 % non-zero rate, the
   order of the rate reported in lpnh.cn/news/2428882, section 2.1);
-* scales  one per 128 weights along K, uniform in [0.005, 0.05], rounded to
-  fp16 (round to nearest even);
+* signs   (the 1-bit weights of Q1_0) i.i.d., P(-1) = P(+1) = 1/2;
+* scales  one per 128 weights along K (per 64 for Q2_0_g64), uniform in
+  [0.005, 0.05], rounded to fp16 (round to nearest even);
 * x       i.i.d. N(0, 1), rounded to fp16.
 
 Every element is a counter-based SplitMix64 draw (see synth.c), so a row of a
@@ -73,9 +74,29 @@ def trits(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarra
     return out
 
 
-def scales_f16(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarray:
-    """fp16 [n, k/128] scales, uniform in [0.005, 0.05] then rounded to fp16."""
-    g = k // GROUP
+def signs(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarray:
+    """int8 [n, k] weights in {-1, +1}, each +1 with probability 1/2."""
+    u = np.empty((n, k), dtype=np.float64)
+    if u.size:
+        _load().synth_uniform(seed, matrix_id, row0 * k, u.size, u.ctypes.data)
+    return np.where(u < 0.5, 1, -1).astype(np.int8)
+
+
+def weights(fmt: str, seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarray:
+    """The weights of a matrix stored in format fmt: signs for Q1_0, else trits."""
+    return (signs if fmt == "Q1_0" else trits)(seed, matrix_id, n, k, row0)
+
+
+def scale_group(fmt: str) -> int:
+    """Weights per fp16 scale along K in format fmt (a property of the file
+    format, used to size the scale arrays drawn here)."""
+    return 64 if fmt == "Q2_0_G64" else GROUP
+
+
+def scales_f16(seed: int, matrix_id: int, n: int, k: int, row0: int = 0,
+               group: int = GROUP) -> np.ndarray:
+    """fp16 [n, k/group] scales, uniform in [0.005, 0.05] then rounded to fp16."""
+    g = k // group
     u = np.empty((n, g), dtype=np.float64)
     if u.size:
         _load().synth_uniform(seed, matrix_id, row0 * g, u.size, u.ctypes.data)
@@ -148,9 +169,11 @@ WORKLOADS = {
 ACT_STREAM = 1000  # activation stream ids start here (one per input width)
 
 
-def workload_matrix(m: Matrix, seed: int):
-    """(trits int8 [n,k], scales fp16 [n,k/128]) of one workload matrix."""
-    return trits(seed, m.matrix_id, m.n, m.k), scales_f16(seed, m.matrix_id, m.n, m.k)
+def workload_matrix(m: Matrix, seed: int, fmt: str = "PQ2_0"):
+    """(weights int8 [n,k], scales fp16 [n,k/group]) of one workload matrix
+    stored in format fmt (trits and a scale per 128 for PQ2_0 and PTQ1_0)."""
+    return (weights(fmt, seed, m.matrix_id, m.n, m.k),
+            scales_f16(seed, m.matrix_id, m.n, m.k, group=scale_group(fmt)))
 
 
 def workload_x(seed: int, m: int, k: int) -> np.ndarray:

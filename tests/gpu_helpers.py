@@ -18,8 +18,11 @@ def relerr(y, ref) -> np.ndarray:
     return np.max(np.abs(y - ref), axis=-1) / den
 
 
-def gen_matrix(seed, mid, N, K, row0=0):
-    return synth.trits(seed, mid, N, K, row0), synth.scales_f16(seed, mid, N, K, row0)
+def gen_matrix(seed, mid, N, K, row0=0, fmt="PQ2_0"):
+    """Seeded weights and scales of a matrix stored in format fmt (signs for
+    Q1_0, trits otherwise; a scale per 64 weights for Q2_0_G64)."""
+    return (synth.weights(fmt, seed, mid, N, K, row0),
+            synth.scales_f16(seed, mid, N, K, row0, group=synth.scale_group(fmt)))
 
 
 class Dev:

@@ -13,7 +13,9 @@ import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bgg.h")
-FMTS = ("PQ2_0", "PTQ1_0")
+FMTS = ("PQ2_0", "PTQ1_0", "Q1_0", "Q2_0_G64")
+# the byte of zero trits (Q1_0: all -1, under a zero scale in padding rows)
+ZERO_BYTE = {"PQ2_0": 0x55, "PTQ1_0": 121, "Q1_0": 0x00, "Q2_0_G64": 0x55}
 RNG = np.random.default_rng(99)
 
 
@@ -33,7 +35,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert bgg.bgg_abi_version() == 2
+    assert bgg.bgg_abi_version() == 3
     for s in range(10):
         assert bgg.bgg_status_string(s)
     assert bgg.bgg_status_string(0) == "ok"
@@ -44,18 +46,20 @@ def test_abi_version_and_status_strings():
 def test_describe_sizes(fmt, N, K):
     d = bgg.bgg_describe(fmt, N, K)
     assert d.groups == K // 128
+    assert d.scale_group == oracle.scale_group(fmt)
+    assert d.scales == K // d.scale_group
     assert d.row_bytes == oracle.row_bytes(fmt, K)
     assert d.format_bytes == oracle.format_bytes(fmt, N, K)
     assert d.row_tiles == -(-N // 64)
     assert d.chunks == -(-d.row_bytes // 16)
     assert d.trit_bytes == d.row_tiles * d.chunks * 1024
     assert d.scale_offset % 256 == 0 and d.scale_offset >= d.trit_bytes
-    assert d.scale_bytes == d.row_tiles * d.groups * 128
+    assert d.scale_bytes == d.row_tiles * d.scales * 128
     assert d.total_bytes == d.scale_offset + d.scale_bytes + bgg.BGG_READ_SLACK
 
 
 def test_describe_rejects_bad_shapes_and_formats():
-    for (f, N, K, st) in [(3, 64, 128, 2), (0, 64, 128, 2), (1, 0, 128, 3), (1, 64, 100, 3),
+    for (f, N, K, st) in [(5, 64, 128, 2), (0, 64, 128, 2), (3, 64, 64, 3), (4, 64, 192, 3), (1, 0, 128, 3), (1, 64, 100, 3),
                           (2, 64, 0, 3), (2, 64, 64, 3), (1, -5, 128, 3)]:
         with pytest.raises(bgg.BggError) as e:
             bgg.bgg_describe(f, N, K)
@@ -65,7 +69,7 @@ def test_describe_rejects_bad_shapes_and_formats():
 def _canonical_from_layout(d, packed):
     """Read row r's canonical byte stream back out of the tiled device layout
     (the layout documented in bgg.h)."""
-    C, G = d.chunks, d.groups
+    C, G = d.chunks, d.scales
     tiles = packed[:d.trit_bytes].reshape(d.row_tiles, C, 64, 16)
     rows = tiles.transpose(0, 2, 1, 3).reshape(d.row_tiles * 64, C * 16)
     sc = packed[d.scale_offset:d.scale_offset + d.scale_bytes].view(np.uint16)
@@ -76,14 +80,14 @@ def _canonical_from_layout(d, packed):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(1, 128), (100, 640), (130, 1152), (64, 6144)])
 def test_pack_layout_matches_oracle_canonical_bytes(fmt, N, K):
-    T = synth.trits(5, 1, N, K)
-    S = synth.scales_f16(5, 1, N, K)
+    T = synth.weights(fmt, 5, 1, N, K)
+    S = synth.scales_f16(5, 1, N, K, group=synth.scale_group(fmt))
     d = bgg.bgg_describe(fmt, N, K)
     packed = bgg.bgg_pack_weights(d, T, S)
     rows, sc = _canonical_from_layout(d, packed)
     canon = oracle.pack(fmt, T)
     assert np.array_equal(rows[:N, :d.row_bytes], canon)
-    zero = 0x55 if fmt == "PQ2_0" else 121
+    zero = ZERO_BYTE[fmt]
     assert np.all(rows[:N, d.row_bytes:] == zero)       # zero trits past the row stream
     assert np.all(rows[N:] == zero)                      # zero trits in padding rows
     assert np.array_equal(sc[:N], S.view(np.uint16))
@@ -104,6 +108,17 @@ def test_pack_rejects_bad_trits_and_scales():
     T[2, 7] = -2
     with pytest.raises(bgg.BggError):
         bgg.bgg_pack_weights(d, T, S)
+    # Q1_0 holds signs only: a zero weight is an error
+    d1 = bgg.bgg_describe("Q1_0", 4, 128)
+    T1 = np.ones((4, 128), np.int8)
+    T1[3, 100] = 0
+    with pytest.raises(bgg.BggError) as e:
+        bgg.bgg_pack_weights(d1, T1, S)
+    assert e.value.status == 4 and "row 3 col 100" in str(e.value)
+    # Q2_0_G64 wants a scale per 64 weights
+    d64 = bgg.bgg_describe("Q2_0_G64", 4, 128)
+    with pytest.raises(ValueError):
+        bgg.bgg_pack_weights(d64, T, S)
     T[2, 7] = 0
     for bad in (np.inf, -np.inf, np.nan):
         S2 = S.copy()
@@ -117,26 +132,35 @@ def test_pack_rejects_bad_trits_and_scales():
 def test_validate_catches_bad_bytes(fmt):
     N, K = 70, 256
     d = bgg.bgg_describe(fmt, N, K)
-    T = synth.trits(9, 2, N, K)
-    S = synth.scales_f16(9, 2, N, K)
+    T = synth.weights(fmt, 9, 2, N, K)
+    S = synth.scales_f16(9, 2, N, K, group=synth.scale_group(fmt))
     p = bgg.bgg_pack_weights(d, T, S)
     bgg.bgg_validate_packed(d, p)
-    bad = p.copy()
-    bad[17] = 0xFF                     # PQ2_0 code 3 / PTQ1_0 byte 255
-    with pytest.raises(bgg.BggError) as e:
-        bgg.bgg_validate_packed(d, bad)
-    assert e.value.status == 5
-    canon = oracle.pack(fmt, T)
-    canon[3, 2] = 0xC0 if fmt == "PQ2_0" else 250
-    with pytest.raises(bgg.BggError) as e:
-        bgg.bgg_repack_canonical(d, canon, S)
-    assert e.value.status == 5
-    # a padding row that holds a non-zero trit is rejected
+    if fmt != "Q1_0":                  # (every Q1_0 byte is eight valid signs)
+        bad = p.copy()
+        bad[17] = 0xFF                 # a 2-bit code 3 / base-3 byte 255
+        with pytest.raises(bgg.BggError) as e:
+            bgg.bgg_validate_packed(d, bad)
+        assert e.value.status == 5
+        canon = oracle.pack(fmt, T)
+        canon[3, 2] = 250 if fmt == "PTQ1_0" else 0xC0
+        with pytest.raises(bgg.BggError) as e:
+            bgg.bgg_repack_canonical(d, canon, S)
+        assert e.value.status == 5
+    # a padding row that holds anything but the zero byte is rejected
     rows_layout = p.copy()
     t_last, l_last = (N // 64), (N % 64)   # first padding row
-    rows_layout[((t_last * d.chunks) * 64 + l_last) * 16] = 0 if fmt == "PQ2_0" else 0
-    with pytest.raises(bgg.BggError):
+    rows_layout[((t_last * d.chunks) * 64 + l_last) * 16] = 0x01 if fmt == "Q1_0" else 0
+    with pytest.raises(bgg.BggError) as e:
         bgg.bgg_validate_packed(d, rows_layout)
+    assert e.value.status == 5
+    # and so is a non-zero scale of a padding row
+    sc = p.copy()
+    s16 = sc[d.scale_offset:d.scale_offset + d.scale_bytes].view(np.uint16)
+    s16[(t_last * d.scales) * 64 + l_last] = 0x3C00
+    with pytest.raises(bgg.BggError) as e:
+        bgg.bgg_validate_packed(d, sc)
+    assert e.value.status == 9
 
 
 def test_descriptor_tampering_is_rejected():
