@@ -211,6 +211,59 @@ def decode_stack_bench(args, bgg, torch, dev, capture):
     return res
 
 
+def sister_bench(args, bgg, torch, dev, capture):
+    """The projection matrices (gate_up 17408x5120, down 5120x17408) in the
+    sister formats Q1_0 (sign bits, scale per 128) and Q2_0_G64 (2-bit codes,
+    scale per 64), at M = 1 and M = 16: microseconds per bgg_ternary_gemv
+    call (prepare + matrix-core run) from HIP events around a graph of
+    back-to-back calls that cycle through the weight copies, and GB/s of
+    the format's packed bytes."""
+    import synth
+    w = synth.WORKLOADS["projection"]
+    seed = w["seed"]
+    reps = args.kernel_reps
+    out = {}
+    for fmt in ("Q1_0", "Q2_0_G64"):
+        rows = []
+        for mat in w["matrices"]:
+            T, S = synth.workload_matrix(mat, seed, fmt)
+            d = bgg.bgg_describe(fmt, mat.n, mat.k)
+            host = bgg.bgg_pack_weights(d, T, S)
+            del T, S
+            copies = [bgg.upload(host, dev) for _ in range(args.copies)]
+            x = torch.from_numpy(synth.workload_x(seed, 16, mat.k)).to(dev)
+            y = torch.empty((16, mat.n), dtype=torch.float16, device=dev)
+            ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d, 16), dev)
+            for M in (1, 16):
+                g = capture(lambda st, M=M: [
+                    bgg.bgg_ternary_gemv(d, copies[r % args.copies], x, y, M, bgg.BGG_ROTATE_INPUT,
+                                         ws, st) for r in range(reps)])
+                g.replay()
+                cur = torch.cuda.current_stream()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(cur)
+                g.replay()
+                b.record(cur)
+                b.synchronize()
+                us = a.elapsed_time(b) * 1e3 / reps
+                rows.append(dict(matrix=mat.name, n=mat.n, k=mat.k, m=M,
+                                 kernel=bgg.bgg_gemv_kernel_name(d, M),
+                                 bytes_per_call=int(d.format_bytes), avg_us=round(us, 3),
+                                 gbs=round(d.format_bytes / us / 1e3, 1)))
+                del g
+            del copies
+        step = {}
+        for M in (1, 16):
+            r = [e for e in rows if e["m"] == M]
+            tot_us = sum(e["avg_us"] for e in r)
+            step[f"m{M}"] = dict(us=round(tot_us, 2),
+                                 gbs=round(sum(e["bytes_per_call"] for e in r) / tot_us / 1e3, 1))
+        out[fmt] = dict(calls=rows, gate_up_plus_down=step)
+        log(f"sister {fmt}: " + ", ".join(f"{e['matrix']} M={e['m']} {e['avg_us']:.2f}us "
+                                          f"{e['gbs']:.0f}GB/s" for e in rows))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +278,8 @@ def main() -> int:
     ap.add_argument("--gemm-warmup", type=int, default=40,
                     help="untimed rotate + GEMM pairs before the timed prefill launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sister", action="store_true",
+                    help="skip the Q1_0 / Q2_0_G64 lines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-reps", type=int, default=100,
                     help="back-to-back launches per per-kernel timing")
@@ -441,6 +496,11 @@ def main() -> int:
     if not args.no_decode_step:
         stack = decode_stack_bench(args, bgg, torch, dev, capture)
 
+    # ------------------------------------------ sister formats, M = 1 and 16
+    sister = None
+    if not args.no_sister:
+        sister = sister_bench(args, bgg, torch, dev, capture)
+
     # ----------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -479,6 +539,7 @@ def main() -> int:
         "kernels": kernels,
         "prefill_gemm": prefill,
         "decode_step": stack,
+        "sister_formats": sister,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)
