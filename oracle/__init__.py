@@ -17,7 +17,11 @@ rows).  What each function follows on the source pages is stated in oracle.c:
 * ``format_bytes``       bytes of a packed matrix incl. its fp16 scales;
 * ``matvec(T, S, xr)``   y = sum_k S[n][k/group] T[n][k] xr[m][k] in fp64
                          (group = K / scales per row);
-* ``linear(...)``        unpack + rotate + matvec from the stored form.
+* ``linear(...)``        unpack + rotate + matvec from the stored form;
+* ``f64_to_f16(v)``      one round-to-nearest-even conversion to fp16 bits;
+* ``ternarize(W)``       the offline front end: rotate float weight rows per
+                         128-block, scale = fp16(mean |w'|) per group (a
+                         reading), trits = nearest of {-s, 0, s}.
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, library routines, brute force and the numbers the pages print.
@@ -71,6 +75,10 @@ def configure(lib):
     lib.oracle_unpack.argtypes = [ci, vp, i64, i64, vp]
     lib.oracle_matvec.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.oracle_linear.argtypes = [ci, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+    lib.oracle_ternarize.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_ternarize.restype = ci
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
     for f in (lib.oracle_sylvester, lib.oracle_rotate, lib.oracle_pack, lib.oracle_unpack,
@@ -217,3 +225,21 @@ def linear(fmt, packed, S, x, rotate: bool = True) -> np.ndarray:
     _check(_load().oracle_linear(_fmt(fmt), packed.ctypes.data, Sb.ctypes.data, xb.ctypes.data,
                                  M, N, K, 1 if rotate else 0, y.ctypes.data), "linear")
     return y
+
+
+def f64_to_f16(v: float) -> int:
+    """fp16 bits of v, rounded to nearest even (inf past the fp16 range)."""
+    return int(_load().oracle_f64_to_f16(float(v)))
+
+
+def ternarize(W):
+    """Trits int8 [N, K] and fp16 scales [N, K/128] of float32 weights
+    W [N, K] in the layer's stored coordinates (rotate, mean-magnitude
+    scale per 128-group, nearest of {-s, 0, s})."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.int8)
+    S = np.empty((N, K // BLOCK), dtype=np.uint16)
+    _check(_load().oracle_ternarize(W.ctypes.data, N, K, T.ctypes.data, S.ctypes.data),
+           "ternarize")
+    return T, S.view(np.float16)

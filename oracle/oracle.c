@@ -39,7 +39,8 @@
  *     FP16 scale per 64 weights (2 + 16/64 = 2.25 bits).  The activation
  *     transform keeps its 128-blocks for every format.
  *
- * All floating point is fp64; fp16 inputs are decoded exactly.
+ * All floating point is fp64; fp16 inputs are decoded exactly and fp16
+ * outputs (the front end's scales) are rounded once, to nearest even.
  */
 #include <math.h>
 #include <stdint.h>
@@ -249,6 +250,81 @@ int oracle_linear(int fmt, const uint8_t* packed, const uint16_t* S, const uint1
   free(T);
   free(xr);
   return rc;
+}
+
+/* double -> IEEE 754 binary16 bits, rounded to nearest with ties to even:
+ * the value is written as m * 2^q with the integer m of the target's 11
+ * significant bits (fewer for subnormals, whose exponent is pinned at -24),
+ * the remainder decides the rounding, and a carry out of the significand
+ * moves to the next binade; magnitudes that round past 65504 become inf. */
+uint16_t oracle_f64_to_f16(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return 0x7E00;
+  if (isinf(v)) return (uint16_t)(sign | 0x7C00);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                 /* a = f * 2^e, f in [0.5, 1) */
+  int q = e - 11;               /* 2^q = weight of the last kept bit */
+  if (q < -24) q = -24;         /* subnormal range: fixed step 2^-24 */
+  double scaled = ldexp(a, -q); /* exact: a power-of-two scaling */
+  double m = floor(scaled);
+  double rem = scaled - m;      /* exact: the fraction of a double */
+  if (rem > 0.5 || (rem == 0.5 && fmod(m, 2.0) == 1.0)) m += 1.0;
+  if (m >= 2048.0) {            /* carried into the next binade */
+    m /= 2.0;
+    q += 1;
+  }
+  if (m < 1024.0)               /* subnormal (q == -24): exponent field 0 */
+    return (uint16_t)(sign | (uint16_t)m);
+  int ef = q + 25;              /* value = m * 2^q = (1 + f/1024) 2^(ef - 15) */
+  if (ef >= 31) return (uint16_t)(sign | 0x7C00);
+  return (uint16_t)(sign | (uint16_t)(ef << 10) | (uint16_t)((int)m - 1024));
+}
+
+/* Offline front end: float weights W [N][K] -> trits T [N][K] and fp16
+ * scales S [N][K/128] in the coordinates the layer stores.
+ *   1. rotate: every 128-block of a row becomes H_128/sqrt(128) times that
+ *      block (the weight side of the rotation: y = W x = (W Hn)(Hn x) with
+ *      Hn symmetric and orthogonal, so the stored rows are W Hn) [A method
+ *      paragraph, B "它怎么做到的"];
+ *   2. scale of each 128-group: the mean magnitude of its rotated weights,
+ *      rounded to fp16 (a reading: the pages give no scale rule);
+ *   3. ternary rounding: each rotated weight goes to the nearest of -s, 0,
+ *      +s, i.e. t = sign(w') when |w'| > s/2 and 0 otherwise (a tie at s/2
+ *      goes to 0, the even neighbour of rint) [B "它怎么做到的"].
+ * Returns 0, -1 for K not a multiple of 128, -2 when out of memory. */
+int oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* T, uint16_t* S) {
+  if (K % BLOCK || N < 0) return -1;
+  double* H = (double*)malloc(sizeof(double) * BLOCK * BLOCK);
+  if (!H) return -2;
+  oracle_sylvester(BLOCK, H);
+  const double norm = 1.0 / sqrt((double)BLOCK);
+  const int64_t G = K / BLOCK;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    double blk[BLOCK], wr[BLOCK];
+    for (int64_t b = 0; b < G; ++b) {
+      for (int i = 0; i < BLOCK; ++i) blk[i] = (double)W[n * K + b * BLOCK + i];
+      double mag = 0.0;
+      for (int r = 0; r < BLOCK; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < BLOCK; ++i) acc += H[r * BLOCK + i] * blk[i];
+        wr[r] = acc * norm;
+        mag += fabs(wr[r]);
+      }
+      const uint16_t sh = oracle_f64_to_f16(mag / BLOCK);
+      const double s = oracle_f16_to_f64(sh);
+      S[n * G + b] = sh;
+      for (int r = 0; r < BLOCK; ++r) {
+        int8_t t = 0;
+        if (fabs(wr[r]) > 0.5 * s) t = wr[r] > 0.0 ? 1 : -1;
+        T[n * K + b * BLOCK + r] = t;
+      }
+    }
+  }
+  free(H);
+  return 0;
 }
 
 /* Threads the OpenMP loops above run on (for reporting only). */

@@ -11,6 +11,8 @@ ternary model on the source pages; no trained weights exist here):
 * trits   i.i.d., P(-1) = P(+1) = 0.31, P(0) = 0.38 (a 62 % non-zero rate, the
   order of the rate reported in lpnh.cn/news/2428882, section 2.1);
 * signs   (the 1-bit weights of Q1_0) i.i.d., P(-1) = P(+1) = 1/2;
+* float weights (input of the offline front end) i.i.d. N(0, 0.02^2), each
+  an outlier 40 times larger with probability 0.004;
 * scales  one per 128 weights along K (per 64 for Q2_0_g64), uniform in
   [0.005, 0.05], rounded to fp16 (round to nearest even);
 * x       i.i.d. N(0, 1), rounded to fp16.
@@ -72,6 +74,19 @@ def trits(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarra
     if out.size:
         _load().synth_trits(seed, matrix_id, row0 * k, out.size, out.ctypes.data)
     return out
+
+
+def float_weights(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarray:
+    """float32 [n, k] weights before ternarization: N(0, 0.02^2), and each
+    element independently (probability 0.004) an outlier 40 times larger --
+    a stand-in for the few large weights the pages say carry most of a
+    layer's information (no trained weights exist here)."""
+    z = np.empty((n, k), dtype=np.float64)
+    u = np.empty((n, k), dtype=np.float64)
+    if z.size:
+        _load().synth_normal(seed, matrix_id, row0 * k, z.size, z.ctypes.data)
+        _load().synth_uniform(seed, matrix_id + (1 << 32), row0 * k, u.size, u.ctypes.data)
+    return (0.02 * z * np.where(u < 0.004, 40.0, 1.0)).astype(np.float32)
 
 
 def signs(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarray:

@@ -347,6 +347,94 @@ def pin_linear_sister_formats():
             assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# offline front end: fp16 rounding and rotate-then-ternarize
+# --------------------------------------------------------------------------
+def pin_f64_to_f16_matches_numpy():
+    """One round-to-nearest-even conversion, as numpy's double -> half."""
+    vals = [0.0, -0.0, 1.0, -2.5, 65504.0, 65519.99, 65520.0, 1e6, -1e6, 2.0 ** -14,
+            2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -25 * 1.0000001, 6.1e-5, 1e-9,
+            0.1, 1.0 / 3.0, np.inf, -np.inf]
+    # exact ties between neighbouring halves, both parities, normal and subnormal
+    for h in (0x3C00, 0x3C01, 0x0001, 0x0002, 0x03FF, 0x0400, 0x7BFE, 0x1234, 0x5555):
+        a = float(np.array([h], np.uint16).view(np.float16)[0])
+        b = float(np.array([h + 1], np.uint16).view(np.float16)[0])
+        vals += [(a + b) / 2, -(a + b) / 2, np.nextafter((a + b) / 2, 0), np.nextafter((a + b) / 2, 1e9)]
+    vals += list(RNG.standard_normal(2000) * 10.0 ** RNG.uniform(-9, 5, 2000))
+    for v in vals:
+        want = int(np.array([v], np.float64).astype(np.float16).view(np.uint16)[0])
+        assert oracle.f64_to_f16(v) == want, (v, hex(want))
+
+
+def _rotate_rows_f64(W):
+    """W blockdiag(H_128/sqrt(128)) by scipy's Hadamard routine."""
+    return np.asarray(W, np.float64) @ _hhat_blockdiag(W.shape[1])
+
+
+def pin_ternarize_brute_force():
+    """Small random inputs: the scale is numpy's fp16 of the mean rotated
+    magnitude, and each trit is the candidate of {-1, 0, 1} whose multiple
+    of the scale lies nearest to the rotated weight (found by trying all)."""
+    for (N, K) in ((3, 128), (5, 384)):
+        W = (RNG.standard_normal((N, K)) * 0.02).astype(np.float32)
+        T, S = oracle.ternarize(W)
+        Wr = _rotate_rows_f64(W)
+        for n in range(N):
+            for g in range(K // 128):
+                blk = Wr[n, 128 * g:128 * g + 128]
+                s = np.float16(np.mean(np.abs(blk)))
+                assert S[n, g].view(np.uint16) == s.view(np.uint16)
+                cand = np.array([-1, 0, 1])
+                err = np.abs(blk[:, None] - cand[None, :] * float(s))
+                assert np.array_equal(T[n, 128 * g:128 * g + 128], cand[np.argmin(err, axis=1)])
+
+
+def pin_ternarize_sylvester_rows_and_zeros():
+    """A block equal to c times Sylvester row r rotates to c sqrt(128) e_r:
+    one trit sign(c) at r, scale fp16(|c| / sqrt(128)); a zero block gives
+    zero trits and a zero scale; a constant block is Sylvester row 0."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(128)
+    K = 512
+    cases = [(0, 0, 0.25), (1, 77, -1.5), (2, 127, 3.0), (3, 5, 0.0078125)]
+    W = np.zeros((len(cases) + 1, K), np.float32)
+    for n, (b, r, c) in enumerate(cases):
+        W[n, 128 * b:128 * b + 128] = (c * math.sqrt(128.0)) * H[r]
+    W[len(cases), 128:256] = 0.75                       # constant block
+    T, S = oracle.ternarize(W)
+    for n, (b, r, c) in enumerate(cases):
+        want = np.zeros(K, np.int8)
+        want[128 * b + r] = 1 if c > 0 else -1
+        assert np.array_equal(T[n], want)
+        assert S[n, b] == np.float16(abs(c)) and np.all(S[n, np.arange(4) != b] == 0)
+    want = np.zeros(K, np.int8)
+    want[128] = 1
+    assert np.array_equal(T[len(cases)], want)
+    assert S[len(cases), 1] == np.float16(0.75 * 128 / math.sqrt(128.0) / 128)
+    Tz, Sz = oracle.ternarize(np.zeros((2, 256), np.float32))
+    assert not Tz.any() and not Sz.view(np.uint16).any()
+
+
+def pin_ternarize_rotation_spreads_outliers():
+    """The pages' reason for rotating first: with a few large outliers per
+    row, ternary rounding after the rotation loses less than rounding the
+    weights as they are (same scale rule).  Feeding W Hn to the front end
+    makes it round W itself, since Hn Hn = I."""
+    N, K = 64, 1024
+    W = RNG.standard_normal((N, K)) * 0.02
+    idx = RNG.random((N, K)) < 0.004
+    W[idx] *= 40.0
+    W = W.astype(np.float32)
+    T1, S1 = oracle.ternarize(W)
+    rec_rot = (T1 * S1.astype(np.float64).repeat(128, axis=1)) @ _hhat_blockdiag(K)
+    V = _rotate_rows_f64(W).astype(np.float32)
+    T2, S2 = oracle.ternarize(V)
+    rec_direct = T2 * S2.astype(np.float64).repeat(128, axis=1)
+    err_rot = np.linalg.norm(W - rec_rot) / np.linalg.norm(W)
+    err_direct = np.linalg.norm(W - rec_direct) / np.linalg.norm(W)
+    assert err_rot < 0.8 * err_direct, (err_rot, err_direct)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -376,6 +464,14 @@ MUTANTS = {
                          "int64_t k = 5 * j + (4 - i);\n          if (k < K) T[n * K + k] = (int8_t)((int)digit - 1);"),
     "f16_exponent_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     "transposed_x": ("* xr[m * K + k];", "* xr[k * M + m];"),
+    "f16_ties_to_odd": ("fmod(m, 2.0) == 1.0", "fmod(m, 2.0) == 0.0"),
+    "f16_subnormal_step": ("if (q < -24) q = -24;", "if (q < -25) q = -25;"),
+    "f16_exponent_field": ("int ef = q + 25;", "int ef = q + 24;"),
+    "ternarize_threshold": ("if (fabs(wr[r]) > 0.5 * s)", "if (fabs(wr[r]) > s)"),
+    "ternarize_scale_mean": ("oracle_f64_to_f16(mag / BLOCK)", "oracle_f64_to_f16(mag / K)"),
+    "ternarize_rotation_norm": ("wr[r] = acc * norm;", "wr[r] = acc;"),
+    "ternarize_no_rotation": ("acc += H[r * BLOCK + i] * blk[i];\n        wr[r]",
+                              "acc += (r == i) * blk[i];\n        wr[r]"),
 }
 
 
