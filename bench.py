@@ -264,6 +264,42 @@ def sister_bench(args, bgg, torch, dev, capture):
     return out
 
 
+def ternarize_bench(args, bgg, torch, dev):
+    """The offline front end on the projection shapes: float32 weights ->
+    trits and fp16 scales (bgg_rotate_ternarize), HIP events around 10
+    back-to-back calls after 3 warm-up calls; GB/s of the algorithmic bytes
+    (4 read + 1 written per weight, 2 written per 128-block)."""
+    import synth
+    w = synth.WORKLOADS["projection"]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for mat in w["matrices"]:
+        W = torch.from_numpy(synth.float_weights(w["seed"], mat.matrix_id, mat.n, mat.k)).to(dev)
+        T = torch.empty((mat.n, mat.k), dtype=torch.int8, device=dev)
+        S = torch.empty((mat.n, mat.k // 128), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            bgg.bgg_rotate_ternarize(W, mat.n, mat.k, T, S, stream)
+        reps = 10
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            bgg.bgg_rotate_ternarize(W, mat.n, mat.k, T, S, stream)
+        b.record(stream)
+        b.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = mat.n * mat.k * 5 + mat.n * (mat.k // 128) * 2
+        rows.append(dict(matrix=mat.name, n=mat.n, k=mat.k, avg_us=round(us, 1), bytes=nbytes,
+                         gbs=round(nbytes / us / 1e3, 1),
+                         frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)))
+        del W, T, S
+    log("ternarize: " + ", ".join(f"{r['matrix']} {r['avg_us']}us {r['gbs']}GB/s" for r in rows))
+    best = max(r["gbs"] for r in rows)
+    return dict(kernel="k_rotate_ternarize", workload="float32 weights of the projection shapes "
+                "-> trits + fp16 scales (rotate, mean-magnitude scale, nearest trit)",
+                shapes=rows, roofline=dict(bound="hbm", achieved=best, peak=HBM_PEAK_GBS,
+                                           unit="GB/s", frac=round(best / HBM_PEAK_GBS, 4)))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +314,8 @@ def main() -> int:
     ap.add_argument("--gemm-warmup", type=int, default=40,
                     help="untimed rotate + GEMM pairs before the timed prefill launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ternarize", action="store_true",
+                    help="skip the offline front end lines")
     ap.add_argument("--no-sister", action="store_true",
                     help="skip the Q1_0 / Q2_0_G64 lines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -501,6 +539,11 @@ def main() -> int:
     if not args.no_sister:
         sister = sister_bench(args, bgg, torch, dev, capture)
 
+    # ------------------------------------------- offline front end (float W)
+    tern = None
+    if not args.no_ternarize:
+        tern = ternarize_bench(args, bgg, torch, dev)
+
     # ----------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -540,6 +583,7 @@ def main() -> int:
         "prefill_gemm": prefill,
         "decode_step": stack,
         "sister_formats": sister,
+        "ternarize": tern,
         "source_hash": source_hash(),
     }
     print(json.dumps(out), flush=True)

@@ -76,6 +76,7 @@ _SIGS = {
     "bgg_validate_packed": ([_P, _vp], _i32),
     "bgg_unpack_weights": ([_P, _vp, _vp, _vp, _vp], _i32),
     "bgg_hadamard_rotate": ([_vp, _vp, _i64, _i64, _vp], _i32),
+    "bgg_rotate_ternarize": ([_vp, _i64, _i64, _vp, _vp, _vp], _i32),
     "bgg_gemv_workspace_size": ([_P, _i64], _sz),
     "bgg_ternary_gemv": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_gemv_prepare": ([_P, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
@@ -208,6 +209,15 @@ def bgg_unpack_weights(desc, packed_dev, trits_dev, scales_dev, stream=None) -> 
 def bgg_hadamard_rotate(x_dev, xr_dev, M: int, K: int, stream=None) -> None:
     _ok(_lib.bgg_hadamard_rotate(_dev_ptr(x_dev, M * K * 2, "x"), _dev_ptr(xr_dev, M * K * 2, "xr"),
                                  M, K, _stream(stream)), "bgg_hadamard_rotate")
+
+
+def bgg_rotate_ternarize(w_dev, N: int, K: int, trits_dev, scales_dev, stream=None) -> None:
+    """Device float32 weights [N, K] -> device int8 trits [N, K] and fp16
+    scales [N, K/128] in the layer's stored coordinates."""
+    _ok(_lib.bgg_rotate_ternarize(_dev_ptr(w_dev, N * K * 4, "w"), N, K,
+                                  _dev_ptr(trits_dev, N * K, "trits"),
+                                  _dev_ptr(scales_dev, N * (K // 128) * 2, "scales"),
+                                  _stream(stream)), "bgg_rotate_ternarize")
 
 
 def bgg_ternary_gemv(desc, packed_dev, x_dev, y_dev, M: int, flags: int, workspace, stream=None) -> None:

@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbgg.so")
-SOURCES = ["bgg_host.cpp", "bgg_rotate.hip", "bgg_gemv.hip", "bgg_unpack.hip", "bgg_gemm.hip"]
+SOURCES = ["bgg_host.cpp", "bgg_rotate.hip", "bgg_gemv.hip", "bgg_unpack.hip", "bgg_gemm.hip",
+           "bgg_ternarize.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of the generated code.

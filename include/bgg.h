@@ -179,6 +179,26 @@ bgg_status bgg_unpack_weights(const bgg_weights_desc* desc, const void* packed_d
 bgg_status bgg_hadamard_rotate(const void* x_dev, void* xr_dev, int64_t M, int64_t K,
                                void* stream);
 
+/* Offline front end: float weights in model coordinates -> the trits and
+ * fp16 scales that bgg_pack_weights takes [B 它怎么做到的: rotate the weight
+ * matrix by a Hadamard transform, then round to -1, 0, +1; A method
+ * paragraph: one FP16 scale per 128 weights].  For every 128-block of every
+ * row: w' = H_128/sqrt(128) times the block (fp32 butterflies; the stored
+ * rows are W blockdiag(Hn), so that W x = (W Hn)(Hn x)); the block's scale
+ * s = fp16(mean |w'|), rounded to nearest even once (the pages give no scale
+ * rule: this is the library's reading); trit = sign(w') where 2|w'| > s,
+ * else 0 (the nearest of -s, 0, +s; a tie goes to 0).
+ *   w_dev       device float32 [N][K], 16-byte aligned (read only)
+ *   trits_dev   device int8 [N][K], 8-byte aligned (written)
+ *   scales_dev  device fp16 bits [N][K/128], 2-byte aligned (written)
+ * A block whose mean magnitude is past the fp16 range gets an infinite
+ * scale, and a non-finite weight a non-finite scale: bgg_pack_weights
+ * rejects both (BGG_ERR_SCALE).  Errors: BGG_ERR_NULL, BGG_ERR_SHAPE (K %
+ * 128, N < 0, more than 2^40 weights), BGG_ERR_BUFFER (alignment),
+ * BGG_ERR_HIP.  N == 0 is a no-op.  Asynchronous on stream. */
+bgg_status bgg_rotate_ternarize(const void* w_dev, int64_t N, int64_t K, int8_t* trits_dev,
+                                uint16_t* scales_dev, void* stream);
+
 /* Device workspace bytes that bgg_ternary_gemv needs for M tokens (0 on a
  * bad descriptor or M outside 1..16). */
 size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);

@@ -35,6 +35,12 @@ _LIB = os.path.join(_HERE, "_synth.so")
 _lib = None
 
 GROUP = 128  # weights per fp16 scale (and Hadamard block) along K
+# Stream ids are 16 bits wide (synth.c keys a stream by id << 40 below an
+# 8-bit tag); matrix ids stay below 0x4000, and the streams derived from a
+# matrix id (its signs, its outlier mask) set one of the two top bits, so
+# they never reuse the draws of another stream.
+SIGN_STREAM = 0x4000
+OUTLIER_STREAM = 0x8000
 
 
 def build(force: bool = False) -> str:
@@ -85,7 +91,7 @@ def float_weights(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> n
     u = np.empty((n, k), dtype=np.float64)
     if z.size:
         _load().synth_normal(seed, matrix_id, row0 * k, z.size, z.ctypes.data)
-        _load().synth_uniform(seed, matrix_id + (1 << 32), row0 * k, u.size, u.ctypes.data)
+        _load().synth_uniform(seed, matrix_id ^ OUTLIER_STREAM, row0 * k, u.size, u.ctypes.data)
     return (0.02 * z * np.where(u < 0.004, 40.0, 1.0)).astype(np.float32)
 
 
@@ -93,7 +99,7 @@ def signs(seed: int, matrix_id: int, n: int, k: int, row0: int = 0) -> np.ndarra
     """int8 [n, k] weights in {-1, +1}, each +1 with probability 1/2."""
     u = np.empty((n, k), dtype=np.float64)
     if u.size:
-        _load().synth_uniform(seed, matrix_id, row0 * k, u.size, u.ctypes.data)
+        _load().synth_uniform(seed, matrix_id ^ SIGN_STREAM, row0 * k, u.size, u.ctypes.data)
     return np.where(u < 0.5, 1, -1).astype(np.int8)
 
 
