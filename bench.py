@@ -481,53 +481,64 @@ def main() -> int:
     if not args.no_prefill:
         pw = synth.WORKLOADS["prefill"]
         M = pw["m"][0]
-        shapes, fwht = [], []
-        for mat in pw["matrices"]:
-            T, S = synth.workload_matrix(mat, pw["seed"])
-            d = bgg.bgg_describe("PQ2_0", mat.n, mat.k)
-            packed = bgg.upload(bgg.bgg_pack_weights(d, T, S), dev)
-            x = torch.from_numpy(synth.workload_x(pw["seed"], M, mat.k)).to(dev)
-            xr = torch.empty_like(x)
-            y = torch.empty((M, mat.n), dtype=torch.float16, device=dev)
-            # warm-up long enough (tens of ms of matrix work) for the clocks to
-            # settle: the first launches after the GEMV part run up to 25 %
-            # slower than the steady state
-            reps = 10
-            for _ in range(args.gemm_warmup):
-                bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
-                bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
-            torch.cuda.synchronize()
-            e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                  torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for r in range(reps):
-                e[r][0].record(stream)
-                bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
-                e[r][1].record(stream)
-                bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
-                e[r][2].record(stream)
-            torch.cuda.synchronize()
-            f_us = float(np.mean([a.elapsed_time(b) for a, b, _ in e])) * 1e3
-            g_us = float(np.mean([b.elapsed_time(c) for _, b, c in e])) * 1e3
-            flops = 2.0 * M * mat.n * mat.k
-            shapes.append(dict(matrix=mat.name, m=M, n=mat.n, k=mat.k, avg_us=round(g_us, 1),
-                               tflops=round(flops / g_us / 1e6, 1)))
-            fbytes = 2 * M * mat.k * 2
-            fwht.append(dict(m=M, k=mat.k, avg_us=round(f_us, 1), gbs=round(fbytes / f_us / 1e3, 1)))
-            del T, S, packed, x, xr, y
+        shapes, fwht, ptq1 = [], [], []
+        for fmt in ("PQ2_0", "PTQ1_0"):
+            for mat in pw["matrices"]:
+                T, S = synth.workload_matrix(mat, pw["seed"])
+                d = bgg.bgg_describe(fmt, mat.n, mat.k)
+                packed = bgg.upload(bgg.bgg_pack_weights(d, T, S), dev)
+                x = torch.from_numpy(synth.workload_x(pw["seed"], M, mat.k)).to(dev)
+                xr = torch.empty_like(x)
+                y = torch.empty((M, mat.n), dtype=torch.float16, device=dev)
+                # warm-up long enough (tens of ms of matrix work) for the clocks
+                # to settle: the first launches after the GEMV part run up to
+                # 25 % slower than the steady state
+                reps = 10
+                for _ in range(args.gemm_warmup):
+                    bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
+                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+                torch.cuda.synchronize()
+                e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                      torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                for r in range(reps):
+                    e[r][0].record(stream)
+                    bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
+                    e[r][1].record(stream)
+                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+                    e[r][2].record(stream)
+                torch.cuda.synchronize()
+                f_us = float(np.mean([a.elapsed_time(b) for a, b, _ in e])) * 1e3
+                g_us = float(np.mean([b.elapsed_time(c) for _, b, c in e])) * 1e3
+                flops = 2.0 * M * mat.n * mat.k
+                row = dict(matrix=mat.name, m=M, n=mat.n, k=mat.k, avg_us=round(g_us, 1),
+                           tflops=round(flops / g_us / 1e6, 1))
+                if fmt == "PQ2_0":
+                    shapes.append(row)
+                    fbytes = 2 * M * mat.k * 2
+                    fwht.append(dict(m=M, k=mat.k, avg_us=round(f_us, 1),
+                                     gbs=round(fbytes / f_us / 1e3, 1)))
+                else:
+                    ptq1.append(row)
+                del T, S, packed, x, xr, y
         tot_flops = sum(2.0 * s["m"] * s["n"] * s["k"] for s in shapes)
         tot_us = sum(s["avg_us"] for s in shapes)
         tf = tot_flops / tot_us / 1e6
+        tf3 = tot_flops / sum(s["avg_us"] for s in ptq1) / 1e6
         prefill = dict(
             workload="prefill: 4096 tokens x (5120->17408, 17408->5120), PQ2_0, x' precomputed",
             tflops=round(tf, 1), unit="TFLOP/s", shapes=shapes,
             roofline=dict(bound="mfma", achieved=round(tf, 1), peak=F16_MFMA_PEAK_TFLOPS,
                           unit="TFLOP/s", frac=round(tf / F16_MFMA_PEAK_TFLOPS, 4), traffic=None,
                           kernel="k_gemm_pq2 (fp16 MFMA, fp32 accumulate)"),
+            ptq1_0=dict(kernel="k_gemm_ptq1 (base-3 bytes -> 2-bit codes -> fp16 MFMA)",
+                        tflops=round(tf3, 1), frac=round(tf3 / F16_MFMA_PEAK_TFLOPS, 4),
+                        shapes=ptq1),
             fwht=dict(kernel="k_hadamard_rotate", shapes=fwht,
                       roofline=dict(bound="hbm", achieved=max(f["gbs"] for f in fwht),
                                     peak=HBM_PEAK_GBS, unit="GB/s",
                                     frac=round(max(f["gbs"] for f in fwht) / HBM_PEAK_GBS, 4))))
-        log(f"prefill {tf:.0f} TFLOP/s; " + ", ".join(f"{s['matrix']} {s['tflops']} TF" for s in shapes))
+        log(f"prefill PQ2_0 {tf:.0f} TFLOP/s; " + ", ".join(f"{s['matrix']} {s['tflops']} TF" for s in shapes)
+            + f"; PTQ1_0 {tf3:.0f} TFLOP/s; " + ", ".join(f"{s['matrix']} {s['tflops']} TF" for s in ptq1))
 
     # ------------------------------------- 64-layer decode step, M = 1 .. 16
     stack = None

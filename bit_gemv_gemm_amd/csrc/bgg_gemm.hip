@@ -1,4 +1,5 @@
-// Prompt-time product (PQ2_0) for gfx950: Y[M][N] = X'[M][K] . (S*T)[N][K]^T.
+// Prompt-time products for gfx950: Y[M][N] = X'[M][K] . (S*T)[N][K]^T, for
+// PQ2_0 (k_gemm_pq2) and PTQ1_0 (k_gemm_ptq1).
 //
 // allhereai.com/news/1346 ("27B 模型压到 5.95GB…"), packing paragraph: PQ2_0
 // is the packing that wins prompt processing; method paragraph: trits with
@@ -156,6 +157,175 @@ __global__ void __launch_bounds__(256, 2)
     }
 }
 
+// ---------------------------------------------------------------------------
+// PTQ1_0 (allhereai.com/news/1346, packing paragraph: the compact packing;
+// wmrh.cn/news/471187, section 关键机制: five trits per byte).  The same
+// tiling as k_gemm_pq2 with a K step of 80: one 16-byte chunk of a row's
+// base-3 stream.  Each lane turns the 16 bytes of its two rows into the
+// 2-bit code string of their 80 trits (code t + 1 in natural order, ten bits
+// per byte from a 256-entry LDS table), which is exactly the PQ2_0 code
+// word layout, so the same fp16 s*t decode feeds the MFMA; every 16-K slice
+// lies inside one 128-group, whose scale it takes.  Activation loads past K
+// (the last chunk's tail, and the padding step when the chunk count is odd)
+// are zero, so the zero trits there meet zeros.
+// ---------------------------------------------------------------------------
+constexpr int kBK3 = 80;
+constexpr int kLdsStride3 = kBK3 + 8;  // halves per LDS row (176 bytes)
+
+__global__ void __launch_bounds__(256, 2)
+    k_gemm_ptq1(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
+                uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
+                int64_t NT, uint16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride3];
+  __shared__ uint32_t lut[256];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+
+  // byte -> its five codes t_i + 1 in bits 2i..2i+1 (bytes past 242: zero trits)
+  {
+    uint32_t b = (uint32_t)tid, c = 0;
+    if (b < 243) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        c |= (b % 3u) << (2 * i);
+        b /= 3u;
+      }
+    } else {
+      c = 0x155u;
+    }
+    lut[tid] = c;
+  }
+
+  // activation loader: row tid/2 of the tile, 40 halves (five 16-byte
+  // pieces) at 40 (tid % 2); rows past M re-read row M-1 (never stored)
+  const int lr = tid >> 1, lh = tid & 1;
+  const int64_t am = m0 + lr < M ? m0 + lr : M - 1;
+  const uint16_t* a_src = X + am * K + lh * 40;
+
+  const int64_t tw = n0 / kTileRows + wave;
+  const bool w_ok = tw < NT;
+  const int64_t tcl = w_ok ? tw : NT - 1;
+  const uint4* b_src = reinterpret_cast<const uint4*>(packed) + tcl * C * kTileRows + li;
+  const uint16_t* s_src =
+      reinterpret_cast<const uint16_t*>(packed + scale_offset) + tcl * G * kTileRows + li;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // The pipeline of k_gemm_pq2 over steps of 80; an odd chunk count gets a
+  // padding step of zero activations so the two register sets alternate.
+  const int64_t steps = C, steps2 = (C + 1) & ~int64_t(1);
+  uint4 xa[5], ya[5], b0, b1;
+  uint16_t s0[2], s1[2];
+#define BGG_LOAD_A3(KS, R)                                                      \
+  do {                                                                         \
+    const int64_t k_ = (KS) * kBK3 + lh * 40;                                  \
+    const uint4* ap_ = reinterpret_cast<const uint4*>(a_src + (KS) * kBK3);     \
+    _Pragma("unroll") for (int q = 0; q < 5; ++q)                              \
+      R[q] = (KS) < steps && k_ + 8 * q < K ? ap_[q] : make_uint4(0, 0, 0, 0);  \
+  } while (0)
+#define BGG_LOAD_B3(KS)                                                         \
+  do {                                                                         \
+    const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                       \
+    b0 = b_src[kc_ * kTileRows], b1 = b_src[kc_ * kTileRows + 32];             \
+    const int64_t g0_ = (kc_ * kBK3) >> 7;                                      \
+    const int64_t g1_ = g0_ + 1 < G ? g0_ + 1 : G - 1;                          \
+    s0[0] = s_src[g0_ * kTileRows], s1[0] = s_src[g0_ * kTileRows + 32];       \
+    s0[1] = s_src[g1_ * kTileRows], s1[1] = s_src[g1_ * kTileRows + 32];       \
+  } while (0)
+#define BGG_STORE_A3(BUF, R)                                                    \
+  do {                                                                         \
+    uint4* d_ = reinterpret_cast<uint4*>(&As[BUF][lr * kLdsStride3 + lh * 40]); \
+    _Pragma("unroll") for (int q = 0; q < 5; ++q) d_[q] = R[q];                \
+  } while (0)
+#define BGG_STEP3(KS, CUR, L, S)                                                \
+  do {                                                                         \
+    const uint4 bw[2] = {b0, b1};                                              \
+    __half2 s2[2][2];                                                          \
+    _Pragma("unroll") for (int e = 0; e < 2; ++e) {                            \
+      s2[0][e] = __halves2half2(__ushort_as_half(s0[e]), __ushort_as_half(s0[e])); \
+      s2[1][e] = __halves2half2(__ushort_as_half(s1[e]), __ushort_as_half(s1[e])); \
+    }                                                                          \
+    /* the 80 codes of each row as five words of sixteen 2-bit codes; the   \
+       lane keeps the half of each word that its K slice reads (codes     \
+       16 kk + 8 h .. + 7), two halves per register */                     \
+    uint32_t ch[2][3];                                                         \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                            \
+      uint64_t bits_ = 0;                                                      \
+      int nb_ = 0, w_ = 0;                                                     \
+      _Pragma("unroll") for (int q = 0; q < 16; ++q) {                         \
+        const uint32_t word_ = q < 4 ? bw[j].x : q < 8 ? bw[j].y : q < 12 ? bw[j].z : bw[j].w; \
+        bits_ |= (uint64_t)lut[(word_ >> (8 * (q & 3))) & 0xFFu] << nb_;       \
+        nb_ += 10;                                                             \
+        if (nb_ >= 32) {                                                       \
+          const uint32_t half_ = __builtin_amdgcn_ubfe((uint32_t)bits_, 16 * h, 16); \
+          if (w_ % 2 == 0)                                                     \
+            ch[j][w_ / 2] = half_;                                             \
+          else                                                                 \
+            ch[j][w_ / 2] |= half_ << 16;                                      \
+          ++w_;                                                                \
+          bits_ >>= 32;                                                        \
+          nb_ -= 32;                                                           \
+        }                                                                      \
+      }                                                                        \
+    }                                                                          \
+    const int64_t g0s_ = ((KS) < steps ? (KS) : steps - 1) * kBK3 >> 7;        \
+    const int64_t kbase_ = ((KS) < steps ? (KS) : steps - 1) * kBK3;            \
+    BGG_LOAD_A3((KS) + 2, L);                                                  \
+    BGG_LOAD_B3((KS) + 1);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                         \
+    _Pragma("unroll") for (int kk = 0; kk < kBK3 / 16; ++kk) {                 \
+      const int sel_ = ((kbase_ + 16 * kk) >> 7) != g0s_;                      \
+      f16x8 a[4], b[2];                                                        \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) a[i] =                     \
+          *reinterpret_cast<const f16x8*>(                                     \
+              &As[CUR][(i * 32 + li) * kLdsStride3 + kk * 16 + h * 8]);        \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                            \
+          b[j] = decode8_pq2(ch[j][kk / 2] >> (16 * (kk % 2)), sel_ ? s2[j][1] : s2[j][0]); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                            \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =             \
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0); \
+    }                                                                          \
+    BGG_STORE_A3((CUR) ^ 1, S);                                                \
+    __syncthreads();                                                           \
+  } while (0)
+
+  BGG_LOAD_A3(0, xa);
+  BGG_LOAD_B3(0);
+  BGG_STORE_A3(0, xa);
+  BGG_LOAD_A3(1, ya);
+  __syncthreads();  // (also publishes the code table)
+  for (int64_t ks = 0; ks < steps2; ks += 2) {
+    BGG_STEP3(ks, 0, xa, ya);
+    BGG_STEP3(ks + 1, 1, ya, xa);
+  }
+#undef BGG_LOAD_A3
+#undef BGG_LOAD_B3
+#undef BGG_STORE_A3
+#undef BGG_STEP3
+
+  if (!w_ok) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = tw * kTileRows + j * 32 + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        if (m < M && n < N) Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
+      }
+    }
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -172,8 +342,9 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
                             size_t workspace_bytes, void* stream) {
   bgg_status st = bgg::check_desc(d);
   if (st) return st;
-  if (d->format != BGG_FMT_PQ2_0)
-    return fail(BGG_ERR_FORMAT, "bgg_ternary_gemm: only PQ2_0 weights have a prompt-time kernel");
+  if (d->format != BGG_FMT_PQ2_0 && d->format != BGG_FMT_PTQ1_0)
+    return fail(BGG_ERR_FORMAT, "bgg_ternary_gemm: only PQ2_0 and PTQ1_0 weights have a "
+                                "prompt-time kernel");
   if (!packed_dev || !x_dev || !y_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemm: NULL buffer");
   if (M < 1 || M > (int64_t(1) << 31))
     return fail(BGG_ERR_SHAPE, "bgg_ternary_gemm: M must be >= 1 (got %lld)", (long long)M);
@@ -192,9 +363,9 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
     xr = workspace;
   }
   const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(k_gemm_pq2, grid, dim3(256), 0, s, (const uint16_t*)xr,
-                     (const uint8_t*)packed_dev, d->scale_offset, M, d->N, d->K, d->chunks,
-                     d->groups, d->row_tiles, (uint16_t*)y_dev);
+  hipLaunchKernelGGL(d->format == BGG_FMT_PQ2_0 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
+                     (const uint16_t*)xr, (const uint8_t*)packed_dev, d->scale_offset, M, d->N,
+                     d->K, d->chunks, d->groups, d->row_tiles, (uint16_t*)y_dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BGG_ERR_HIP, "bgg_ternary_gemm: %s", hipGetErrorString(e));
   return BGG_OK;

@@ -276,13 +276,17 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* o
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
 
 /*
- * Prompt-time product for any M >= 1 (PQ2_0 only) [A packing paragraph:
- * prompt processing].  Trit tiles are decoded to fp16 s*t (exact) in LDS and
- * multiplied with fp16 x' on the matrix cores, fp32 accumulation, fp16 y.
+ * Prompt-time product for any M >= 1, PQ2_0 and PTQ1_0 [A packing paragraph:
+ * prompt processing, where PQ2_0 is the faster packing].  Trits are decoded
+ * to fp16 s*t (exact) in registers and multiplied with fp16 x' tiles staged
+ * in LDS on the matrix cores, fp32 accumulation, fp16 y.  PTQ1_0's base-3
+ * bytes are first turned into 2-bit codes (an LDS table per byte value).
+ *   x_dev      device fp16 [M][K] (model coordinates with BGG_ROTATE_INPUT,
+ *              else already rotated); y_dev device fp16 [M][N]
  *   workspace  device, bgg_gemm_workspace_size(desc, M) bytes (holds x' when
  *              BGG_ROTATE_INPUT is set; may be NULL when it is not).
- * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (PTQ1_0), BGG_ERR_SHAPE,
- * BGG_ERR_BUFFER, BGG_ERR_HIP.
+ * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (Q1_0, Q2_0_G64),
+ * BGG_ERR_SHAPE, BGG_ERR_BUFFER, BGG_ERR_HIP.
  */
 bgg_status bgg_ternary_gemm(const bgg_weights_desc* desc, const void* packed_dev,
                             const void* x_dev, void* y_dev, int64_t M, uint32_t flags,

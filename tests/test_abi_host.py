@@ -211,7 +211,7 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 24, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
-    dp = bgg.bgg_describe("PTQ1_0", 64, 128)
+    dp = bgg.bgg_describe("Q1_0", 64, 128)   # no prompt-time kernel: rejected before any work
     lib.bgg_ternary_gemm.argtypes = lib.bgg_ternary_gemv.argtypes
     assert lib.bgg_ternary_gemm(ctypes.addressof(dp), 16, 16, 16, 4, 0, None, 0, None) == 2
 

@@ -387,37 +387,61 @@ def test_gemv_workspace_shared_across_shapes(env, fmt):
 # ---------------------------------------------------------------------------
 # prompt GEMM
 # ---------------------------------------------------------------------------
+GEMM_FMTS = ("PQ2_0", "PTQ1_0")
+
+
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (96, 256, 512), (200, 300, 640), (129, 1000, 1152),
-                                   (257, 129, 2048)])
-def test_gemm_parity(env, M, N, K):
+                                   (257, 129, 2048), (64, 70, 384), (130, 513, 5248)])
+def test_gemm_parity(env, fmt, M, N, K):
+    """Ragged M and N tiles; for PTQ1_0 also odd chunk counts (K = 384 and
+    1152: 5 and 15 chunks of 80 trits) and chunks that straddle 128-groups."""
     bgg, torch = env
-    say(f"gemm M={M} N={N} K={K}")
+    say(f"gemm {fmt} M={M} N={N} K={K}")
     T, S = gen_matrix(71, 9, N, K)
     x = synth.activations_f16(71, 10, M, K)
-    d = Dev(bgg, torch, "PQ2_0", T, S)
+    d = Dev(bgg, torch, fmt, T, S)
     y = d.gemm(x)
     assert not np.isnan(y).any()
-    ref = oracle_y("PQ2_0", T, S, x)
+    ref = oracle_y(fmt, T, S, x)
     e = relerr(y, ref)
     say(f"  rel err max {e.max():.3g}")
     assert np.all(e <= TOL)
     # without rotation, given x'
     xr = oracle.rotate(x).astype(np.float16)
     y2 = d.gemm(xr, rotate=False)
-    assert np.all(relerr(y2, oracle_y("PQ2_0", T, S, xr, rotate=False)) <= TOL)
+    assert np.all(relerr(y2, oracle_y(fmt, T, S, xr, rotate=False)) <= TOL)
 
 
+def test_gemm_ptq1_basis_vectors_bit_exact(env):
+    """PTQ1_0 GEMM, rotation off, x = e_k: y_n = S[n][k/128] T[n][k] exactly
+    (one non-zero product per output), at chunk and group edges."""
+    bgg, torch = env
+    N, K = 130, 1152
+    T, S = gen_matrix(45, 2, N, K)
+    d = Dev(bgg, torch, "PTQ1_0", T, S)
+    ks = [0, 1, 79, 80, 127, 128, 159, 160, 639, 640, 1039, 1040, 1119, 1120, 1151]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    y = d.gemm(x, rotate=False)
+    for j, k in enumerate(ks):
+        want = (S[:, k // 128].astype(np.float64) * T[:, k]).astype(np.float16)
+        assert np.array_equal(y[j].view(np.uint16), want.view(np.uint16)), f"k={k}"
+
+
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("name", ["gate_up", "down"])
-def test_gemm_prefill_full_size_sampled(env, name):
+def test_gemm_prefill_full_size_sampled(env, fmt, name):
     """The prefill workload (4096 tokens) at full size; 24 token rows checked
     against the oracle over all N outputs."""
     bgg, torch = env
     w = synth.WORKLOADS["prefill"]
     mat = [m for m in w["matrices"] if m.name == name][0]
-    say(f"gemm full {name} M=4096 N={mat.n} K={mat.k}")
+    say(f"gemm full {fmt} {name} M=4096 N={mat.n} K={mat.k}")
     T, S = synth.workload_matrix(mat, w["seed"])
     x = synth.workload_x(w["seed"], 4096, mat.k)
-    y = Dev(bgg, torch, "PQ2_0", T, S).gemm(x)
+    y = Dev(bgg, torch, fmt, T, S).gemm(x)
     assert not np.isnan(y).any()
     rows = np.array([0, 1, 2, 31, 32, 127, 128, 255, 256, 1000, 2047, 2048, 3000, 4031, 4064, 4095,
                      511, 512, 767, 1023, 1536, 2560, 3583, 3584])
