@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256, 2)
   // The pipeline of k_gemm_pq2 over steps of 80; an odd chunk count gets a
   // padding step of zero activations so the two register sets alternate.
   const int64_t steps = C, steps2 = (C + 1) & ~int64_t(1);
-  uint4 xa[5], ya[5], b0, b1;
+  uint4 xa[5], ya[5], bown;
   uint16_t s0[2], s1[2];
 #define BGG_LOAD_A3(KS, R)                                                      \
   do {                                                                         \
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256, 2)
 #define BGG_LOAD_B3(KS)                                                         \
   do {                                                                         \
     const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                       \
-    b0 = b_src[kc_ * kTileRows], b1 = b_src[kc_ * kTileRows + 32];             \
+    bown = b_src[kc_ * kTileRows + 32 * h];                                    \
     const int64_t g0_ = (kc_ * kBK3) >> 7;                                      \
     const int64_t g1_ = g0_ + 1 < G ? g0_ + 1 : G - 1;                          \
     s0[0] = s_src[g0_ * kTileRows], s1[0] = s_src[g0_ * kTileRows + 32];       \
@@ -248,34 +248,48 @@ __global__ void __launch_bounds__(256, 2)
   } while (0)
 #define BGG_STEP3(KS, CUR, L, S)                                                \
   do {                                                                         \
-    const uint4 bw[2] = {b0, b1};                                              \
+    const uint4 bw = bown;                                                     \
     __half2 s2[2][2];                                                          \
     _Pragma("unroll") for (int e = 0; e < 2; ++e) {                            \
       s2[0][e] = __halves2half2(__ushort_as_half(s0[e]), __ushort_as_half(s0[e])); \
       s2[1][e] = __halves2half2(__ushort_as_half(s1[e]), __ushort_as_half(s1[e])); \
     }                                                                          \
-    /* the 80 codes of each row as five words of sixteen 2-bit codes; the   \
-       lane keeps the half of each word that its K slice reads (codes     \
-       16 kk + 8 h .. + 7), two halves per register */                     \
-    uint32_t ch[2][3];                                                         \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                            \
+    /* lane (li, h) turns the chunk of its own row 32 h + li into the 80     \
+       codes (five words of sixteen 2-bit codes), keeps the halves its K   \
+       slices read (codes 16 kk + 8 h .. + 7) and hands the other halves    \
+       to lane (li, 1 - h), which reads the same slices of the other half   \
+       of K for this row; two halves per register */                        \
+    uint32_t mine[3], theirs[3];                                               \
+    {                                                                          \
       uint64_t bits_ = 0;                                                      \
       int nb_ = 0, w_ = 0;                                                     \
       _Pragma("unroll") for (int q = 0; q < 16; ++q) {                         \
-        const uint32_t word_ = q < 4 ? bw[j].x : q < 8 ? bw[j].y : q < 12 ? bw[j].z : bw[j].w; \
+        const uint32_t word_ = q < 4 ? bw.x : q < 8 ? bw.y : q < 12 ? bw.z : bw.w; \
         bits_ |= (uint64_t)lut[(word_ >> (8 * (q & 3))) & 0xFFu] << nb_;       \
         nb_ += 10;                                                             \
         if (nb_ >= 32) {                                                       \
-          const uint32_t half_ = __builtin_amdgcn_ubfe((uint32_t)bits_, 16 * h, 16); \
-          if (w_ % 2 == 0)                                                     \
-            ch[j][w_ / 2] = half_;                                             \
-          else                                                                 \
-            ch[j][w_ / 2] |= half_ << 16;                                      \
+          const uint32_t cw_ = (uint32_t)bits_;                                \
+          const uint32_t my_ = __builtin_amdgcn_ubfe(cw_, 16 * h, 16);         \
+          const uint32_t ot_ = __builtin_amdgcn_ubfe(cw_, 16 - 16 * h, 16);    \
+          if (w_ % 2 == 0) {                                                   \
+            mine[w_ / 2] = my_;                                                \
+            theirs[w_ / 2] = ot_;                                              \
+          } else {                                                             \
+            mine[w_ / 2] |= my_ << 16;                                         \
+            theirs[w_ / 2] |= ot_ << 16;                                       \
+          }                                                                    \
           ++w_;                                                                \
           bits_ >>= 32;                                                        \
           nb_ -= 32;                                                           \
         }                                                                      \
       }                                                                        \
+    }                                                                          \
+    uint32_t ch[2][3];                                                         \
+    _Pragma("unroll") for (int r_ = 0; r_ < 3; ++r_) {                         \
+      const uint32_t got_ = (uint32_t)__builtin_amdgcn_ds_bpermute(            \
+          (lane ^ 32) * 4, (int)theirs[r_]);                                   \
+      ch[0][r_] = h ? got_ : mine[r_];                                         \
+      ch[1][r_] = h ? mine[r_] : got_;                                         \
     }                                                                          \
     const int64_t g0s_ = ((KS) < steps ? (KS) : steps - 1) * kBK3 >> 7;        \
     const int64_t kbase_ = ((KS) < steps ? (KS) : steps - 1) * kBK3;            \
@@ -362,10 +376,17 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
     if ((st = bgg_hadamard_rotate(x_dev, workspace, M, d->K, stream))) return st;
     xr = workspace;
   }
-  const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(d->format == BGG_FMT_PQ2_0 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
-                     (const uint16_t*)xr, (const uint8_t*)packed_dev, d->scale_offset, M, d->N,
-                     d->K, d->chunks, d->groups, d->row_tiles, (uint16_t*)y_dev);
+  // token blocks go on grid.y, which holds at most 65535 blocks: longer
+  // prompts run as several launches over consecutive token ranges
+  const int64_t max_m = int64_t(65535) * kBM;
+  for (int64_t m0 = 0; m0 < M; m0 += max_m) {
+    const int64_t mc = M - m0 < max_m ? M - m0 : max_m;
+    const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM));
+    hipLaunchKernelGGL(d->format == BGG_FMT_PQ2_0 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
+                       (const uint16_t*)xr + m0 * d->K, (const uint8_t*)packed_dev,
+                       d->scale_offset, mc, d->N, d->K, d->chunks, d->groups, d->row_tiles,
+                       (uint16_t*)y_dev + m0 * d->N);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BGG_ERR_HIP, "bgg_ternary_gemm: %s", hipGetErrorString(e));
   return BGG_OK;
