@@ -222,12 +222,14 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * Arithmetic.  The activations are carried as 15-bit integers q with a
  * power-of-two scale per 128-block (absolute error at most 2^-14 of the
  * block's largest |x'|); each group's trit sum p = sum t q is exact, and is
- * scaled and accumulated in fp32 in a fixed order.  One token: one
- * pass over the weights on the vector ALUs.  2..16 tokens: one pass for all
- * of them on the matrix cores, with the same sums and fp32 steps, so a
- * token's y does not depend on the other tokens or on M (PTQ1_0 at M == 1
- * may split a 640-weight period between two waves, whose partial sums then
- * round differently in the last bits).
+ * scaled and accumulated in fp32 in a fixed order.  PQ2_0 and PTQ1_0, one
+ * token: one pass over the weights on the vector ALUs.  2..16 tokens (and
+ * every token count of Q1_0 and Q2_0_G64): one pass for all of them on the
+ * matrix cores, with the same sums and fp32 steps, so a token's y does not
+ * depend on the other tokens or on M (PTQ1_0 at M == 1 may split a
+ * 640-weight period between two waves, whose partial sums then round
+ * differently in the last bits).  Q2_0_G64 scales each 64-weight half of a
+ * group by its own scale (two exact half sums).
  * Where K is split over workgroups their partial rows are added as 64-bit
  * fixed-point integers (resolution 2^-30, magnitude below 2^19), whose sum
  * does not depend on the order.  y is rounded to fp16 once, and the same
