@@ -211,6 +211,16 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 24, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
+    # the offline front end: NULL, shape and alignment errors before any work
+    lib.bgg_rotate_ternarize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.bgg_rotate_ternarize(None, 4, 128, 16, 16, None) == 1
+    assert lib.bgg_rotate_ternarize(16, 4, 100, 16, 16, None) == 3
+    assert lib.bgg_rotate_ternarize(16, -1, 128, 16, 16, None) == 3
+    assert lib.bgg_rotate_ternarize(24, 4, 128, 16, 16, None) == 6
+    assert lib.bgg_rotate_ternarize(16, 4, 128, 12, 16, None) == 6
+    assert lib.bgg_rotate_ternarize(16, 4, 128, 16, 17, None) == 6
+    assert lib.bgg_rotate_ternarize(16, 0, 128, 16, 16, None) == 0   # N == 0: nothing to do
     dp = bgg.bgg_describe("Q1_0", 64, 128)   # no prompt-time kernel: rejected before any work
     lib.bgg_ternary_gemm.argtypes = lib.bgg_ternary_gemv.argtypes
     assert lib.bgg_ternary_gemm(ctypes.addressof(dp), 16, 16, 16, 4, 0, None, 0, None) == 2

@@ -451,6 +451,46 @@ def test_gemm_prefill_full_size_sampled(env, fmt, name):
     assert np.all(e <= TOL)
 
 
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
+def test_gemm_graph_replay_matches_eager(env, fmt):
+    """Transform + GEMM captured in a HIP graph: every replay, with eager work
+    on the same workspace between replays, gives the eager bits (no memset
+    nodes: the transform writes the whole workspace it reads)."""
+    bgg, torch = env
+    M, N, K = 300, 1000, 1152
+    say(f"gemm graph replay {fmt}")
+    T, S = gen_matrix(97, 2, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    x = torch.from_numpy(synth.activations_f16(97, 3, M, K)).cuda()
+    x_other = torch.from_numpy(synth.activations_f16(97, 4, M, K)).cuda()
+    ws = bgg.workspace(bgg.bgg_gemm_workspace_size(d.desc, M))
+    y_eager = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    bgg.bgg_ternary_gemm(d.desc, d.packed, x, y_eager, M, bgg.BGG_ROTATE_INPUT, ws)
+    torch.cuda.synchronize()
+    want = y_eager.cpu().numpy()
+    assert np.all(relerr(want, oracle_y(fmt, T, S, x.cpu().numpy())) <= TOL)
+    y_graph = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bgg.bgg_ternary_gemm(d.desc, d.packed, x, y_graph, M, bgg.BGG_ROTATE_INPUT, ws, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bgg.bgg_ternary_gemm(d.desc, d.packed, x, y_graph, M, bgg.BGG_ROTATE_INPUT, ws,
+                             torch.cuda.current_stream())
+    y_other = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    for rep in range(4):
+        y_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y_graph.cpu().numpy().view(np.uint16), want.view(np.uint16)), \
+            f"replay {rep}"
+        bgg.bgg_ternary_gemm(d.desc, d.packed, x_other, y_other, M, bgg.BGG_ROTATE_INPUT, ws)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_shared_preparation(env, fmt):
     """q, k and v read the same input: one prepare, three runs."""
