@@ -490,13 +490,15 @@ def main() -> int:
                 x = torch.from_numpy(synth.workload_x(pw["seed"], M, mat.k)).to(dev)
                 xr = torch.empty_like(x)
                 y = torch.empty((M, mat.n), dtype=torch.float16, device=dev)
+                # (the workspace holds the partial sums where the GEMM splits K)
+                wsg = bgg.workspace(bgg.bgg_gemm_workspace_size(d, M), dev)
                 # warm-up long enough (tens of ms of matrix work) for the clocks
                 # to settle: the first launches after the GEMV part run up to
                 # 25 % slower than the steady state
                 reps = 10
                 for _ in range(args.gemm_warmup):
                     bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
-                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, wsg, stream)
                 torch.cuda.synchronize()
                 e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                       torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -504,7 +506,7 @@ def main() -> int:
                     e[r][0].record(stream)
                     bgg.bgg_hadamard_rotate(x, xr, M, mat.k, stream)
                     e[r][1].record(stream)
-                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, None, stream)
+                    bgg.bgg_ternary_gemm(d, packed, xr, y, M, 0, wsg, stream)
                     e[r][2].record(stream)
                 torch.cuda.synchronize()
                 f_us = float(np.mean([a.elapsed_time(b) for a, b, _ in e])) * 1e3
@@ -519,7 +521,7 @@ def main() -> int:
                                      gbs=round(fbytes / f_us / 1e3, 1)))
                 else:
                     ptq1.append(row)
-                del T, S, packed, x, xr, y
+                del T, S, packed, x, xr, y, wsg
         tot_flops = sum(2.0 * s["m"] * s["n"] * s["k"] for s in shapes)
         tot_us = sum(s["avg_us"] for s in shapes)
         tf = tot_flops / tot_us / 1e6

@@ -25,12 +25,16 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <cstdlib>
+
 #include "bgg_device.h"
 
 using bgg::fail;
 using bgg::f16x8;
 using bgg::f32x16;
 using bgg::decode8_pq2;
+using bgg::ceil_div;
 
 namespace {
 
@@ -38,10 +42,13 @@ constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // halves per LDS row (+16 bytes against bank conflicts)
 constexpr int kTileRows = BGG_ROW_TILE;
 
+// K split (gridDim.z == 2): workgroup z runs K steps [0, kmid) or [kmid,
+// steps) and writes fp32 partial sums to P[z][M][N]; k_gemm_sum2 adds the two
+// and rounds to fp16.  gridDim.z == 1: all of K, fp16 y.
 __global__ void __launch_bounds__(256, 2)
     k_gemm_pq2(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
                uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
-               int64_t NT, uint16_t* __restrict__ Y) {
+               int64_t NT, int64_t kmid, float* __restrict__ P, uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -80,7 +87,9 @@ __global__ void __launch_bounds__(256, 2)
   // last step re-read the last step (no branch splits the registers), and
   // the two activation register sets alternate, so the loop is unrolled by
   // two (K / 64 is even since K is a multiple of 128).
-  const int64_t steps = K / kBK;
+  // this workgroup's K steps [kb, steps): both ranges have even lengths
+  const int64_t kb = blockIdx.z == 0 ? 0 : kmid;
+  const int64_t steps = gridDim.z == 1 || blockIdx.z == 1 ? K / kBK : kmid;
   uint4 xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3, b0, b1;
   uint16_t s0, s1;
 #define BGG_LOAD_A(KS, R0, R1, R2, R3)                                       \
@@ -127,12 +136,12 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();                                                         \
   } while (0)
 
-  BGG_LOAD_A(0, xa0, xa1, xa2, xa3);
-  BGG_LOAD_B(0);
+  BGG_LOAD_A(kb, xa0, xa1, xa2, xa3);
+  BGG_LOAD_B(kb);
   BGG_STORE_A(0, xa0, xa1, xa2, xa3);
-  BGG_LOAD_A(1, ya0, ya1, ya2, ya3);
+  BGG_LOAD_A(kb + 1, ya0, ya1, ya2, ya3);
   __syncthreads();
-  for (int64_t ks = 0; ks < steps; ks += 2) {
+  for (int64_t ks = kb; ks < steps; ks += 2) {
     BGG_STEP(ks, 0, xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3);
     BGG_STEP(ks + 1, 1, ya0, ya1, ya2, ya3, xa0, xa1, xa2, xa3);
   }
@@ -152,9 +161,40 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-        if (m < M && n < N) Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
+        if (m < M && n < N) {
+          if (gridDim.z > 1)
+            P[(blockIdx.z * M + m) * N + n] = acc[i][j][r];
+          else
+            Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
+        }
       }
     }
+}
+
+// y = fp16(P[0] + P[1]) over M*N values, four per thread (16-byte loads
+// when M*N is a multiple of 4, so that the second partial is aligned too;
+// else, and for the tail, one by one).
+__global__ void __launch_bounds__(256) k_gemm_sum2(const float* __restrict__ P, int64_t MN,
+                                                   uint16_t* __restrict__ Y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  if (i + 4 <= MN && (MN & 3) == 0) {
+    const float4 a = *reinterpret_cast<const float4*>(P + i);
+    const float4 b = *reinterpret_cast<const float4*>(P + MN + i);
+    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(a.x + b.x)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(a.y + b.y)) << 16);
+    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(a.z + b.z)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(a.w + b.w)) << 16);
+    if (((uintptr_t)(Y + i) & 7) == 0) {
+      *reinterpret_cast<uint2*>(Y + i) = make_uint2(lo, hi);
+    } else {
+      Y[i] = (uint16_t)lo, Y[i + 1] = (uint16_t)(lo >> 16);
+      Y[i + 2] = (uint16_t)hi, Y[i + 3] = (uint16_t)(hi >> 16);
+    }
+  } else {
+    const int64_t e = i + 4 < MN ? i + 4 : MN;
+    for (int64_t k = i; k < e; ++k) Y[k] = __half_as_ushort(__float2half_rn(P[k] + P[MN + k]));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -175,7 +215,7 @@ constexpr int kLdsStride3 = kBK3 + 8;  // halves per LDS row (176 bytes)
 __global__ void __launch_bounds__(256, 2)
     k_gemm_ptq1(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
                 uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
-                int64_t NT, uint16_t* __restrict__ Y) {
+                int64_t NT, int64_t kmid, float* __restrict__ P, uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride3];
   __shared__ uint32_t lut[256];
 
@@ -222,7 +262,11 @@ __global__ void __launch_bounds__(256, 2)
 
   // The pipeline of k_gemm_pq2 over steps of 80; an odd chunk count gets a
   // padding step of zero activations so the two register sets alternate.
-  const int64_t steps = C, steps2 = (C + 1) & ~int64_t(1);
+  // this workgroup's chunks [kb, steps) (the K split as in k_gemm_pq2),
+  // padded to an even count with zero activations
+  const int64_t kb = blockIdx.z == 0 ? 0 : kmid;
+  const int64_t steps = gridDim.z == 1 || blockIdx.z == 1 ? C : kmid;
+  const int64_t steps2 = kb + ((steps - kb + 1) & ~int64_t(1));
   uint4 xa[5], ya[5], bown;
   uint16_t s0[2], s1[2];
 #define BGG_LOAD_A3(KS, R)                                                      \
@@ -312,12 +356,12 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();                                                           \
   } while (0)
 
-  BGG_LOAD_A3(0, xa);
-  BGG_LOAD_B3(0);
+  BGG_LOAD_A3(kb, xa);
+  BGG_LOAD_B3(kb);
   BGG_STORE_A3(0, xa);
-  BGG_LOAD_A3(1, ya);
+  BGG_LOAD_A3(kb + 1, ya);
   __syncthreads();  // (also publishes the code table)
-  for (int64_t ks = 0; ks < steps2; ks += 2) {
+  for (int64_t ks = kb; ks < steps2; ks += 2) {
     BGG_STEP3(ks, 0, xa, ya);
     BGG_STEP3(ks + 1, 1, ya, xa);
   }
@@ -335,12 +379,61 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-        if (m < M && n < N) Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
+        if (m < M && n < N) {
+          if (gridDim.z > 1)
+            P[(blockIdx.z * M + m) * N + n] = acc[i][j][r];
+          else
+            Y[m * N + n] = __half_as_ushort(__float2half_rn(acc[i][j][r]));
+        }
       }
     }
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device (cached per device).
+int64_t gemm_device_cus() {
+  static int64_t cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// K split in two when the output blocks fill the resident workgroup slots
+// (two per CU) much less evenly than twice as many would: the last, partly
+// empty round of workgroups (e.g. 640 blocks on 512 slots for 4096 tokens x
+// 5120 rows) costs as much as a full one.  The fp32 partials cost an extra
+// pass over 2 M N floats, so the split must gain at least 15 %.
+bool gemm_split(const bgg_weights_desc* d, int64_t M) {
+  static const int64_t on = [] {
+    const char* e = getenv("BGG_GEMM_SPLIT");
+    return e && *e ? (int64_t)atoll(e) : int64_t(1);
+  }();
+  if (!on) return false;
+  const int64_t steps = d->format == BGG_FMT_PQ2_0 ? d->K / kBK : d->chunks;
+  if (steps < 8) return false;
+  const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
+  const double wgs = (double)((d->N + kBN - 1) / kBN) * (double)((mc + kBM - 1) / kBM);
+  const double waves = wgs / (double)(2 * gemm_device_cus());
+  const double eff1 = waves / std::ceil(waves), eff2 = 2 * waves / std::ceil(2 * waves);
+  return eff2 > 1.15 * eff1;
+}
+
+uint64_t gemm_rot_bytes(const bgg_weights_desc* d, int64_t M) {
+  return ((uint64_t)M * d->K * 2 + 255) & ~uint64_t(255);
+}
+
+// fp32 partials of one launch (at most 65535 token blocks)
+uint64_t gemm_part_bytes(const bgg_weights_desc* d, int64_t M) {
+  const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
+  return (uint64_t)2 * mc * d->N * 4;
+}
 
 }  // namespace
 
@@ -348,7 +441,7 @@ extern "C" {
 
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* d, int64_t M) {
   if (bgg::check_desc(d) != BGG_OK || M < 1) return 0;
-  return (size_t)(((uint64_t)M * d->K * 2 + 255) & ~uint64_t(255));
+  return (size_t)(gemm_rot_bytes(d, M) + (gemm_split(d, M) ? gemm_part_bytes(d, M) : 0));
 }
 
 bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, const void* x_dev,
@@ -366,26 +459,43 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
     return fail(BGG_ERR_SHAPE, "bgg_ternary_gemm: unknown flags 0x%x", flags);
   if (!aligned16(packed_dev) || !aligned16(x_dev) || ((uintptr_t)y_dev & 1))
     return fail(BGG_ERR_BUFFER, "bgg_ternary_gemm: misaligned buffer");
+  if (workspace && !aligned16(workspace))
+    return fail(BGG_ERR_BUFFER, "bgg_ternary_gemm: misaligned workspace");
   hipStream_t s = (hipStream_t)stream;
   const void* xr = x_dev;
+  uint64_t used = 0;
   if (flags & BGG_ROTATE_INPUT) {
-    const size_t need = bgg_gemm_workspace_size(d, M);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    const uint64_t need = gemm_rot_bytes(d, M);
+    if (!workspace || workspace_bytes < need)
       return fail(BGG_ERR_BUFFER, "bgg_ternary_gemm: rotation needs a 16-byte aligned workspace "
-                                  "of %zu bytes", need);
+                                  "of %llu bytes", (unsigned long long)need);
     if ((st = bgg_hadamard_rotate(x_dev, workspace, M, d->K, stream))) return st;
     xr = workspace;
+    used = need;
   }
+  // the K split runs only when the workspace also holds its partials
+  float* P = nullptr;
+  if (workspace && gemm_split(d, M) && workspace_bytes >= used + gemm_part_bytes(d, M))
+    P = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + used);
+  const int64_t steps = d->format == BGG_FMT_PQ2_0 ? d->K / kBK : d->chunks;
+  const int64_t kmid = (steps / 2) & ~int64_t(1);  // even: both halves stay even
   // token blocks go on grid.y, which holds at most 65535 blocks: longer
   // prompts run as several launches over consecutive token ranges
   const int64_t max_m = int64_t(65535) * kBM;
   for (int64_t m0 = 0; m0 < M; m0 += max_m) {
     const int64_t mc = M - m0 < max_m ? M - m0 : max_m;
-    const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM));
+    const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM),
+                    P ? 2u : 1u);
+    uint16_t* y = (uint16_t*)y_dev + m0 * d->N;
     hipLaunchKernelGGL(d->format == BGG_FMT_PQ2_0 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
                        (const uint16_t*)xr + m0 * d->K, (const uint8_t*)packed_dev,
-                       d->scale_offset, mc, d->N, d->K, d->chunks, d->groups, d->row_tiles,
-                       (uint16_t*)y_dev + m0 * d->N);
+                       d->scale_offset, mc, d->N, d->K, d->chunks, d->groups, d->row_tiles, kmid,
+                       P, y);
+    if (P) {
+      const int64_t mn = mc * d->N;
+      hipLaunchKernelGGL(k_gemm_sum2, dim3((unsigned)ceil_div(ceil_div(mn, 4), 256)), dim3(256), 0,
+                         s, (const float*)P, mn, y);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BGG_ERR_HIP, "bgg_ternary_gemm: %s", hipGetErrorString(e));

@@ -274,7 +274,8 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);
 
-/* Device workspace bytes that bgg_ternary_gemm needs for M tokens. */
+/* Device workspace bytes that bgg_ternary_gemm uses at most for M tokens
+ * (0 on a bad descriptor or M < 1). */
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
 
 /*
@@ -285,8 +286,13 @@ size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * bytes are first turned into 2-bit codes (an LDS table per byte value).
  *   x_dev      device fp16 [M][K] (model coordinates with BGG_ROTATE_INPUT,
  *              else already rotated); y_dev device fp16 [M][N]
- *   workspace  device, bgg_gemm_workspace_size(desc, M) bytes (holds x' when
- *              BGG_ROTATE_INPUT is set; may be NULL when it is not).
+ *   workspace  device, 16-byte aligned, bgg_gemm_workspace_size(desc, M)
+ *              bytes: x' when BGG_ROTATE_INPUT is set, then, for shapes whose
+ *              output blocks fill the GPU unevenly (few output rows, long K),
+ *              the fp32 partial sums of a K split in two.  Smaller (down to
+ *              x' only, or NULL without BGG_ROTATE_INPUT) runs without the
+ *              split, whose last-bit rounding differs; each choice gives
+ *              bit-identical y for the same inputs.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (Q1_0, Q2_0_G64),
  * BGG_ERR_SHAPE, BGG_ERR_BUFFER, BGG_ERR_HIP.
  */
