@@ -145,25 +145,28 @@ def decode_stack_bench(args, bgg, torch, dev, capture):
                                  tflops=round(2.0 * M * weights / us / 1e6, 2))
             log(f"  M={M}: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
 
-        # M = 1 with the transform shared as a model would share it
+        # the transform shared as a model would share it: one prepare for
+        # q, k and v, one for o, one for gate and up, one for down, each
+        # followed by a run per matrix
         groups = []  # (input width, [calls])
         for i in range(0, len(calls), 7):
             layer = calls[i:i + 7]
             groups += [layer[0:3], layer[3:4], layer[4:6], layer[6:7]]
-
-        def step_shared(st):
-            for grp in groups:
-                m0, d0, _ = grp[0]
-                bgg.bgg_gemv_prepare(d0, xs[m0.k][:1], 1, bgg.BGG_ROTATE_INPUT, ws, st)
-                for m, d, p in grp:
-                    bgg.bgg_gemv_run(d, p, ys[m.n][:1], 1, ws, st)
-        g = capture(step_shared)
-        us = median_replay_us(g, args.stack_replays)
-        del g
-        shared = dict(us_per_step=round(us, 1), gbs=round(step_bytes / us / 1e3, 1),
-                      frac=round(step_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                      launches=len(groups) + len(calls))
-        log(f"  M=1 shared transform: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
+        shared = dict(launches=len(groups) + len(calls), per_m={})
+        for M in ms:
+            def step_shared(st, M=M):
+                for grp in groups:
+                    m0, d0, _ = grp[0]
+                    bgg.bgg_gemv_prepare(d0, xs[m0.k][:M], M, bgg.BGG_ROTATE_INPUT, ws, st)
+                    for m, d, p in grp:
+                        bgg.bgg_gemv_run(d, p, ys[m.n][:M], M, ws, st)
+            g = capture(step_shared)
+            us = median_replay_us(g, args.stack_replays)
+            del g
+            shared["per_m"][str(M)] = dict(us_per_step=round(us, 1),
+                                           gbs=round(step_bytes / us / 1e3, 1),
+                                           frac=round(step_bytes / us / 1e3 / HBM_PEAK_GBS, 4))
+            log(f"  M={M} shared transform: {us:.0f} us per step, {step_bytes / us / 1e3:.0f} GB/s")
         del calls
         torch.cuda.empty_cache()
 
@@ -203,7 +206,7 @@ def decode_stack_bench(args, bgg, torch, dev, capture):
             grouped[str(M)] = dict(us_per_step=round(us, 1), gbs=round(gbytes / us / 1e3, 1),
                                    frac=round(gbytes / us / 1e3 / HBM_PEAK_GBS, 4))
             log(f"  grouped M={M}: {us:.0f} us per step, {gbytes / us / 1e3:.0f} GB/s")
-        res["formats"][fmt] = dict(packed_bytes=step_bytes, per_m=per_m, m1_shared_transform=shared,
+        res["formats"][fmt] = dict(packed_bytes=step_bytes, per_m=per_m, shared_transform=shared,
                                    grouped=dict(packed_bytes=gbytes, launches=len(gcalls),
                                                 per_m=grouped))
         del gcalls, gys, ws
