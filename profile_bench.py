@@ -51,7 +51,7 @@ def kernels(stats_csv: str, out_md: str, command: str) -> None:
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
     lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             "Command (repository root of a GPU box, one MI355X):", "", "```", command, "```", "",
+             "Command (run from the repository root, one MI355X):", "", "```", command, "```", "",
              "| kernel | calls | average us | min us | max us | share |",
              "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
