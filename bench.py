@@ -330,7 +330,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the path has no multi-GPU part", file=sys.stderr)
         return 2
 
