@@ -267,9 +267,10 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
  * calls).  The last template argument is true for the one-launch kernel
  * that also encodes the activations (M == 1) and false for the kernel that
  * reads a preparation (bgg_gemv_run launches that one, with the same other
- * arguments).  2..16 tokens name the matrix-core kernel, e.g.
- * "k_gemv_pq2_mx<5, 8>" or "k_gemv_ptq1_mx<8>", which covers all M tokens
- * in one launch.
+ * arguments).  2..16 tokens (every M for Q1_0 and Q2_0_G64) name the
+ * matrix-core kernel, e.g. "k_gemv_pq2_mx<5, 8>", "k_gemv_ptq1_mx<8>",
+ * "k_gemv_q1_mx<5, 8>" or "k_gemv_q2g64_mx<4, 8>", which covers all M
+ * tokens in one launch after the preparation kernel "k_gemv_prep_mx<...>".
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);
