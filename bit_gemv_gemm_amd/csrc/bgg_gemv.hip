@@ -1299,7 +1299,7 @@ __global__ void __launch_bounds__(64)
                    uint32_t* __restrict__ xa, uint32_t* __restrict__ xs, float* __restrict__ xc,
                    float* __restrict__ xh) {
   // the e4m3 bytes of every digit, slot and group position
-  __shared__ uint8_t dig[kMxDigits][kPrepMxSlots][kGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kMxDigits][kPrepMxSlots][kGroup];
   const int64_t blk = blockIdx.x;
   const int ts = threadIdx.x >> 4, l16 = threadIdx.x & 15;
   const int t = (int)blockIdx.y * kPrepMxSlots + ts;
@@ -1355,17 +1355,24 @@ __global__ void __launch_bounds__(64)
   // this block's words: 3 digits x 4 lane groups x 4 slots x 8 words; word
   // dd of lane (slot tt, lane group ga) holds A bytes e = 4 dd .. 4 dd + 3,
   // i.e. the digits at the group positions that the B nibbles of those K
-  // carry
+  // carry.  Those four K are consecutive from K0 = mx_k_of_a(ga, 4 dd), a
+  // multiple of 4: in natural order four consecutive bytes (one 32-bit
+  // read); in PQ2_0 order the positions p0, p0 + 2, p0 + 4, p0 + 6 with p0
+  // = mx_pos_of_k(K0), all in the 8-byte block at p0 & ~7 (p0 % 8 is 0 or
+  // 1): one 64-bit read and a byte select.
 #pragma unroll
   for (int it0 = 0; it0 < kMxDigits * 4 * kPrepMxSlots * 8; it0 += 64) {
     const int it = it0 + threadIdx.x;
     const int k = it >> 7, ga = (it >> 5) & 3, tl = (it >> 3) & 3, dd = it & 7;
     const uint8_t* row = dig[k][tl];
-    uint32_t word = 0;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int kk = mx_k_of_a(ga, 4 * dd + bb);
-      word |= (uint32_t)row[NATURAL ? kk : mx_pos_of_k(kk)] << (8 * bb);
+    const int k0 = mx_k_of_a(ga, 4 * dd);
+    uint32_t word;
+    if (NATURAL) {
+      word = *reinterpret_cast<const uint32_t*>(row + k0);
+    } else {
+      const int p0 = mx_pos_of_k(k0);
+      const uint2 blk8 = *reinterpret_cast<const uint2*>(row + (p0 & ~7));
+      word = __builtin_amdgcn_perm(blk8.y, blk8.x, 0x06040200u + (uint32_t)(p0 & 1) * 0x01010101u);
     }
     const int l = 16 * ga + (int)blockIdx.y * kPrepMxSlots + tl;
     xa[((blk * kMxDigits + k) * 64 + l) * 8 + dd] = word;
