@@ -232,4 +232,15 @@ inline bgg_status hip_check(const char* what) {
   return BGG_OK;
 }
 
+// The matrix-core GEMV of bgg_mxv.hip (PQ2_0, 1..4 tokens, one launch that
+// also transforms x): whether it serves (format, M), the workspace bytes it
+// uses at the start of a GEMV workspace (row words that every launch leaves
+// zero), the name of the kernel it launches (snprintf's return), and the
+// launch.
+bool mxv_supported(const bgg_weights_desc* d, int64_t M);
+uint64_t mxv_workspace_bytes();
+int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap);
+bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void* x, void* y,
+                      int64_t M, int rotate, void* workspace, hipStream_t st);
+
 }  // namespace bgg

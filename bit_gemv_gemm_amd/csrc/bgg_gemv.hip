@@ -1508,7 +1508,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   frag_bytes = std::max<uint64_t>(frag_bytes, (uint64_t)p.G * kMxDigits * 64 * 32);
   meta_q_bytes = std::max<uint64_t>(meta_q_bytes, (uint64_t)p.G * kMmaSlots * 16);
   p.off_sums = 0;
-  p.off_frag = kSumBytes;
+  p.off_frag = std::max<uint64_t>(kSumBytes, mxv_workspace_bytes());
   uint64_t off = align256(p.off_frag + frag_bytes);
   p.off_meta_q = off;
   off = align256(off + meta_q_bytes);
@@ -1710,7 +1710,9 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
   const char* fused =
       M == 1 && gemv_fuse_enabled(d->format) && !p.mma ? "true" : "false";
   int n;
-  if (p.mma && d->format == BGG_FMT_PTQ1_0) {
+  if (mxv_supported(d, M)) {
+    n = mxv_kernel_name(d, M, out, cap);
+  } else if (p.mma && d->format == BGG_FMT_PTQ1_0) {
     n = snprintf(out, cap, "k_gemv_ptq1_mx<8>");
   } else if (p.mma) {
     const char* kn = d->format == BGG_FMT_Q1_0       ? "k_gemv_q1_mx"
@@ -1778,6 +1780,17 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
   if (!packed_dev || !y_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemv: NULL buffer");
   if (!aligned16(packed_dev) || ((uintptr_t)y_dev & 1))
     return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned buffer");
+  if (mxv_supported(d, M)) {
+    GemvPlan p;
+    st = gemv_args_check("bgg_ternary_gemv", d, M, workspace, workspace_bytes, &p);
+    if (st) return st;
+    if (!x_dev) return fail(BGG_ERR_NULL, "bgg_ternary_gemv: NULL x");
+    if (!aligned16(x_dev)) return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned x");
+    if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
+      return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: unknown flags 0x%x", flags);
+    return mxv_launch(d, packed_dev, x_dev, y_dev, M, (flags & BGG_ROTATE_INPUT) ? 1 : 0, workspace,
+                      (hipStream_t)stream);
+  }
   // (the one-launch kernel wants the digit words of a block or period to
   // fill whole 64-byte lines: a workspace aligned to 64 bytes)
   if (M != 1 || !gemv_fuse_enabled(d->format) || ((uintptr_t)workspace & 63) ||

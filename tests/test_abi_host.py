@@ -206,9 +206,10 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_hadamard_rotate(None, None, 1, 128, None) == 1
     # shape errors are reported before any device work
     assert lib.bgg_hadamard_rotate(16, 16, 1, 100, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 0, 1, 16, 1 << 24, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, 1 << 24, None) == 3
-    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, 1 << 24, None) == 3
+    wsz = bgg.bgg_gemv_workspace_size(d, 16)
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 0, 1, 16, wsz, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, wsz, None) == 3
+    assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, wsz, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
     # the offline front end: NULL, shape and alignment errors before any work

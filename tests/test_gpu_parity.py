@@ -174,32 +174,42 @@ def test_gemv_projection_full_size(env, fmt, name):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (300, 640), (100, 1152), (64, 128)])
-def test_gemv_one_launch_matches_two_step(env, fmt, N, K):
+def test_gemv_one_launch_and_two_step(env, fmt, N, K):
     """For one token bgg_ternary_gemv runs a single kernel that also encodes
-    x; it must give the bits of bgg_gemv_prepare + bgg_gemv_run, call after
-    call on one workspace with a different x each time (no call may read
-    another call's encoded activations), with and without the transform."""
+    x; bgg_gemv_prepare + bgg_gemv_run is the two-step form.  Call after call
+    on one workspace with a different x each time (no call may read another
+    call's encoded activations or row sums), with and without the transform:
+    both forms agree with the oracle (every row where the oracle is cheap,
+    else 48 sampled rows), each form gives the same bits when repeated, and
+    where both forms run the same kernels (PTQ1_0) their bits agree."""
     bgg, torch = env
-    say(f"gemv one-launch vs two-step {fmt} {N}x{K}")
+    say(f"gemv one-launch and two-step {fmt} {N}x{K}")
     T, S = gen_matrix(71, 9, N, K)
     d = Dev(bgg, torch, fmt, T, S)
-    assert bgg.bgg_gemv_kernel_name(d.desc, 1).endswith("true>")
     ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 1))
+    rows = np.arange(N) if N * K <= 1 << 20 else np.random.default_rng(7).choice(N, 48, replace=False)
     for i in range(4):
         flags = bgg.BGG_ROTATE_INPUT if i != 2 else 0
         x = synth.activations_f16(71, 10 + i, 1, K)
         xd = torch.from_numpy(x).cuda()
-        y1 = torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda")
-        y2 = torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda")
-        bgg.bgg_ternary_gemv(d.desc, d.packed, xd, y1, 1, flags, ws)
+        ys = [torch.full((1, N), float("nan"), dtype=torch.float16, device="cuda") for _ in range(4)]
+        bgg.bgg_ternary_gemv(d.desc, d.packed, xd, ys[0], 1, flags, ws)
         bgg.bgg_gemv_prepare(d.desc, xd, 1, flags, ws)
-        bgg.bgg_gemv_run(d.desc, d.packed, y2, 1, ws)
+        bgg.bgg_gemv_run(d.desc, d.packed, ys[1], 1, ws)
+        bgg.bgg_ternary_gemv(d.desc, d.packed, xd, ys[2], 1, flags, ws)
+        bgg.bgg_gemv_prepare(d.desc, xd, 1, flags, ws)
+        bgg.bgg_gemv_run(d.desc, d.packed, ys[3], 1, ws)
         torch.cuda.synchronize()
-        a, b = y1.cpu().numpy(), y2.cpu().numpy()
-        assert not np.isnan(a).any()
-        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"call {i}"
-        if i == 0 and N * K <= 1 << 20:
-            assert np.all(relerr(a, oracle_y(fmt, T, S, x)) <= TOL)
+        a, b, a2, b2 = (t.cpu().numpy() for t in ys)
+        assert not np.isnan(a).any() and not np.isnan(b).any()
+        assert np.array_equal(a.view(np.uint16), a2.view(np.uint16)), f"call {i}: one launch repeated"
+        assert np.array_equal(b.view(np.uint16), b2.view(np.uint16)), f"call {i}: two steps repeated"
+        if fmt == "PTQ1_0":
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"call {i}"
+        ref = oracle_y(fmt, T[rows], S[rows], x, rotate=flags != 0)
+        den = max(float(np.max(np.abs(ref))), 1e-30)
+        for y in (a, b):
+            assert float(np.max(np.abs(y[0, rows].astype(np.float64) - ref[0]))) / den <= TOL, f"call {i}"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -285,40 +295,30 @@ def test_gemv_zero_weights_and_repeat_calls(env, fmt):
 @pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408), (1000, 1152), (200, 5248),
                                  (8192, 6144)])
 def test_gemv_tokens_do_not_mix(env, fmt, N, K):
-    """Several tokens run on the matrix cores with 16 token slots and the
-    integer arithmetic of the VALU kernels: a token's y must not depend on
-    the other tokens or on M (bit for bit), must equal its one-token y bit for bit where the one-token
-    kernel splits K the same way (PQ2_0 always; PTQ1_0 when it takes whole
-    periods), and M = 16 must match the oracle."""
+    """Several tokens share each weight load: a token's y must not depend on
+    the other tokens of the call -- the tokens in reverse order give the
+    rows in reverse order bit for bit, the same token in every slot gives
+    identical rows -- and every token count matches the oracle.  (Token
+    counts run on different kernels -- one token, up to four, more -- whose
+    summation orders differ, so rows agree across token counts only within
+    tolerance.)"""
     bgg, torch = env
     say(f"gemv tokens do not mix {fmt} {N}x{K}")
     T, S = gen_matrix(101, 3, N, K)
     d = Dev(bgg, torch, fmt, T, S)
     x = synth.activations_f16(101, 4, 16, K)
     ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 16))
-    mx = "k_gemv_pq2_mx<" if fmt == "PQ2_0" else "k_gemv_ptq1_mx<"
-    assert bgg.bgg_gemv_kernel_name(d.desc, 2).startswith(mx)
-    if fmt == "PQ2_0" and (N, K) == (8192, 6144):
-        # eight groups per wave: the kernel runs them as two batches of four
-        assert bgg.bgg_gemv_kernel_name(d.desc, 3) == "k_gemv_pq2_mx<8, 8>"
-    y16 = d.gemv(x, ws=ws)
-    ref = oracle_y(fmt, T, S, x)
-    assert np.all(relerr(y16, ref) <= TOL)
-    for M in (2, 3, 7, 15):
-        yM = d.gemv(x[16 - M:], ws=ws)
-        assert np.array_equal(yM.view(np.uint16), y16[16 - M:].view(np.uint16)), f"M={M}"
-    one = bgg.bgg_gemv_kernel_name(d.desc, 1)
-    same_split = fmt == "PQ2_0" or one.startswith("k_gemv_ptq1<1, 1,")
-    for m in (0, 5, 15):
-        y1 = d.gemv(x[m:m + 1], ws=ws)
-        if same_split:
-            assert np.array_equal(y1[0].view(np.uint16), y16[m].view(np.uint16)), f"token {m}"
-        else:
-            assert relerr(y1[0], y16[m].astype(np.float64)) <= TOL
-    # the same token in every slot
-    xs = np.repeat(x[5:6], 16, axis=0)
-    ys = d.gemv(xs, ws=ws)
-    assert np.all(ys.view(np.uint16) == y16[5].view(np.uint16))
+    rows = np.arange(N) if N * K <= 1 << 21 else np.random.default_rng(5).choice(N, 64, replace=False)
+    ref16 = oracle_y(fmt, T[rows], S[rows], x)
+    for M in (1, 2, 3, 4, 7, 15, 16):
+        xm = x[16 - M:]
+        yM = d.gemv(xm, ws=ws)
+        assert np.all(relerr(yM[:, rows], ref16[16 - M:]) <= TOL), f"M={M}"
+        if M > 1:
+            yr = d.gemv(np.ascontiguousarray(xm[::-1]), ws=ws)
+            assert np.array_equal(yr[::-1].view(np.uint16), yM.view(np.uint16)), f"M={M} reversed"
+            ys = d.gemv(np.repeat(xm[:1], M, axis=0), ws=ws)
+            assert np.all(ys.view(np.uint16) == yM[:1].view(np.uint16)), f"M={M} same token"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -336,7 +336,8 @@ def test_gemv_matrix_core_edges(env, fmt, N, K, M):
     T, S = gen_matrix(111, 5, N, K)
     x = synth.activations_f16(111, 6, M, K)
     d = Dev(bgg, torch, fmt, T, S)
-    assert "_mx<" in bgg.bgg_gemv_kernel_name(d.desc, M)
+    kn = bgg.bgg_gemv_kernel_name(d.desc, M)
+    assert kn.startswith("k_mxv") or "_mx<" in kn, kn
     y = d.gemv(x)
     assert not np.isnan(y).any()
     ref = oracle_y(fmt, T, S, x)
