@@ -79,6 +79,7 @@ _SIGS = {
     "bgg_rotate_ternarize": ([_vp, _i64, _i64, _vp, _vp, _vp], _i32),
     "bgg_gemv_workspace_size": ([_P, _i64], _sz),
     "bgg_ternary_gemv": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
+    "bgg_ternary_gemv_noalloc": ([_P, _vp, _vp, _vp, _i64, _u32, _vp], _i32),
     "bgg_gemv_prepare": ([_P, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_gemv_run": ([_P, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
     "bgg_gemv_kernel_name": ([_P, _i64, ctypes.c_char_p, _sz], _i32),
@@ -226,6 +227,12 @@ def bgg_ternary_gemv(desc, packed_dev, x_dev, y_dev, M: int, flags: int, workspa
     _ok(_lib.bgg_ternary_gemv(ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
                               _dev_ptr(x_dev, M * desc.K * 2, "x"), _dev_ptr(y_dev, M * desc.N * 2, "y"),
                               M, flags, ws, wsb, _stream(stream)), "bgg_ternary_gemv")
+
+
+def bgg_ternary_gemv_noalloc(desc, packed_dev, x_dev, y_dev, M: int, flags: int, stream=None) -> None:
+    _ok(_lib.bgg_ternary_gemv_noalloc(ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
+                                      _dev_ptr(x_dev, M * desc.K * 2, "x"), _dev_ptr(y_dev, M * desc.N * 2, "y"),
+                                      M, flags, _stream(stream)), "bgg_ternary_gemv_noalloc")
 
 
 def bgg_gemv_prepare(desc, x_dev, M: int, flags: int, workspace, stream=None) -> None:

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbgg.so")
-SOURCES = ["bgg_host.cpp", "bgg_rotate.hip", "bgg_gemv.hip", "bgg_mxv.hip", "bgg_unpack.hip", "bgg_gemm.hip",
+SOURCES = ["bgg_host.cpp", "bgg_rotate.hip", "bgg_gemv.hip", "bgg_gemv_noalloc.hip", "bgg_mxv.hip", "bgg_unpack.hip", "bgg_gemm.hip",
            "bgg_ternarize.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -242,6 +242,26 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bgg_ternary_gemv for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same product, kernels and bits, with no workspace
+ * argument.  Its workspace is a static device array of 48 MiB per GPU (held
+ * by each GPU the library runs on until the process ends); a shape whose
+ * bgg_gemv_workspace_size exceeds that is rejected with BGG_ERR_SHAPE
+ * before anything is enqueued (48 MiB serves every format and M for K up to
+ * 65536).  The call allocates nothing: the array's address on the current
+ * device is looked up once, and the first call on a device clears the
+ * array on `stream` ahead of its own kernels.  All calls on one GPU share
+ * the array, so calls that overlap in time on one GPU race; calls that do
+ * not overlap may run on any streams.
+ * Arguments, flags and errors: as bgg_ternary_gemv (BGG_ERR_HIP also if the
+ * array's address cannot be taken).
+ */
+bgg_status bgg_ternary_gemv_noalloc(const bgg_weights_desc* desc, const void* packed_dev,
+                                    const void* x_dev, void* y_dev, int64_t M, uint32_t flags,
+                                    void* stream);
+
+/*
  * The two halves of bgg_ternary_gemv, for projections that share an input
  * (q, k and v, or gate and up, read the same x).
  *

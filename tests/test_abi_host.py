@@ -211,6 +211,19 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, wsz, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, wsz, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
+    # the no-allocation variant: shape checks, its 48 MiB limit and NULL
+    # buffers, all before any device work
+    lib.bgg_ternary_gemv_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_uint32,
+                                                                     ctypes.c_void_p]
+    assert lib.bgg_ternary_gemv_noalloc(None, 16, 16, 16, 1, 1, None) == 1
+    assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), 16, 16, 16, 0, 1, None) == 3
+    assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), 16, 16, 16, 17, 1, None) == 3
+    assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), None, 16, 16, 1, 1, None) == 1
+    big = bgg.bgg_describe("PTQ1_0", 128, 131072)
+    assert bgg.bgg_gemv_workspace_size(big, 16) > 48 << 20
+    assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(big), 16, 16, 16, 16, 1, None) == 3
+    lib.bgg_last_error.restype = ctypes.c_char_p
+    assert b"static workspace" in lib.bgg_last_error()
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 17, 16, 16, 1, 1, 16, 1 << 20, None) == 6
     # the offline front end: NULL, shape and alignment errors before any work
     lib.bgg_rotate_ternarize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
