@@ -30,6 +30,7 @@
 //     addition does not depend on the order; one launch, no waiting on other
 //     workgroups).
 #include "bgg_device.h"
+#include "bgg_rowsum.h"
 
 #include <algorithm>
 #include <cstdio>
@@ -123,12 +124,21 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
       for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
     }
     float amax = 0.0f;
+    int nf = 0;  // a non-finite x' in the block
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) {
+      amax = fmaxf(amax, fabsf(v[j]));
+      nf |= !(fabsf(v[j]) <= 3.0e38f);
+    }
     amax = fmaxf(amax, xor16_f<1>(amax));
     amax = fmaxf(amax, xor16_f<2>(amax));
     amax = fmaxf(amax, xor16_f<4>(amax));
     amax = fmaxf(amax, xor16_f<8>(amax));
+    nf |= xor16_i<1>(nf);
+    nf |= xor16_i<2>(nf);
+    nf |= xor16_i<4>(nf);
+    nf |= xor16_i<8>(nf);
+    if (nf) amax = 0.0f;  // digits 0; the block's scale below is NaN
     int e = 0;
     frexpf(amax, &e);  // amax = f * 2^e, f in [0.5, 1): |x'| < 2^e
     int qsum = 0;
@@ -147,7 +157,9 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
     qsum += xor16_i<2>(qsum);
     qsum += xor16_i<4>(qsum);
     qsum += xor16_i<8>(qsum);
-    const float f = amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
+    // a block with a non-finite x' scales its groups by NaN: every row of
+    // the token becomes NaN, as 0 * inf and NaN do in the fp64 product
+    const float f = nf ? __builtin_nanf("") : amax > 0.0f ? ldexpf(1.0f, e - 14) : 0.0f;
     meta.q[pass] = qsum;
     meta.f[pass] = f;
     if (metaQ && in_set && lane16 == 0 && g < gpad) {
@@ -286,37 +298,15 @@ __global__ void __launch_bounds__(64)
 
 // ---------------------------------------------------------------------------
 // Workgroup end: the W waves' partial sums are added in wave order in LDS and
-// wave 0 writes y when the workgroup covers all of K.  Otherwise (Sg
-// workgroups per tile) each lane adds its row's partial sum into the row's
-// 64-bit word with one device-scope atomic add:
-//   bits 0..56   sum over the arrived workgroups of (v + 2^49), where
-//                v = round(partial * 2^30), clamped to |v| < 2^49
-//   bits 57..63  number of arrived workgroups
-// The lane that sees Sg - 1 arrivals before its own has the whole sum: it
-// removes the biases, writes y and sets the word back to zero for the next
-// launch.  Integer addition is exact, so y does not depend on the order of
-// arrival (deterministic), and one atomic replaces a store, a wait for it, a
-// counter update and reloads of the other partial rows.  Partial sums are
-// kept to 2^-30 absolute (far below an fp16 ulp of any normal y) and up to
-// 2^19 in magnitude (beyond fp16's range).
+// wave 0 writes y when the workgroup covers all of K; otherwise (Sg
+// workgroups per tile) each lane adds its row's partial sum into the row
+// words at the start of the workspace (bgg_rowsum.h: fixed point, exact and
+// order-independent, NaN sticky), and the workgroup that completes a row
+// writes y.  A launch covers at most kSumRows rows of split tiles.
 // ---------------------------------------------------------------------------
-constexpr int kSumCountShift = 57;
-constexpr uint64_t kSumBias = 1ull << 49;
-constexpr uint64_t kSumMask = (1ull << kSumCountShift) - 1;
-constexpr int kMaxSumSlices = 127;  // arrivals the count field holds
-// The row sums sit at the start of every GEMV workspace, whatever the format,
-// K, M and N: kSumSlots token slots of kSumRows words.  A launch covers at
-// most kSumRows rows of split tiles.  Every launch leaves the words it used
-// at zero, so a zero-filled workspace stays ready for any GEMV call.
-constexpr int64_t kSumSlots = 16;
-constexpr int64_t kSumRows = 65536;
-constexpr uint64_t kSumBytes = (uint64_t)kSumSlots * kSumRows * 8;  // 8 MiB
-
-__device__ __forceinline__ uint64_t sum_term(float s) {
-  const double lim = (double)(kSumBias - 1);
-  const double v = fmin(fmax(rint((double)s * 0x1p30), -lim), lim);
-  return (uint64_t)((int64_t)v + (int64_t)kSumBias);
-}
+constexpr int kMaxSumSlices = kMaxSlices;  // arrivals the row words count
+constexpr int64_t kSumRows = kRowWordRows;
+constexpr uint64_t kSumBytes = 2 * kRowWordBytes;  // fine and coarse words
 
 template <int M, int W>
 __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M][64], int wave,
@@ -340,18 +330,11 @@ __device__ __forceinline__ void wg_finish(const float (&acc)[M], float (*red)[M]
       if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h(s[m]);
     return;
   }
+  if (row >= N) return;
+  const RowWords rw = row_words_of(sums);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    unsigned long long* word = &sums[(int64_t)m * kSumRows + local_row];
-    const uint64_t term = sum_term(s[m]);
-    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int)(old >> kSumCountShift) == Sg - 1) {
-      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)Sg * (int64_t)kSumBias;
-      if (m < Mreal && row < N) y[(int64_t)m * N + row] = f2h((float)((double)tot * 0x1p-30));
-      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  for (int m = 0; m < M; ++m)
+    if (m < Mreal) add_partial(rw, m, local_row, Sg, s[m], y + (int64_t)m * N + row);
 }
 
 // ---------------------------------------------------------------------------
@@ -1074,15 +1057,7 @@ __device__ __forceinline__ void mx_gemv_body(const uint8_t* __restrict__ packed,
       if (row < N) y[(int64_t)t * N + row] = f2h(v);
       continue;
     }
-    unsigned long long* word = &sums[(int64_t)t * kSumRows + ws.local * kTile + r];
-    const uint64_t term = sum_term(v);
-    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int)(old >> kSumCountShift) == ws.Sg - 1) {
-      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)ws.Sg * (int64_t)kSumBias;
-      if (row < N) y[(int64_t)t * N + row] = f2h((float)((double)tot * 0x1p-30));
-      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (row < N) add_partial(row_words_of(sums), t, ws.local * kTile + r, ws.Sg, v, y + (int64_t)t * N + row);
   }
 }
 
@@ -1269,15 +1244,7 @@ __global__ void __launch_bounds__(64 * W)
       if (row < N) y[(int64_t)t * N + row] = f2h(v);
       continue;
     }
-    unsigned long long* word = &sums[(int64_t)t * kSumRows + ws.local * kTile + r];
-    const uint64_t term = sum_term(v);
-    const uint64_t old = __hip_atomic_fetch_add(word, (1ull << kSumCountShift) + term,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int)(old >> kSumCountShift) == ws.Sg - 1) {
-      const int64_t tot = (int64_t)((old & kSumMask) + term) - (int64_t)ws.Sg * (int64_t)kSumBias;
-      if (row < N) y[(int64_t)t * N + row] = f2h((float)((double)tot * 0x1p-30));
-      __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (row < N) add_partial(row_words_of(sums), t, ws.local * kTile + r, ws.Sg, v, y + (int64_t)t * N + row);
   }
 }
 
@@ -1312,12 +1279,22 @@ __global__ void __launch_bounds__(64)
     for (int j = 0; j < 8; ++j) v[j] *= kHadamardNorm;
   }
   float amax = 0.0f;
+  int nf = 0;  // a non-finite x' in the block
 #pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) {
+    amax = fmaxf(amax, fabsf(v[j]));
+    nf |= !(fabsf(v[j]) <= 3.0e38f);
+  }
   amax = fmaxf(amax, xor16_f<1>(amax));
   amax = fmaxf(amax, xor16_f<2>(amax));
   amax = fmaxf(amax, xor16_f<4>(amax));
   amax = fmaxf(amax, xor16_f<8>(amax));
+  nf |= xor16_i<1>(nf);
+  nf |= xor16_i<2>(nf);
+  nf |= xor16_i<4>(nf);
+  nf |= xor16_i<8>(nf);
+  if (nf) amax = 0.0f;  // digits 0; the correction terms below are NaN
+  const float nanf_ = __builtin_nanf("");
   int e = 0;
   frexpf(amax, &e);
   int qsum = 0;
@@ -1343,13 +1320,15 @@ __global__ void __launch_bounds__(64)
   // lanes 0-7 (positions 0-63) and 8-15 (64-127) now hold their half's sum
   if (xh && (l16 & 7) == 0)
     xh[(blk * 2 + (l16 >> 3)) * kMmaSlots + t] =
-        amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
+        nf ? nanf_ : amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
   qsum += xor16_i<8>(qsum);
   if (l16 == 0) {
     const int eb = amax > 0.0f ? e : 0;
     xs[blk * kMmaSlots + t] = (uint32_t)(123 + eb) | ((uint32_t)(118 + eb) << 8) |
                               ((uint32_t)(113 + eb) << 16) | (127u << 24);
-    xc[blk * kMmaSlots + t] = amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
+    // a block with a non-finite x' starts its groups' sums at NaN: every
+    // row of the token becomes NaN, as 0 * inf and NaN do in the fp64 product
+    xc[blk * kMmaSlots + t] = nf ? nanf_ : amax > 0.0f ? -(float)qsum * ldexpf(1.0f, e - 14) : 0.0f;
   }
   __syncthreads();
   // this block's words: 3 digits x 4 lane groups x 4 slots x 8 words; word

@@ -204,36 +204,36 @@ bgg_status bgg_rotate_ternarize(const void* w_dev, int64_t N, int64_t K, int8_t*
 size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
 
 /*
- * Decode-time product, 1 <= M <= 16 tokens [A packing paragraph: decode].
+ * Decode-time product, 1 <= M <= 16 tokens: y = x' (S*T)^T with x' the
+ * normalised block-128 Walsh-Hadamard transform of x [A method and runtime
+ * paragraphs; B 它怎么做到的], for the packings of [A packing paragraph].
  *   packed_dev  device buffer made from bgg_pack_weights output
  *   x_dev       device fp16 [M][K] (model coordinates with BGG_ROTATE_INPUT,
  *               else already rotated)
  *   y_dev       device fp16 [M][N]
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
- *               bytes, 16-byte aligned (64-byte aligned for the one-launch
- *               path below).  Its first 8 MiB hold the row sums of split-K
- *               launches, which must be zero when a call starts: zero-fill a
- *               new workspace once; every GEMV call (any format, K, M or N)
- *               leaves them zero again.  A workspace used for anything else
- *               in between must be zero-filled again.  The rest is scratch.
- * For M == 1 one kernel launch encodes the activations and computes y;
- * otherwise it is bgg_gemv_prepare followed by bgg_gemv_run.  Both give the
- * same bits.
- * Arithmetic.  The activations are carried as 15-bit integers q with a
- * power-of-two scale per 128-block (absolute error at most 2^-14 of the
- * block's largest |x'|); each group's trit sum p = sum t q is exact, and is
- * scaled and accumulated in fp32 in a fixed order.  PQ2_0 and PTQ1_0, one
- * token: one pass over the weights on the vector ALUs.  2..16 tokens (and
- * every token count of Q1_0 and Q2_0_G64): one pass for all of them on the
- * matrix cores, with the same sums and fp32 steps, so a token's y does not
- * depend on the other tokens or on M (PTQ1_0 at M == 1 may split a
- * 640-weight period between two waves, whose partial sums then round
- * differently in the last bits).  Q2_0_G64 scales each 64-weight half of a
- * group by its own scale (two exact half sums).
- * Where K is split over workgroups their partial rows are added as 64-bit
- * fixed-point integers (resolution 2^-30, magnitude below 2^19), whose sum
- * does not depend on the order.  y is rounded to fp16 once, and the same
- * inputs always give bit-identical y.
+ *               bytes, 16-byte aligned (64-byte aligned lets a PTQ1_0 token
+ *               run in one launch).  Its first 16 MiB hold the row words
+ *               of launches that split K (fixed-point partial sums, 8 MiB,
+ *               then 8 MiB of coarse words), which must be zero when a call
+ *               starts: zero-fill a new workspace once; every GEMV call (any
+ *               format, K, M or N) leaves them zero again.  A workspace used
+ *               for anything else in between must be zero-filled again.
+ *               The rest is scratch (encoded activations).
+ * One launch transforms and encodes the activations and computes y (PQ2_0
+ * up to 4 tokens, PTQ1_0 one token); otherwise it is bgg_gemv_prepare
+ * followed by bgg_gemv_run.
+ * Arithmetic.  x' is computed in fp32 and carried per 128-block as integers
+ * |q| <= 2^14 with a power-of-two scale (absolute error at most 2^-14 of the
+ * block's largest |x'|); each group's trit sum over q is exact, and is
+ * scaled by the group's fp16 scale and accumulated in fp32.  Where K is
+ * split over workgroups their partial rows are added as 64-bit fixed-point
+ * integers (2^-30 below 2^17 in magnitude, 1/16 above), exact and
+ * independent of the order, so the same inputs always give the same bits,
+ * and a token's y does not depend on the other tokens of the call.  Every
+ * fp16 x and scale is in range; y beyond the fp16 range is +-inf.  A NaN or
+ * inf in a token's x makes that token's whole y row NaN.  y is rounded to
+ * fp16 once.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER,
  * BGG_ERR_HIP.
  */

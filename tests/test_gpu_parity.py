@@ -587,3 +587,30 @@ def test_gemv_graph_replay_matches_eager(env, fmt, N, K):
         # eager work on the same workspace between replays
         bgg.bgg_ternary_gemv(d.desc, d.packed, x_other, y_other, 1, bgg.BGG_ROTATE_INPUT, ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_rows_beyond_one_launch(env, fmt):
+    """N = 65600, K = 8320: K is split over workgroups and the tiles exceed
+    what one launch's row words hold (65536 rows), so the call runs as
+    several launches that reuse the words.  Rows on both sides of the launch
+    boundary and a random sample match the oracle for one and two tokens,
+    and the call leaves every row word zero."""
+    bgg, torch = env
+    N, K = 65600, 8320
+    say(f"gemv rows beyond one launch {fmt} N={N} K={K}")
+    T, S = gen_matrix(241, 1, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65535, 65536, 65537, 65599],
+                                     rng.choice(N, 56, replace=False)]))
+    wsz = bgg.bgg_gemv_workspace_size(d.desc, 2)
+    for M in (1, 2):
+        ws = bgg.workspace(wsz)
+        x = synth.activations_f16(241, 2 + M, M, K)
+        y = d.gemv(x, ws=ws)
+        assert not np.isnan(y).any()
+        ref = oracle_y(fmt, T[rows], S[rows], x)
+        assert np.all(relerr(y[:, rows], ref) <= TOL), f"M={M}"
+        words = ws[:16 << 20].view(torch.int64)
+        assert int(torch.count_nonzero(words)) == 0, f"M={M}: row words left non-zero"
