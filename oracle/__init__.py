@@ -81,6 +81,8 @@ def configure(lib):
     lib.oracle_ternarize.restype = ci
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
+    lib.oracle_set_num_threads.argtypes = [ci]
+    lib.oracle_set_num_threads.restype = None
     for f in (lib.oracle_sylvester, lib.oracle_rotate, lib.oracle_pack, lib.oracle_unpack,
               lib.oracle_matvec, lib.oracle_linear):
         f.restype = ci
@@ -130,6 +132,11 @@ def _f16bits(a) -> np.ndarray:
 def num_threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Run the oracle's loops on n threads from now on (for timing)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def f16_to_f64(bits: int) -> float:

@@ -338,3 +338,12 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Run the OpenMP loops on n threads from now on (n >= 1; timing only). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

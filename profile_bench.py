@@ -6,15 +6,20 @@ under profiles/.
       per-kernel calls / average / min / max duration from a
       `rocprofv3 --kernel-trace --stats -f csv` run (the *_kernel_stats.csv).
 
-  traffic  FETCH_CSV WRITE_CSV COPY_MIB OUT_JSON "COMMAND" "COMMAND"
+  traffic  FETCH_CSV WRITE_CSV CALIB_MIB OUT_JSON "COMMAND" "COMMAND"
       HBM bytes per dispatch of every kernel from two
       `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE -f csv` runs (the
-      *_counter_collection.csv files) of `bench.py --calib-copy COPY_MIB`.
-      FETCH_SIZE and WRITE_SIZE count KiB; each is scaled by the factor that
-      makes the plain device copy of COPY_MIB MiB (kernel
-      __amd_rocclr_copyBuffer) read and write exactly COPY_MIB MiB.  The JSON
+      *_counter_collection.csv files) of `bench.py --calib CALIB_MIB`.
+      FETCH_SIZE and WRITE_SIZE count KiB; FETCH_SIZE is scaled by the factor
+      that makes this project's streaming read probe (k_probe_read) of
+      CALIB_MIB MiB read exactly that, WRITE_SIZE by the factor that makes
+      the streaming write probe (k_probe_write) write exactly that.  The JSON
       carries bench.source_hash() so bench.py ignores it once the kernel
       sources change.
+
+  counters COUNTER_CSV OUT_MD "COMMAND" KERNEL [KERNEL...]
+      per-dispatch averages of every counter in a `rocprofv3 --pmc ...`
+      run, for the named kernels (short names; a prefix matches).
 """
 from __future__ import annotations
 
@@ -28,7 +33,8 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
+READ_PROBE = "k_probe_read"
+WRITE_PROBE = "k_probe_write"
 
 
 def short_name(name: str) -> str:
@@ -64,44 +70,32 @@ def kernels(stats_csv: str, out_md: str, command: str) -> None:
 
 
 def _per_dispatch(counter_csv: str, counter: str) -> dict:
-    """kernel short name -> list of per-dispatch counter values.  For the
-    copy kernel only the dispatches with the largest grid are kept: those are
-    the calibration copy (the runtime uses the same kernel for small copies
-    of its own)."""
+    """kernel short name -> list of per-dispatch counter values."""
     out = defaultdict(list)
-    copy_rows = []
     with open(counter_csv) as f:
         for r in csv.DictReader(f):
-            if r.get("Counter_Name") != counter:
-                continue
-            name = short_name(r["Kernel_Name"])
-            if name == COPY_KERNEL:
-                copy_rows.append((int(r["Grid_Size"]), float(r["Counter_Value"])))
-            else:
-                out[name].append(float(r["Counter_Value"]))
-    if copy_rows:
-        g = max(c[0] for c in copy_rows)
-        out[COPY_KERNEL] = [v for gs, v in copy_rows if gs == g]
+            if r.get("Counter_Name") == counter:
+                out[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return out
 
 
-def traffic(fetch_csv: str, write_csv: str, copy_mib: int, out_json: str, cmd_fetch: str,
+def traffic(fetch_csv: str, write_csv: str, calib_mib: int, out_json: str, cmd_fetch: str,
             cmd_write: str) -> None:
     import bench
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
-    known_kib = copy_mib * 1024.0
-    f_copy = statistics.mean(fetch[COPY_KERNEL])
-    w_copy = statistics.mean(write[COPY_KERNEL])
-    f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
+    known_kib = calib_mib * 1024.0
+    f_probe = statistics.mean(fetch[READ_PROBE])
+    w_probe = statistics.mean(write[WRITE_PROBE])
+    f_scale, w_scale = known_kib / f_probe, known_kib / w_probe
     res = {"source_hash": bench.source_hash(),
            "counters": "FETCH_SIZE and WRITE_SIZE (KiB per dispatch), averaged over dispatches",
-           "calibration": {"kernel": COPY_KERNEL, "bytes": copy_mib << 20,
-                           "fetch_kib": f_copy, "write_kib": w_copy,
+           "calibration": {"read_kernel": READ_PROBE, "write_kernel": WRITE_PROBE,
+                           "bytes": calib_mib << 20, "fetch_kib": f_probe, "write_kib": w_probe,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "commands": [cmd_fetch, cmd_write], "kernels": {}}
     for name in sorted(set(fetch) & set(write)):
-        if name == COPY_KERNEL:
+        if name in (READ_PROBE, WRITE_PROBE):
             continue
         fb = statistics.mean(fetch[name]) * 1024 * f_scale
         wb = statistics.mean(write[name]) * 1024 * w_scale
@@ -113,11 +107,34 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: int, out_json: str, cmd_fe
     print(json.dumps(res, indent=1))
 
 
+def counters(counter_csv: str, out_md: str, command: str, kernels_wanted) -> None:
+    vals = defaultdict(lambda: defaultdict(list))
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            name = short_name(r["Kernel_Name"])
+            if any(name.startswith(k) for k in kernels_wanted):
+                vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in vals.values() for c in v})
+    lines = ["# Counters per dispatch (rocprofv3 --pmc)", "", "Command (run from the repository root, one MI355X):",
+             "", "```", command, "```", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---:|" + "---:|" * len(names)]
+    for k in sorted(vals):
+        n = max(len(v) for v in vals[k].values())
+        cells = [f"{statistics.mean(vals[k][c]):.4g}" if vals[k].get(c) else "" for c in names]
+        lines.append(f"| `{k}` | {n} | " + " | ".join(cells) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "kernels":
         kernels(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 8 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5], sys.argv[6], sys.argv[7])
+    elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     else:
         print(__doc__, file=sys.stderr)
         sys.exit(2)
