@@ -167,14 +167,19 @@ __device__ __forceinline__ uint32_t ptq1_codes10(uint32_t b) {
   for (int i = 0; i < 5; ++i) r |= ((c >> (4 * i)) & 3u) << (2 * i);
   return r;
 }
+// Entry forms of the table below.
+constexpr int kLutTrits = 0;  // signed trit nibbles (ptq1_trit_nibbles)
+constexpr int kLutCodes = 1;  // 2-bit codes (ptq1_codes10)
+template <int FORM>
+__device__ __forceinline__ uint32_t ptq1_lut_entry(uint32_t b) {
+  return FORM == kLutCodes ? ptq1_codes10(b) : ptq1_trit_nibbles(b);
+}
 // Built in two steps: the first 256 threads each decode one byte value into
 // seed[], then (after a barrier) every thread copies entries out, 16 bytes
 // per store.  Needs blockDim.x >= 256; the caller synchronises afterwards.
-// CODES: entries in the 2-bit code form instead of trit nibbles.
-template <bool CODES = false>
+template <int FORM = kLutTrits>
 __device__ __forceinline__ void build_lut32(uint32_t* lut, uint32_t* seed) {
-  if (threadIdx.x < 256)
-    seed[threadIdx.x] = CODES ? ptq1_codes10(threadIdx.x) : ptq1_trit_nibbles(threadIdx.x);
+  if (threadIdx.x < 256) seed[threadIdx.x] = ptq1_lut_entry<FORM>(threadIdx.x);
   __syncthreads();
   constexpr int kQuads = kLutCopies32 / 4, kRowQuads = kLutRowBytes / 16;
   for (int i = threadIdx.x; i < 256 * kQuads; i += blockDim.x) {
@@ -182,6 +187,14 @@ __device__ __forceinline__ void build_lut32(uint32_t* lut, uint32_t* seed) {
     const uint32_t v = seed[e];
     reinterpret_cast<uint4*>(lut)[e * kRowQuads + q] = make_uint4(v, v, v, v);
   }
+}
+
+// The wave's own LDS writes are visible to all its lanes after this: LDS
+// executes a wave's instructions in order, and the fence keeps the compiler
+// from moving the reads above the writes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 // s_waitcnt lgkmcnt(0) with the other counters left alone (gfx9 encoding:

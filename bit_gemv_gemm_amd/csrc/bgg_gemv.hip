@@ -170,14 +170,6 @@ __device__ __forceinline__ EncodeMeta<NG> wave_encode_finish(const EncodeRaw<NG>
   return meta;
 }
 
-// The wave's own LDS writes are visible to all its lanes after this: LDS
-// executes a wave's instructions in order, and the fence keeps the compiler
-// from moving the reads above the writes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 // PQ2_0 digit words of chunks c0 .. c0+2*NG-1 (those below C) from sd:
 // word (d, par, L) of chunk c holds in nibble n digit L of q at chunk
 // position 16 d + 2 n + par.  Lane item (chunk, d, par) packs the four words
@@ -1161,7 +1153,7 @@ __global__ void __launch_bounds__(64 * W)
     for (int i = 0; i < PRE; ++i) BGG_MX_LOAD_A(i, i);
   }
   __builtin_amdgcn_sched_barrier(0);
-  build_lut32<true>(lut, lut_seed);
+  build_lut32<kLutCodes>(lut, lut_seed);
   __syncthreads();
 
   uint32_t* cw = codes[wave];

@@ -204,8 +204,6 @@ def test_gemv_one_launch_and_two_step(env, fmt, N, K):
         assert not np.isnan(a).any() and not np.isnan(b).any()
         assert np.array_equal(a.view(np.uint16), a2.view(np.uint16)), f"call {i}: one launch repeated"
         assert np.array_equal(b.view(np.uint16), b2.view(np.uint16)), f"call {i}: two steps repeated"
-        if fmt == "PTQ1_0":
-            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"call {i}"
         ref = oracle_y(fmt, T[rows], S[rows], x, rotate=flags != 0)
         den = max(float(np.max(np.abs(ref))), 1e-30)
         for y in (a, b):
