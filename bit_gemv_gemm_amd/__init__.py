@@ -78,6 +78,7 @@ _SIGS = {
     "bgg_hadamard_rotate": ([_vp, _vp, _i64, _i64, _vp], _i32),
     "bgg_rotate_ternarize": ([_vp, _i64, _i64, _vp, _vp, _vp], _i32),
     "bgg_gemv_workspace_size": ([_P, _i64], _sz),
+    "bgg_gemv_workspace_reset": ([_vp, _sz, _vp], _i32),
     "bgg_ternary_gemv": ([_P, _vp, _vp, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
     "bgg_ternary_gemv_noalloc": ([_P, _vp, _vp, _vp, _i64, _u32, _vp], _i32),
     "bgg_gemv_prepare": ([_P, _vp, _i64, _u32, _vp, _sz, _vp], _i32),
@@ -227,6 +228,12 @@ def bgg_ternary_gemv(desc, packed_dev, x_dev, y_dev, M: int, flags: int, workspa
     _ok(_lib.bgg_ternary_gemv(ctypes.byref(desc), _dev_ptr(packed_dev, desc.total_bytes, "packed"),
                               _dev_ptr(x_dev, M * desc.K * 2, "x"), _dev_ptr(y_dev, M * desc.N * 2, "y"),
                               M, flags, ws, wsb, _stream(stream)), "bgg_ternary_gemv")
+
+
+def bgg_gemv_workspace_reset(workspace, stream=None) -> None:
+    wsb = workspace.numel() * workspace.element_size()
+    _ok(_lib.bgg_gemv_workspace_reset(_dev_ptr(workspace, 0, "workspace"), wsb, _stream(stream)),
+        "bgg_gemv_workspace_reset")
 
 
 def bgg_ternary_gemv_noalloc(desc, packed_dev, x_dev, y_dev, M: int, flags: int, stream=None) -> None:

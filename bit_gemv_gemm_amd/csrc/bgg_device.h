@@ -126,19 +126,6 @@ __device__ __forceinline__ uint32_t ptq1_entry(uint32_t b) {
   return e;
 }
 
-// The LUT: 256 entries, each stored 32 times so that lane l reads copy l%32
-// and a wave's 64 random lookups hit 32 distinct banks (32 KiB of LDS).
-constexpr int kLutCopies = 32;
-__device__ __forceinline__ void build_lut(uint32_t* lut) {
-  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
-    const uint32_t e = ptq1_entry((uint32_t)b);
-    const uint4 v = make_uint4(e, e, e, e);
-    uint4* dst = reinterpret_cast<uint4*>(lut + b * kLutCopies);
-#pragma unroll
-    for (int c = 0; c < kLutCopies / 4; ++c) dst[c] = v;
-  }
-}
-
 // The GEMV's LUT holds the trits themselves, t = c - 1 as signed 4-bit
 // nibbles (-1 = 0xF), five to a word.  Entry e occupies a 256-byte row at
 // e * 256; copy c of it is the word at e * 256 + c * 4, and lane l reads copy

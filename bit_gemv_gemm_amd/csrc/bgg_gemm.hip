@@ -411,11 +411,6 @@ int64_t gemm_device_cus() {
 // 5120 rows) costs as much as a full one.  The fp32 partials cost an extra
 // pass over 2 M N floats, so the split must gain at least 15 %.
 bool gemm_split(const bgg_weights_desc* d, int64_t M) {
-  static const int64_t on = [] {
-    const char* e = getenv("BGG_GEMM_SPLIT");
-    return e && *e ? (int64_t)atoll(e) : int64_t(1);
-  }();
-  if (!on) return false;
   const int64_t steps = d->format == BGG_FMT_PQ2_0 ? d->K / kBK : d->chunks;
   if (steps < 8) return false;
   const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;

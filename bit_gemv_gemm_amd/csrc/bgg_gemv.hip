@@ -296,6 +296,12 @@ __global__ void __launch_bounds__(64)
 // order-independent, NaN sticky), and the workgroup that completes a row
 // writes y.  A launch covers at most kSumRows rows of split tiles.
 // ---------------------------------------------------------------------------
+// Zeroes n16 16-byte words (bgg_gemv_workspace_reset).
+__global__ void __launch_bounds__(256) k_fill_zero16(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 constexpr int kMaxSumSlices = kMaxSlices;  // arrivals the row words count
 constexpr int64_t kSumRows = kRowWordRows;
 constexpr uint64_t kSumBytes = 2 * kRowWordBytes;  // fine and coarse words
@@ -381,48 +387,27 @@ __device__ __forceinline__ WgSlot wg_slot(int64_t tile0, int64_t ntl, int64_t nt
 // No global round trip: a wait for the wave's own global stores
 // (s_waitcnt vmcnt(0)) would also wait for every weight load issued before
 // them.  The per-block meta comes from the registers of the lanes that
-// computed it.  (A PTQ1_0 workgroup of 16 waves has too few LUT rows; its
-// waves store the words to one of kFuseCopies copies in the workspace, wait
-// for those stores and read them back with scalar loads: the scalar cache
-// is invalidated at every launch and a period's words fill whole 64-byte
-// lines, so no line is read before it is written.)
+// computed it.
 // ---------------------------------------------------------------------------
 struct FuseArgs {
   const uint16_t* x;  // the token row, K fp16 values
-  uint32_t* frag;     // kFuseCopies copies of the digit words (16-wave PTQ1_0 only)
-  int32_t* metaQ;     // null: the meta stays in registers
-  float* metaF;
   int rotate;
 };
-// Workgroup b writes and reads copy b % kFuseCopies of the digit words: when
-// every workgroup of the launch wrote the same lines, the scalar loads of
-// those lines waited behind the stream of identical writes from the other
-// CUs (3.5 us more for a PTQ1_0 projection).  Workgroups are dispatched to
-// the 8 XCDs in turn, so each copy is written by a few workgroups of one XCD.
-constexpr int64_t kFuseCopies = 64;
-__device__ __forceinline__ void wait_own_stores() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // ---------------------------------------------------------------------------
-// PQ2_0: wave = 64 rows x BPS groups; workgroup = W consecutive K slices.
-// grid: NT * Sg workgroups of 64*W threads.
+// PQ2_0, the second step of bgg_gemv_prepare + bgg_gemv_run for one token
+// (one launch serves one token through bgg_mxv.hip): wave = 64 rows x BPS
+// groups; workgroup = W consecutive K slices.  grid: NT * Sg workgroups of
+// 64*W threads.
 // ---------------------------------------------------------------------------
-template <int M, int BPS, int W, bool FUSE>
+template <int M, int BPS, int W>
 __global__ void __launch_bounds__(64 * W)
     k_gemv_pq2(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t C, int64_t G,
                int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
-               int64_t rows_pad, int64_t tile0, int64_t ntl,
-               int64_t nta, int sgb, int light_last, FuseArgs fa, uint16_t* __restrict__ y) {
-  static_assert(!FUSE || M == 1, "the one-launch GEMV is for one token");
+               int64_t tile0, int64_t ntl, int64_t nta, int sgb, int light_last,
+               uint16_t* __restrict__ y) {
   __shared__ float red[W][M][64];
-  __shared__ __attribute__((aligned(16))) uint16_t sd_stage[FUSE ? W * BPS * kGroup : 8];
-  // one-launch: each wave's digit words stay in LDS (chunks of its slice)
-  constexpr int kWaveFrag = 2 * BPS * kPqFragWords;
-  __shared__ __attribute__((aligned(16))) uint32_t wfrag[FUSE ? W * kWaveFrag : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WgSlot ws = wg_slot(tile0, ntl, nta, Sg, sgb, light_last != 0);
@@ -438,9 +423,6 @@ __global__ void __launch_bounds__(64 * W)
     const uint4* tdata = reinterpret_cast<const uint4*>(packed) + (tile * C) * kTile + lane;
     const uint16_t* sdata =
         reinterpret_cast<const uint16_t*>(packed + scale_offset) + (tile * G) * kTile;
-    EncodeRaw<BPS> xraw;
-    if (FUSE) xraw = wave_encode_load<BPS>(fa.x, G, gbeg, true, lane);
-    uint32_t* wf = wfrag + (FUSE ? wave * kWaveFrag : 0);
     // Every load of the slice is issued before any is used, without branches
     // (a group past G re-reads group G-1 and gets a zero weight below).
     uint4 w[2 * BPS];
@@ -455,31 +437,15 @@ __global__ void __launch_bounds__(64 * W)
     // per-group activation scale and digit sum, for every token
     float gf[BPS][M];
     int gq[BPS][M];
-    if (FUSE) {
-      __builtin_amdgcn_sched_barrier(0);
-      uint16_t* sdw = sd_stage + wave * (BPS * kGroup);
-      const EncodeMeta<BPS> em =
-          wave_encode_finish<BPS>(xraw, gbeg, fa.rotate, sdw, lane, fa.metaQ, fa.metaF, gpad);
-      wave_lds_sync();
-      wave_pack_pq2<BPS>(sdw, wf, 2 * gbeg, C, lane, 2 * gbeg);
-      // the group meta straight from the registers
 #pragma unroll
-      for (int i = 0; i < BPS; ++i) {
-        gf[i][0] = em.f_of(i);
-        gq[i][0] = em.q_of(i);
+    for (int i = 0; i < BPS; ++i)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const bool gv = gbeg + i < G;
+        const int64_t g = gv ? gbeg + i : G - 1;
+        gf[i][m] = gv ? metaF[(int64_t)m * gpad + g] : 0.0f;
+        gq[i][m] = metaQ[(int64_t)m * gpad + g];
       }
-      wave_lds_sync();
-    } else {
-#pragma unroll
-      for (int i = 0; i < BPS; ++i)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const bool gv = gbeg + i < G;
-          const int64_t g = gv ? gbeg + i : G - 1;
-          gf[i][m] = gv ? metaF[(int64_t)m * gpad + g] : 0.0f;
-          gq[i][m] = metaQ[(int64_t)m * gpad + g];
-        }
-    }
     // keep the scheduler from sinking the loads towards their uses
     __builtin_amdgcn_sched_barrier(0);
 
@@ -499,22 +465,13 @@ __global__ void __launch_bounds__(64 * W)
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const uint32_t* xf = FUSE ? wf + (2 * (g - gbeg)) * kPqFragWords
-                                  : frag + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
+        const uint32_t* xf = frag + (int64_t)m * frag_words_per_token + (2 * g) * kPqFragWords;
         int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-        // one-launch: the group's 64 digit words from LDS, all reads issued
-        // before the first use (a read takes far longer than its four dot8)
-        uint4 fl[FUSE ? 16 : 1];
-        if (FUSE) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) fl[q] = reinterpret_cast<const uint4*>(xf)[q];
-        }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            const uint32_t* f =
-                FUSE ? reinterpret_cast<const uint32_t*>(&fl[c * 8 + d * 2]) : xf + c * kPqFragWords + d * 8;
+            const uint32_t* f = xf + c * kPqFragWords + d * 8;
             const int e = (int)E[c * 4 + d], o = (int)O[c * 4 + d];
             a0 = __builtin_amdgcn_sdot8(e, (int)f[0], a0, false);
             a1 = __builtin_amdgcn_sdot8(e, (int)f[1], a1, false);
@@ -654,8 +611,8 @@ __global__ void __launch_bounds__(64 * W)
                 int64_t N, int Sg, int Mreal, const uint32_t* __restrict__ frag,
                 int64_t frag_words_per_token, const int32_t* __restrict__ metaQ,
                 const float* __restrict__ metaF, int64_t gpad, unsigned long long* __restrict__ sums,
-                int64_t rows_pad, int64_t tile0, int64_t ntl,
-                int64_t nta, int sgb, int light_last, FuseArgs fa, uint16_t* __restrict__ y) {
+                int64_t tile0, int64_t ntl, int64_t nta, int sgb, int light_last, FuseArgs fa,
+                uint16_t* __restrict__ y) {
   constexpr int CH = kPeriodChunks / H;  // chunks per part
   static_assert(W * 64 >= 256, "the LUT build needs 256 threads");
   static_assert(!FUSE || M == 1, "the one-launch GEMV is for one token");
@@ -694,10 +651,10 @@ __global__ void __launch_bounds__(64 * W)
     for (int c = 0; c < CH; ++c) w[c] = ld_stream(tdata + (p * kPeriodChunks + part * CH + c) * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int64_t fcopy = FUSE ? (int64_t)(blockIdx.x % kFuseCopies) * frag_words_per_token : 0;
   // one-launch: the wave's digit words in LDS, in the unused upper halves
-  // of LUT rows wave * kPtqHoleRows .. (when the workgroup's waves fit)
-  constexpr bool kHoles = FUSE && W * kPtqHoleRows <= 256;
+  // of LUT rows wave * kPtqHoleRows ..
+  constexpr bool kHoles = FUSE;
+  static_assert(W * kPtqHoleRows <= 256, "the waves' digit words fit the LUT rows");
   uint32_t* holes = lut + wave * kPtqHoleRows * (kLutRowBytes / 4) + kLutRowBytes / 8;
   // the LUT is built while the loads are in flight (with FUSE: while x is)
   build_lut32(lut, lut_seed);
@@ -707,16 +664,11 @@ __global__ void __launch_bounds__(64 * W)
   EncodeMeta<kPeriodGroups> em;
   if (FUSE && active) {
     uint16_t* sdw = sd_stage + wave * (kPeriodGroups * kGroup);
-    em = wave_encode_finish<kPeriodGroups>(xraw, p * kPeriodGroups, fa.rotate, sdw, lane, fa.metaQ,
-                                           fa.metaF, gpad);
+    em = wave_encode_finish<kPeriodGroups>(xraw, p * kPeriodGroups, fa.rotate, sdw, lane, nullptr,
+                                           nullptr, gpad);
     wave_lds_sync();
-    if (kHoles) {
-      wave_pack_ptq1<true>(sdw, holes, 1, 0, lane);
-      wave_lds_sync();
-    } else {
-      wave_pack_ptq1(sdw, fa.frag + fcopy + p * kPtqFragWords, 1, 0, lane);
-      wait_own_stores();
-    }
+    wave_pack_ptq1<true>(sdw, holes, 1, 0, lane);
+    wave_lds_sync();
   }
 
   float acc[M];
@@ -734,7 +686,7 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
       for (int m = 0; m < M; ++m) gf[k][m] = FUSE ? em.f_of(k) : metaF[(int64_t)m * gpad + gp + k];
     }
-    const uint32_t* fp = kHoles ? holes : frag + fcopy + p * kPtqFragWords * M;
+    const uint32_t* fp = kHoles ? holes : frag + p * kPtqFragWords * M;
     const uint32_t lane_off = lut_lane_off(lane);
     const char* lbase = reinterpret_cast<const char*>(lut);
     static_assert(H == 1 || H == 2, "one or two parts per period");
@@ -1358,35 +1310,23 @@ inline int64_t gemv_m_slots(int64_t M) {
   return M <= 2 ? M : ((M + kGemvTokens - 1) / kGemvTokens) * kGemvTokens;
 }
 
-// A tuning override from the environment (unset or empty: dflt).
-int64_t env_int(const char* name, int64_t dflt) {
-  const char* e = getenv(name);
-  return e && *e ? atoll(e) : dflt;
-}
-
 // Split of K: units along K (PQ2_0: groups, PTQ1_0: periods of 5 groups),
 // units per wave slice, waves per workgroup W, slices S, workgroup slices
 // Sg = ceil(S / W) (Sg > 1: the workgroups of a tile add their rows into
 // 64-bit row sums), and the workspace layout.
 struct GemvPlan {
-  int64_t G, gpad, units, per_slice, W, S, Sg, NT, rows_pad, slots, frag_words_per_token;
-  uint64_t off_frag, off_meta_q, off_meta_f, off_sums, off_fuse, total;
+  int64_t G, gpad, units, per_slice, W, S, Sg, NT, slots, frag_words_per_token;
+  uint64_t off_frag, off_meta_q, off_meta_f, off_sums, total;
   int64_t nta, sgb;  // tiles with Sg slices; one-wave slices of the rest
   bool mma;          // PQ2_0 with several tokens: the matrix-core kernel
 };
 
-// The fewest tokens that run on the matrix-core kernels (fewer: the VALU
-// kernels, up to four tokens per pass; both give the same bits).  From two
-// tokens on they measured faster for both packings (the VALU kernels spend
-// dot8 work per packed word or byte and token); one token stays on the
-// VALU kernels, whose one-launch form also encodes the activations.
+// The fewest tokens that run on the matrix-core kernels of this file: two
+// (they measured faster than the VALU kernels from two tokens on, for both
+// packings: the VALU kernels spend dot8 work per packed word or byte and
+// token); every token count for the sister formats.
 int64_t gemv_mma_min_tokens(int format) {
-  static const int64_t pq2 = env_int("BGG_GEMV_MMA_MIN", 2);
-  static const int64_t ptq1 = env_int("BGG_GEMV_PTQ1_MMA_MIN", 2);
-  // the sister formats have only the matrix-core kernels
-  if (format == BGG_FMT_Q1_0 || format == BGG_FMT_Q2_0_G64) return 1;
-  const int64_t m = format == BGG_FMT_PQ2_0 ? pq2 : ptq1;
-  return m < 1 ? 1 : m;
+  return format == BGG_FMT_Q1_0 || format == BGG_FMT_Q2_0_G64 ? 1 : 2;
 }
 
 // Compute units of the current device (cached per device).
@@ -1403,14 +1343,14 @@ int64_t device_cus() {
   return cus[dev];
 }
 
+// Wave counts the K split aims at (measured on the projection shapes).
+constexpr int64_t kTargetWaves = 2048;     // the split of K aims at this many waves
+constexpr int64_t kMinSingleWaves = 1024;  // one workgroup per tile from this many waves
+
 GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
-  static const int64_t target = env_int("BGG_GEMV_TARGET_WAVES", 2048);
-  static const int64_t min_single = env_int("BGG_GEMV_MIN_WAVES", 1024);
-  static const int64_t ptq1_target = env_int("BGG_GEMV_PTQ1_WAVES", 2048);
   GemvPlan p{};
   p.G = d->groups;
   p.NT = d->row_tiles;
-  p.rows_pad = p.NT * kTile;
   p.slots = gemv_m_slots(M);
   p.W = 8;
   p.mma = M >= gemv_mma_min_tokens(d->format);
@@ -1424,7 +1364,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     const int64_t one_wg[] = {2, 4, 5, 8};
     p.per_slice = 0;
     for (int64_t b : one_wg)
-      if (ceil_div(p.units, b) <= p.W && p.NT * p.W >= min_single &&
+      if (ceil_div(p.units, b) <= p.W && p.NT * p.W >= kMinSingleWaves &&
           !(b == 5 && d->format == BGG_FMT_Q2_0_G64)) {
         p.per_slice = b;
         break;
@@ -1432,26 +1372,23 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
     if (!p.per_slice) {
       // else the largest groups-per-wave that gives the target wave count
       p.per_slice = 8;
-      while (p.per_slice > 2 && p.NT * p.W * ceil_div(ceil_div(p.units, p.per_slice), p.W) < target)
+      // (as long as the slices of a tile stay within what a row word counts)
+      while (p.per_slice > 2 && p.NT * p.W * ceil_div(ceil_div(p.units, p.per_slice), p.W) < kTargetWaves &&
+             ceil_div(ceil_div(p.units, p.per_slice / 2), p.W) <= kMaxSumSlices)
         p.per_slice /= 2;
     }
     p.S = ceil_div(p.units, p.per_slice);
   } else {
     // units are period parts: H parts per period, H = 2 only for one token
     // and only when whole periods give fewer waves than the target (more
-    // parts mean more per-wave and per-workgroup overhead; for several
-    // tokens the digit words need the scalar registers); 8 waves per
-    // workgroup by default (16 measured slower: the LUT barrier waits for
-    // more waves)
+    // parts mean more per-wave and per-workgroup overhead); 8 waves per
+    // workgroup (16 measured slower: the LUT barrier waits for more waves)
     const int64_t P = ceil_div(p.G, kPeriodGroups);
     p.gpad = P * kPeriodGroups;
     p.frag_words_per_token = P * kPtqFragWords;
-    static const int64_t ptq1_w = env_int("BGG_GEMV_PTQ1_W", 8) >= 16 ? 16 : 8;
-    // (every token group of this M runs with p.W; the matrix-core kernel
-    // with 8)
-    p.W = p.mma || gemv_m_bucket(M) >= 4 ? 8 : ptq1_w;
     p.per_slice = 1;
-    while (p.per_slice < 2 && !p.mma && gemv_m_bucket(M) == 1 && p.NT * P * p.per_slice < ptq1_target)
+    while (p.per_slice < 2 && !p.mma && p.NT * P * p.per_slice < kTargetWaves &&
+           ceil_div(P * 2, p.W) <= kMaxSumSlices)
       p.per_slice *= 2;
     p.units = P * p.per_slice;
     p.S = p.units;
@@ -1461,8 +1398,7 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   // tiles left over above a multiple of the CU count: one-wave slices
   p.nta = p.NT;
   p.sgb = 1;
-  static const int64_t split_rest = env_int("BGG_GEMV_SPLIT_REST", 1);
-  if (split_rest && p.Sg == 1 && p.S <= kMaxSumSlices && p.NT * kTile <= kSumRows) {
+  if (p.Sg == 1 && p.S <= kMaxSumSlices && p.NT * kTile <= kSumRows) {
     const int64_t ncu = device_cus(), r = p.NT % ncu;
     if (p.NT > ncu && r != 0 && r * p.S <= 2 * ncu) {
       p.nta = p.NT - r;
@@ -1485,10 +1421,6 @@ GemvPlan plan_gemv(const bgg_weights_desc* d, int64_t M) {
   off = align256(off + meta_q_bytes);
   p.off_meta_f = off;
   off = align256(off + (uint64_t)p.slots * p.gpad * 4);
-  // the one-launch kernel's copies of one token's digit words (reserved for
-  // every M, so that a workspace sized for more tokens serves fewer)
-  p.off_fuse = off;
-  off = align256(off + (uint64_t)kFuseCopies * p.frag_words_per_token * 4);
   p.total = off;
   return p;
 }
@@ -1522,20 +1454,16 @@ void launch_prep(const bgg_weights_desc* d, const GemvPlan& p, const uint16_t* x
                        (int)M, rotate, frag, p.frag_words_per_token, mq, mf, p.gpad);
 }
 
-// GEMV over all weight rows for tokens m0 .. m0+Mreal-1 (one launch, or one
-// per kSumRows rows of split tiles).  With FUSE (one token) the kernel also
-// encodes the activations from fa.x.
-template <int M, bool FUSE>
-void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed,
-                 uint16_t* y, int64_t m0, int Mreal, uint8_t* ws, const FuseArgs& fa,
-                 hipStream_t st) {
-  const uint32_t* frag =
-      FUSE ? reinterpret_cast<const uint32_t*>(ws + p.off_fuse)
-           : reinterpret_cast<const uint32_t*>(ws + p.off_frag) + m0 * p.frag_words_per_token;
-  const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q) + m0 * p.gpad;
-  const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f) + m0 * p.gpad;
+// The VALU GEMV for one token (one launch, or one per kSumRows rows of split
+// tiles).  FUSE (PTQ1_0 only): the kernel also encodes the activations from
+// fa.x; else it reads the preparation in the workspace.
+template <bool FUSE>
+void launch_gemv1(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* packed, uint16_t* y,
+                  uint8_t* ws, const FuseArgs& fa, hipStream_t st) {
+  const uint32_t* frag = reinterpret_cast<const uint32_t*>(ws + p.off_frag);
+  const int32_t* mq = reinterpret_cast<const int32_t*>(ws + p.off_meta_q);
+  const float* mf = reinterpret_cast<const float*>(ws + p.off_meta_f);
   unsigned long long* sums = reinterpret_cast<unsigned long long*>(ws + p.off_sums);
-  uint16_t* yg = y + m0 * d->N;
   const int Sg = (int)p.Sg;
   const dim3 block((unsigned)(64 * p.W));
   // split tiles add into the row sums, which hold kSumRows rows: one launch
@@ -1547,38 +1475,35 @@ void launch_gemv(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t* pa
     // slices; else every tile has Sg slices
     const int64_t nta = p.sgb > 1 ? p.nta : ntl;
     const int sgb = (int)p.sgb;
-    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
-    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
+    // (with split tiles whose slices do not fill the last workgroup: that
+    // light workgroup is dispatched first)
+    const int light = p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
     const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
-    if (d->format == BGG_FMT_PQ2_0) {
+    if constexpr (!FUSE) {
+      if (d->format == BGG_FMT_PQ2_0) {
 #define BGG_PQ2(BPS)                                                                              \
-  hipLaunchKernelGGL((k_gemv_pq2<M, BPS, 8, FUSE>), grid, block, 0, st, packed, d->scale_offset, \
-                     d->chunks, p.G, d->N, Sg, Mreal, frag, p.frag_words_per_token, mq, mf,      \
-                     p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, light, fa, yg)
-      switch (p.per_slice) {
-        case 8: BGG_PQ2(8); break;
-        case 5: BGG_PQ2(5); break;
-        case 4: BGG_PQ2(4); break;
-        default: BGG_PQ2(2); break;
-      }
+  hipLaunchKernelGGL((k_gemv_pq2<1, BPS, 8>), grid, block, 0, st, packed, d->scale_offset, d->chunks, \
+                     p.G, d->N, Sg, 1, frag, p.frag_words_per_token, mq, mf, p.gpad, sums, t0, ntl,  \
+                     nta, sgb, light, y)
+        switch (p.per_slice) {
+          case 8: BGG_PQ2(8); break;
+          case 5: BGG_PQ2(5); break;
+          case 4: BGG_PQ2(4); break;
+          default: BGG_PQ2(2); break;
+        }
 #undef BGG_PQ2
-    } else {
-      // 16-wave workgroups only for the one- and two-token kernels (register
-      // budget); p.W says which one the plan was made for
-      constexpr int W16 = M >= 4 ? 8 : 16;
-      constexpr int H2 = M == 1 ? 2 : 1;
-#define BGG_PTQ1(H, WW)                                                                           \
-  hipLaunchKernelGGL((k_gemv_ptq1<M, H, WW, FUSE>), grid, block, 0, st, packed,                \
-                     d->scale_offset, d->chunks, p.G, d->N, Sg, Mreal, frag,                     \
-                     p.frag_words_per_token, mq, mf, p.gpad, sums, p.rows_pad, t0, ntl, nta, sgb, \
-                     light, fa, yg)
-      if (p.W == 16) {
-        if (p.per_slice == 2) BGG_PTQ1(H2, W16); else BGG_PTQ1(1, W16);
-      } else {
-        if (p.per_slice == 2) BGG_PTQ1(H2, 8); else BGG_PTQ1(1, 8);
+        continue;
       }
-#undef BGG_PTQ1
     }
+#define BGG_PTQ1(H)                                                                                    \
+  hipLaunchKernelGGL((k_gemv_ptq1<1, H, 8, FUSE>), grid, block, 0, st, packed, d->scale_offset,    \
+                     d->chunks, p.G, d->N, Sg, 1, frag, p.frag_words_per_token, mq, mf, p.gpad, sums, \
+                     t0, ntl, nta, sgb, light, fa, y)
+    if (p.per_slice == 2)
+      BGG_PTQ1(2);
+    else
+      BGG_PTQ1(1);
+#undef BGG_PTQ1
   }
 }
 
@@ -1598,8 +1523,7 @@ void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t
     const int64_t ntl = p.NT - t0 < chunk ? p.NT - t0 : chunk;
     const int64_t nta = p.sgb > 1 ? p.nta : ntl;
     const int sgb = (int)p.sgb;
-    static const int64_t light_env = env_int("BGG_GEMV_LIGHT_FIRST", 1);
-    const int light = light_env && p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
+    const int light = p.Sg > 1 && p.S % p.W != 0 ? 1 : 0;
     const dim3 grid((unsigned)(nta * Sg + (ntl - nta) * sgb));
     if (d->format == BGG_FMT_PTQ1_0) {
       hipLaunchKernelGGL((k_gemv_ptq1_mx<8>), grid, block, 0, st, packed, d->scale_offset,
@@ -1633,13 +1557,6 @@ void launch_gemv_mma(const bgg_weights_desc* d, const GemvPlan& p, const uint8_t
   }
 }
 
-// One-launch GEMV for a single token, per format (BGG_GEMV_FUSE: bit 0
-// PQ2_0, bit 1 PTQ1_0; a cleared bit means prep kernel + GEMV kernel).
-bool gemv_fuse_enabled(int format) {
-  static const int64_t mask = env_int("BGG_GEMV_FUSE", 3);
-  return (mask >> (format == BGG_FMT_PQ2_0 ? 0 : 1)) & 1;
-}
-
 bgg_status gemv_args_check(const char* who, const bgg_weights_desc* d, int64_t M,
                            const void* workspace, size_t workspace_bytes, GemvPlan* plan) {
   bgg_status st = check_desc(d);
@@ -1670,6 +1587,17 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* d, int64_t M) {
   return (size_t)plan_gemv(d, M).total;
 }
 
+bgg_status bgg_gemv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(BGG_ERR_NULL, "bgg_gemv_workspace_reset: NULL workspace");
+  if (!aligned16(workspace) || workspace_bytes % 16)
+    return fail(BGG_ERR_BUFFER, "bgg_gemv_workspace_reset: workspace or size not a multiple of 16 bytes");
+  const uint64_t n16 = std::min<uint64_t>(workspace_bytes, kSumBytes) / 16;
+  if (n16 == 0) return BGG_OK;
+  hipLaunchKernelGGL(k_fill_zero16, dim3((unsigned)std::min<uint64_t>(ceil_div(n16, 256), 2048)), dim3(256), 0,
+                     (hipStream_t)stream, reinterpret_cast<uint4*>(workspace), (int64_t)n16);
+  return hip_check("bgg_gemv_workspace_reset");
+}
+
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
   bgg_status st = check_desc(d);
   if (st) return st;
@@ -1677,9 +1605,6 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
   if (M < 1 || M > BGG_MAX_GEMV_M)
     return fail(BGG_ERR_SHAPE, "bgg_gemv_kernel_name: M must be in 1..16 (got %lld)", (long long)M);
   const GemvPlan p = plan_gemv(d, M);
-  const int mb = gemv_m_bucket(M < kGemvTokens ? M : kGemvTokens);
-  const char* fused =
-      M == 1 && gemv_fuse_enabled(d->format) && !p.mma ? "true" : "false";
   int n;
   if (mxv_supported(d, M)) {
     n = mxv_kernel_name(d, M, out, cap);
@@ -1690,11 +1615,10 @@ bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out,
                      : d->format == BGG_FMT_Q2_0_G64 ? "k_gemv_q2g64_mx"
                                                      : "k_gemv_pq2_mx";
     n = snprintf(out, cap, "%s<%d, 8>", kn, (int)p.per_slice);
-  } else if (d->format == BGG_FMT_PQ2_0) {
-    n = snprintf(out, cap, "k_gemv_pq2<%d, %d, 8, %s>", mb, (int)p.per_slice, fused);
+  } else if (d->format == BGG_FMT_PQ2_0) {  // (K beyond the one-launch kernel's reach)
+    n = snprintf(out, cap, "k_gemv_pq2<1, %d, 8>", (int)p.per_slice);
   } else {
-    const int h = (p.per_slice == 2 && mb == 1) ? 2 : 1;
-    n = snprintf(out, cap, "k_gemv_ptq1<%d, %d, %d, %s>", mb, h, mb >= 4 ? 8 : (int)p.W, fused);
+    n = snprintf(out, cap, "k_gemv_ptq1<1, %d, 8, true>", p.per_slice == 2 ? 2 : 1);
   }
   if (n < 0 || (size_t)n >= cap)
     return fail(BGG_ERR_BUFFER, "bgg_gemv_kernel_name: %zu bytes are too few", cap);
@@ -1731,16 +1655,8 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* d, const void* packed_dev, void*
     launch_gemv_mma(d, p, pk, y, (int)M, ws, s);
     return hip_check("bgg_gemv_run");
   }
-  for (int64_t m0 = 0; m0 < M; m0 += kGemvTokens) {
-    const int mg = (int)(M - m0 < kGemvTokens ? M - m0 : kGemvTokens);
-    switch (gemv_m_bucket(mg)) {
-      case 1: launch_gemv<1, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
-      case 2: launch_gemv<2, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
-      default: launch_gemv<4, false>(d, p, pk, y, m0, mg, ws, FuseArgs{}, s); break;
-    }
-    if ((st = hip_check("bgg_gemv_run"))) return st;
-  }
-  return BGG_OK;
+  launch_gemv1<false>(d, p, pk, y, ws, FuseArgs{}, s);  // (one token: the plan has no mma)
+  return hip_check("bgg_gemv_run");
 }
 
 bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, const void* x_dev,
@@ -1762,10 +1678,10 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
     return mxv_launch(d, packed_dev, x_dev, y_dev, M, (flags & BGG_ROTATE_INPUT) ? 1 : 0, workspace,
                       (hipStream_t)stream);
   }
-  // (the one-launch kernel wants the digit words of a block or period to
-  // fill whole 64-byte lines: a workspace aligned to 64 bytes)
-  if (M != 1 || !gemv_fuse_enabled(d->format) || ((uintptr_t)workspace & 63) ||
-      M >= gemv_mma_min_tokens(d->format)) {
+  // one PTQ1_0 token runs in one launch; everything else not served above
+  // (several PTQ1_0 tokens, five and more PQ2_0 tokens, the sister formats,
+  // PQ2_0 K beyond the one-launch kernel's reach) in two steps
+  if (M != 1 || d->format != BGG_FMT_PTQ1_0) {
     st = bgg_gemv_prepare(d, x_dev, M, flags, workspace, workspace_bytes, stream);
     if (st) return st;
     return bgg_gemv_run(d, packed_dev, y_dev, M, workspace, workspace_bytes, stream);
@@ -1778,15 +1694,11 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* d, const void* packed_dev, c
   if (!aligned16(x_dev)) return fail(BGG_ERR_BUFFER, "bgg_ternary_gemv: misaligned x");
   if (flags & ~(uint32_t)BGG_ROTATE_INPUT)
     return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: unknown flags 0x%x", flags);
-  uint8_t* ws = (uint8_t*)workspace;
   FuseArgs fa;
   fa.x = (const uint16_t*)x_dev;
-  fa.frag = reinterpret_cast<uint32_t*>(ws + p.off_fuse);
-  fa.metaQ = nullptr;
-  fa.metaF = nullptr;
   fa.rotate = (flags & BGG_ROTATE_INPUT) ? 1 : 0;
-  launch_gemv<1, true>(d, p, (const uint8_t*)packed_dev, (uint16_t*)y_dev, 0, 1, ws, fa,
-                       (hipStream_t)stream);
+  launch_gemv1<true>(d, p, (const uint8_t*)packed_dev, (uint16_t*)y_dev, (uint8_t*)workspace, fa,
+                     (hipStream_t)stream);
   return hip_check("bgg_ternary_gemv");
 }
 

@@ -22,10 +22,9 @@ using namespace bgg;
 
 namespace {
 
-// Largest workspace the array serves: 48 MiB covers every format at every
-// token count for K up to 65536, and PQ2_0, Q1_0 and Q2_0_G64 up to K =
-// 131072 (the row words alone take 16 MiB).
-constexpr size_t kScratchBytes = size_t(48) << 20;
+// Largest workspace the array serves: 32 MiB covers every format at every
+// token count for K up to 262144 (the row words alone take 16 MiB).
+constexpr size_t kScratchBytes = size_t(32) << 20;
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) uint8_t scratch[kScratchBytes];

@@ -1,7 +1,8 @@
 // Device unpack: packed device layout -> int8 weights [N][K] and fp16 scales
 // [N][K/scale_group], through the same decoders the products use (PQ2_0 and
-// Q2_0_g64 nibble spreading, PTQ1_0 base-3 LUT in LDS, Q1_0 bits).  For
-// checking; not on the hot path.
+// Q2_0_g64 nibble spreading; PTQ1_0 through the one-token GEMV's LDS table,
+// built by the same builder and read with the same addressing; Q1_0 bits).
+// For checking; not on the hot path.
 //
 // Packings: allhereai.com/news/1346, packing paragraph (PQ2_0 one trit per
 // 2-bit slot, PTQ1_0 compact); wmrh.cn/news/471187, section 关键机制 (five
@@ -17,9 +18,10 @@ __global__ void __launch_bounds__(256)
     k_unpack(const uint8_t* __restrict__ packed, uint64_t scale_offset, int64_t NT, int64_t C,
              int64_t G, int64_t N, int64_t K, int8_t* __restrict__ trits,
              uint16_t* __restrict__ scales) {
-  __shared__ uint32_t lut[FMT == BGG_FMT_PTQ1_0 ? 256 * kLutCopies : 1];
+  __shared__ uint32_t lut[FMT == BGG_FMT_PTQ1_0 ? 256 * kLutRowBytes / 4 : 1];
+  __shared__ uint32_t lut_seed[FMT == BGG_FMT_PTQ1_0 ? 256 : 1];
   if (FMT == BGG_FMT_PTQ1_0) {
-    build_lut(lut);
+    build_lut32(lut, lut_seed);
     __syncthreads();
   }
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -49,13 +51,20 @@ __global__ void __launch_bounds__(256)
         }
       }
     } else {
+      const uint32_t lane_off = lut_lane_off((int)(threadIdx.x & 63));
+      const char* lbase = reinterpret_cast<const char*>(lut);
 #pragma unroll
       for (int b = 0; b < 16; ++b) {
-        const uint32_t e = lut[((cw[b >> 2] >> (8 * (b & 3))) & 0xFFu) * kLutCopies];
+        const uint32_t w = cw[b >> 2];
+        const uint32_t addr = (b & 3) == 0 ? lut_addr<0>(w, lane_off)
+                              : (b & 3) == 1 ? lut_addr<1>(w, lane_off)
+                              : (b & 3) == 2 ? lut_addr<2>(w, lane_off)
+                                             : lut_addr<3>(w, lane_off);
+        const uint32_t e = *reinterpret_cast<const uint32_t*>(lbase + addr);  // five signed trit nibbles
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
           const int64_t k = (c * 16 + b) * 5 + i;
-          if (k < K) out[k] = (int8_t)((int)((e >> (4 * i)) & 15u) - 1);
+          if (k < K) out[k] = (int8_t)((int)(e << (28 - 4 * i)) >> 28);
         }
       }
     }

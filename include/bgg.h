@@ -133,7 +133,9 @@ typedef struct bgg_weights_desc {
   int64_t scales;        /* scales per row: K / scale_group */
 } bgg_weights_desc;
 
-/* Fill *out for a format and shape.  Host only, no side effects.
+/* Fill *out for a format and shape: the sizes of [A packing paragraph] and
+ * [C] (bits per weight: 2 + 16/128 for PQ2_0, 8/5 + 16/128 for PTQ1_0) and
+ * the device layout above.  Host only, no side effects.
  * Errors: BGG_ERR_NULL, BGG_ERR_FORMAT, BGG_ERR_SHAPE. */
 bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* out);
 
@@ -148,8 +150,8 @@ bgg_status bgg_describe(int32_t format, int64_t N, int64_t K, bgg_weights_desc* 
 bgg_status bgg_pack_weights(const bgg_weights_desc* desc, const int8_t* trits,
                             const uint16_t* scales, void* packed);
 
-/* Lay out canonical row-stream bytes (the format's file form) in the device
- * layout without decoding them.
+/* Lay out canonical row-stream bytes (the format's file form: the packings
+ * of [A packing paragraph; C]) in the device layout without decoding them.
  *   canonical  host uint8 [N][desc->row_bytes]
  *   scales     host fp16 bits [N][K/scale_group]
  *   packed     host buffer of desc->total_bytes
@@ -157,13 +159,17 @@ bgg_status bgg_pack_weights(const bgg_weights_desc* desc, const int8_t* trits,
 bgg_status bgg_repack_canonical(const bgg_weights_desc* desc, const uint8_t* canonical,
                                 const uint16_t* scales, void* packed);
 
-/* Check a host copy of a packed buffer: every code valid, padding as laid
- * out, every scale a finite fp16.  Errors: BGG_ERR_NULL, BGG_ERR_DESC,
- * BGG_ERR_PACKED_BYTE, BGG_ERR_SCALE. */
+/* Check a host copy of a packed buffer: every code valid for its packing
+ * [A packing paragraph; C: a PTQ1_0 byte holds five base-3 digits, so bytes
+ * past 242 are invalid; a PQ2_0 code 3 is invalid], padding as laid out,
+ * every scale a finite fp16 [A method paragraph].  Errors: BGG_ERR_NULL,
+ * BGG_ERR_DESC, BGG_ERR_PACKED_BYTE, BGG_ERR_SCALE. */
 bgg_status bgg_validate_packed(const bgg_weights_desc* desc, const void* packed);
 
-/* Decode a packed device buffer back to trits and scales with the same
- * device decoders the products use (for checking; not on the hot path).
+/* Decode a packed device buffer back to trits and scales [A packing
+ * paragraph; C] with the same device decoders the products use (PTQ1_0:
+ * the one-token GEMV's LDS table, same builder, same addressing), for
+ * checking; not on the hot path.
  *   packed_dev  device, desc->total_bytes
  *   trits_dev   device int8 [N][K]; scales_dev device fp16 bits [N][K/scale_group]
  * Invalid codes decode as t = 0.  Errors: BGG_ERR_NULL, BGG_ERR_DESC,
@@ -200,8 +206,19 @@ bgg_status bgg_rotate_ternarize(const void* w_dev, int64_t N, int64_t K, int8_t*
                                 uint16_t* scales_dev, void* stream);
 
 /* Device workspace bytes that bgg_ternary_gemv needs for M tokens (0 on a
- * bad descriptor or M outside 1..16). */
+ * bad descriptor, M outside 1..16, or K beyond what one call splits: K up
+ * to 516096, 322560 for PTQ1_0).  Bookkeeping of this interface, no page
+ * passage. */
 size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
+
+/* Set the row words at the start of a GEMV workspace (the first
+ * min(workspace_bytes, 16 MiB)) to zero on `stream`, with a fill kernel
+ * (no memset node, so it may be captured in a graph).  For a new
+ * workspace, one used for anything else, or one whose last GEMV call
+ * failed; every successful GEMV call leaves the words zero by itself.
+ * Bookkeeping of this interface, no page passage.
+ * Errors: BGG_ERR_NULL, BGG_ERR_BUFFER (misaligned), BGG_ERR_HIP. */
+bgg_status bgg_gemv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode-time product, 1 <= M <= 16 tokens: y = x' (S*T)^T with x' the
@@ -212,13 +229,13 @@ size_t bgg_gemv_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *               else already rotated)
  *   y_dev       device fp16 [M][N]
  *   workspace   device buffer of at least bgg_gemv_workspace_size(desc, M)
- *               bytes, 16-byte aligned (64-byte aligned lets a PTQ1_0 token
- *               run in one launch).  Its first 16 MiB hold the row words
+ *               bytes, 16-byte aligned.  Its first 16 MiB hold the row words
  *               of launches that split K (fixed-point partial sums, 8 MiB,
  *               then 8 MiB of coarse words), which must be zero when a call
- *               starts: zero-fill a new workspace once; every GEMV call (any
- *               format, K, M or N) leaves them zero again.  A workspace used
- *               for anything else in between must be zero-filled again.
+ *               starts: zero-fill a new workspace once (or call
+ *               bgg_gemv_workspace_reset); every GEMV call (any format, K, M
+ *               or N) leaves them zero again.  A workspace used for anything
+ *               else in between, or after a failed call, must be reset.
  *               The rest is scratch (encoded activations).
  * One launch transforms and encodes the activations and computes y (PQ2_0
  * up to 4 tokens, PTQ1_0 one token); otherwise it is bgg_gemv_prepare
@@ -245,11 +262,11 @@ bgg_status bgg_ternary_gemv(const bgg_weights_desc* desc, const void* packed_dev
  * bgg_ternary_gemv for callers that cannot allocate device memory (code
  * under graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same product, kernels and bits, with no workspace
- * argument.  Its workspace is a static device array of 48 MiB per GPU (held
+ * argument.  Its workspace is a static device array of 32 MiB per GPU (held
  * by each GPU the library runs on until the process ends); a shape whose
  * bgg_gemv_workspace_size exceeds that is rejected with BGG_ERR_SHAPE
- * before anything is enqueued (48 MiB serves every format and M for K up to
- * 65536).  The call allocates nothing: the array's address on the current
+ * before anything is enqueued (32 MiB serves every format and M for K up to
+ * 262144).  The call allocates nothing: the array's address on the current
  * device is looked up once, and the first call on a device clears the
  * array on `stream` ahead of its own kernels.  All calls on one GPU share
  * the array, so calls that overlap in time on one GPU race; calls that do
@@ -262,8 +279,9 @@ bgg_status bgg_ternary_gemv_noalloc(const bgg_weights_desc* desc, const void* pa
                                     void* stream);
 
 /*
- * The two halves of bgg_ternary_gemv, for projections that share an input
- * (q, k and v, or gate and up, read the same x).
+ * The two halves of bgg_ternary_gemv [A method and runtime paragraphs; B],
+ * for projections that share an input (q, k and v, or gate and up, read the
+ * same x): the activation transform of [A runtime paragraph] done once.
  *
  * bgg_gemv_prepare: transform (with BGG_ROTATE_INPUT) and encode the M
  * activation rows x_dev (fp16 [M][K]) into `workspace`.  What it writes
@@ -282,21 +300,20 @@ bgg_status bgg_gemv_run(const bgg_weights_desc* desc, const void* packed_dev, vo
                         int64_t M, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The name under which a profiler lists the GEMV kernel that
- * bgg_ternary_gemv launches for the first group of up to four of M tokens,
- * e.g. "k_gemv_ptq1<1, 1, 8, true>" (host only; for matching profiles to
- * calls).  The last template argument is true for the one-launch kernel
- * that also encodes the activations (M == 1) and false for the kernel that
- * reads a preparation (bgg_gemv_run launches that one, with the same other
- * arguments).  2..16 tokens (every M for Q1_0 and Q2_0_G64) name the
- * matrix-core kernel, e.g. "k_gemv_pq2_mx<5, 8>", "k_gemv_ptq1_mx<8>",
- * "k_gemv_q1_mx<5, 8>" or "k_gemv_q2g64_mx<4, 8>", which covers all M
- * tokens in one launch after the preparation kernel "k_gemv_prep_mx<...>".
+ * bgg_ternary_gemv launches for M tokens (host only, bookkeeping of this
+ * interface, no page passage; for matching profiles to calls): PQ2_0 with
+ * one token "k_mxv1_pq2<5, T>" and two to four "k_mxv_pq2<8>" (one launch
+ * that also transforms x); PTQ1_0 with one token "k_gemv_ptq1<1, H, 8,
+ * true>" (one launch); otherwise the matrix-core kernel that follows the
+ * preparation kernel "k_gemv_prep_mx<...>", e.g. "k_gemv_pq2_mx<5, 8>",
+ * "k_gemv_ptq1_mx<8>", "k_gemv_q1_mx<5, 8>" or "k_gemv_q2g64_mx<4, 8>".
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_SHAPE, BGG_ERR_BUFFER (cap too
  * small for the name and its terminating zero). */
 bgg_status bgg_gemv_kernel_name(const bgg_weights_desc* desc, int64_t M, char* out, size_t cap);
 
 /* Device workspace bytes that bgg_ternary_gemm uses at most for M tokens
- * (0 on a bad descriptor or M < 1). */
+ * (0 on a bad descriptor or M < 1).  Bookkeeping of this interface, no page
+ * passage. */
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
 
 /*
@@ -321,13 +338,14 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* desc, const void* packed_dev
                             const void* x_dev, void* y_dev, int64_t M, uint32_t flags,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static English name of a status. */
+/* Static English name of a status (bookkeeping, no page passage). */
 const char* bgg_status_string(int32_t status);
 
-/* Details of the last error raised on the calling thread ("" if none). */
+/* Details of the last error raised on the calling thread ("" if none;
+ * bookkeeping, no page passage). */
 const char* bgg_last_error(void);
 
-/* BGG_DESC_VERSION of the loaded library. */
+/* BGG_DESC_VERSION of the loaded library (bookkeeping, no page passage). */
 uint32_t bgg_abi_version(void);
 
 #ifdef __cplusplus

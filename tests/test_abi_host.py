@@ -211,7 +211,7 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 17, 1, 16, wsz, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 4, 16, wsz, None) == 3
     assert lib.bgg_ternary_gemv(ctypes.addressof(d), 16, 16, 16, 1, 1, 16, 8, None) == 6
-    # the no-allocation variant: shape checks, its 48 MiB limit and NULL
+    # the no-allocation variant: shape checks, its 32 MiB limit and NULL
     # buffers, all before any device work
     lib.bgg_ternary_gemv_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_uint32,
                                                                      ctypes.c_void_p]
@@ -219,8 +219,8 @@ def test_null_pointers_are_errors_not_crashes():
     assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), 16, 16, 16, 0, 1, None) == 3
     assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), 16, 16, 16, 17, 1, None) == 3
     assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(d), None, 16, 16, 1, 1, None) == 1
-    big = bgg.bgg_describe("PTQ1_0", 128, 131072)
-    assert bgg.bgg_gemv_workspace_size(big, 16) > 48 << 20
+    big = bgg.bgg_describe("PQ2_0", 128, 516096)
+    assert bgg.bgg_gemv_workspace_size(big, 16) > 32 << 20
     assert lib.bgg_ternary_gemv_noalloc(ctypes.addressof(big), 16, 16, 16, 16, 1, None) == 3
     lib.bgg_last_error.restype = ctypes.c_char_p
     assert b"static workspace" in lib.bgg_last_error()
@@ -247,3 +247,46 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read().splitlines()
     hip = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def _declarations_with_comments():
+    """(function name, the comment block right above its declaration) for
+    every function include/bgg.h declares."""
+    text = open(HEADER).read()
+    out = []
+    for m in re.finditer(r"\n((?:bgg_status|size_t|const char\*|uint32_t)\s+(bgg_\w+)\()", text):
+        before = text[:m.start() + 1]
+        c1 = before.rfind("*/") + 2
+        # only declarations (which may share one comment) between the last
+        # comment and this declaration
+        between = before[c1:].strip()
+        assert all(ln.strip().endswith((",", ");", "(")) or ln.strip().startswith(("bgg_", "size_t", "void*",
+                   "int", "const", "uint"))
+                   for ln in between.splitlines() if ln.strip()), f"{m.group(2)}: no comment above it"
+        out.append((m.group(2), before[before.rfind("/*", 0, c1):c1]))
+    return out
+
+
+def test_every_declaration_cites_a_passage_or_says_it_has_none():
+    """Each exported call's comment cites the page passage it implements
+    ([A ...], [B ...], [C ...]: the sources listed at the top of the
+    header), or says that it is bookkeeping of the interface with no
+    passage."""
+    decls = _declarations_with_comments()
+    assert set(bgg.EXPORTED) <= {name for name, _ in decls}
+    for name, comment in decls:
+        flat = " ".join(ln.strip().lstrip("/*").strip() for ln in comment.splitlines())
+        cites = re.search(r"\[(A|B|C)[ \];]", flat) is not None
+        none = "no page passage" in flat
+        # (the no-allocation variant names the callers it is for instead)
+        for_callers = name == "bgg_ternary_gemv_noalloc" and "cannot allocate" in flat
+        assert cites or none or for_callers, name
+
+
+def test_workspace_reset_argument_errors():
+    lib = ctypes.CDLL(bgg.LIB_PATH)
+    lib.bgg_gemv_workspace_reset.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.bgg_gemv_workspace_reset(None, 256, None) == 1
+    assert lib.bgg_gemv_workspace_reset(8, 256, None) == 6
+    assert lib.bgg_gemv_workspace_reset(16, 100, None) == 6
+    assert lib.bgg_gemv_workspace_reset(16, 0, None) == 0  # nothing to clear

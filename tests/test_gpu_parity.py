@@ -612,3 +612,26 @@ def test_gemv_rows_beyond_one_launch(env, fmt):
         assert np.all(relerr(y[:, rows], ref) <= TOL), f"M={M}"
         words = ws[:16 << 20].view(torch.int64)
         assert int(torch.count_nonzero(words)) == 0, f"M={M}: row words left non-zero"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_workspace_reset(env, fmt):
+    """A workspace filled with other data: bgg_gemv_workspace_reset zeroes
+    its row words (and leaves the rest alone), after which a GEMV whose K is
+    split over workgroups (the row words in use) matches the oracle for one
+    and three tokens."""
+    bgg, torch = env
+    N, K = 300, 5120
+    say(f"gemv workspace reset {fmt}")
+    T, S = gen_matrix(251, 1, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d.desc, 3))
+    ws.fill_(0x5A)
+    bgg.bgg_gemv_workspace_reset(ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:16 << 20])) == 0
+    assert bool(torch.all(ws[16 << 20:] == 0x5A))
+    for M in (1, 3):
+        x = synth.activations_f16(251, 2 + M, M, K)
+        y = d.gemv(x, ws=ws)
+        assert np.all(relerr(y, oracle_y(fmt, T, S, x)) <= TOL), f"M={M}"

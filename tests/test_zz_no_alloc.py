@@ -59,9 +59,9 @@ def test_noalloc_matches_workspace_entry(env, fmt, M):
 
 def test_noalloc_rejects_beyond_its_workspace(env):
     bgg, torch = env
-    d = bgg.bgg_describe("PTQ1_0", 128, 131072)
-    assert bgg.bgg_gemv_workspace_size(d, 16) > 48 << 20
-    x = torch.zeros((16, 131072), dtype=torch.float16, device="cuda")
+    d = bgg.bgg_describe("PQ2_0", 128, 516096)
+    assert bgg.bgg_gemv_workspace_size(d, 16) > 32 << 20
+    x = torch.zeros((16, 516096), dtype=torch.float16, device="cuda")
     y = torch.zeros((16, 128), dtype=torch.float16, device="cuda")
     packed = torch.zeros(d.total_bytes, dtype=torch.uint8, device="cuda")
     with pytest.raises(bgg.BggError) as e:
