@@ -154,12 +154,26 @@ __device__ __forceinline__ uint32_t ptq1_codes10(uint32_t b) {
   for (int i = 0; i < 5; ++i) r |= ((c >> (4 * i)) & 3u) << (2 * i);
   return r;
 }
+// The same five trits as fp4 (e2m1) matrix-core operands, one per nibble
+// 0..4: +1 = 0x2 (1.0), -1 = 0xA (-1.0), 0 = 0x0; nibbles 5..7 are zero.
+__device__ __forceinline__ uint32_t ptq1_e2m1_nibbles(uint32_t b) {
+  const uint32_t c = ptq1_entry(b);
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t ci = (c >> (4 * i)) & 15u;
+    r |= (ci == 2u ? 0x2u : ci == 0u ? 0xAu : 0u) << (4 * i);
+  }
+  return r;
+}
 // Entry forms of the table below.
 constexpr int kLutTrits = 0;  // signed trit nibbles (ptq1_trit_nibbles)
 constexpr int kLutCodes = 1;  // 2-bit codes (ptq1_codes10)
+constexpr int kLutE2m1 = 2;   // e2m1 nibbles (ptq1_e2m1_nibbles)
 template <int FORM>
 __device__ __forceinline__ uint32_t ptq1_lut_entry(uint32_t b) {
-  return FORM == kLutCodes ? ptq1_codes10(b) : ptq1_trit_nibbles(b);
+  return FORM == kLutCodes ? ptq1_codes10(b) : FORM == kLutE2m1 ? ptq1_e2m1_nibbles(b)
+                                                                : ptq1_trit_nibbles(b);
 }
 // Built in two steps: the first 256 threads each decode one byte value into
 // seed[], then (after a barrier) every thread copies entries out, 16 bytes

@@ -52,6 +52,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -514,6 +515,272 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// PTQ1_0, one token: k_mxv1_ptq1<WP>.  A workgroup takes WT = 8 / WP 64-row
+// tiles and WP periods of K (a period is 640 trits = 5 groups = 128 row
+// bytes = 8 chunks); wave w multiplies tile w % WT of period w / WT.  After
+// issuing its loads every wave writes its share of the byte table, and the
+// first waves encode the workgroup's activations straight into matrix-core
+// operands in LDS; one barrier, then the waves multiply.
+//
+// Weights (B, fp4): lane (col, kg) loads chunk 4 h + kg of row 16 b + col
+// for each half h of the period (one 16-byte load); dword u of it feeds
+// matrix operation u of (h, b): B lane (col, kg), dword r, nibble n is trit
+// n of byte 4 u + r of that chunk, looked up in an LDS table of e2m1
+// nibbles (t = +-1 -> +-1.0, t = 0 and nibbles 5-7 -> 0; B scale 1).  So K
+// 32 kg + 8 r + n of operation (h, u) is trit 80 (4 h + kg) + 20 u + 5 r + n
+// of the period.
+//
+// Activations (A, fp8): lane (row i, kgA) bytes 0-15 are K 16 kgA .. +15,
+// i.e. the ten trits of piece j = 32 h + 8 (kgA >> 1) + 2 u + (kgA & 1) of
+// the period (trits 10 j .. 10 j + 4 in bytes 0-4, 10 j + 5 .. 10 j + 9 in
+// bytes 8-12, the rest zero), bytes 16-31 those of piece j + 16.  A half of
+// a period spans three groups, 2 h .. 2 h + 2: row 4 s + d (s, d < 3)
+// carries digit d of the trits of group 2 h + s and zero elsewhere, with
+// that group's E8M0 scale 2^(e - 14 + 10 - 5 d).  The four operations u of
+// (h, b) chain their accumulators; output lane (col, s < 3) then holds in
+// its rows 4 s .. 4 s + 2 the digit sums of group 2 h + s for weight row
+// 16 b + col, which add up exactly (multiples of 2^(e-14) below 2^21 of
+// them); the group's fp16 scale multiplies the sum into an fp32 accumulator
+// (group 2 of a period, cut by the half boundary, once per half).
+//
+// LDS: the e2m1 table, 256 rows of 256 bytes (bytes 0-127 of row v hold 32
+// copies of entry v), and in the free upper halves ("hole rows" of 128 bytes
+// at row * 256 + 128), per period slot p, rows from 96 p:
+//   * A operands: unit U = 4 h + u in rows 10 U .. 10 U + 8: row
+//     q = 3 d + s holds digit plane d of slot s, the half hf of lane group
+//     kgA in the 16 bytes at (32 kgA + 16 hf + 16 q) mod 128 -- rotated by
+//     row, so that the lanes of one A column read different banks; row 9
+//     stays zero and serves the lanes of the unused rows (s = 3 or d = 3),
+//     rotated by 2 (rows 0-7 of A) or 1 (rows 8-15) for the same reason;
+//   * row 80: the groups' exponents e (5 ints) and NaN terms (5 floats).
+// Rows 192 .. 207 take the waves' partial rows for the final reduction.
+// ---------------------------------------------------------------------------
+constexpr int kPtqRowsPerPeriod = 96;
+constexpr int kPtqMetaRow = 80;
+constexpr int kPtqRedRow = 192;
+
+__device__ __forceinline__ uint32_t hole_addr(int row) { return (uint32_t)row * kLutRowBytes + 128u; }
+
+template <int WP>
+__global__ void __launch_bounds__(64 * kWaves) k_mxv1_ptq1(MxvArgs a) {
+  constexpr int WT = kWaves / WP;
+  static_assert(WP >= 1 && WP <= 2 && kWaves % WP == 0, "one or two periods per workgroup");
+  static_assert(kPeriodGroups * WP <= 4 * kWaves, "one pass encodes every group");
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutRowBytes / 4];
+  char* const lds = reinterpret_cast<char*>(lut);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, kg = lane >> 4;
+  const int64_t rr = blockIdx.x % a.RR, sl = blockIdx.x / a.RR;
+  const int64_t NP = ceil_div(a.G, kPeriodGroups);
+  const int ti = wave % WT, ps = wave / WT;
+  const int64_t lt = rr * WT + ti;
+  const int64_t tile = a.tile0 + (lt < a.NTl ? lt : a.NTl - 1);
+  const int64_t per = sl * WP + ps;  // this wave's period
+  const bool has = per < NP;        // (wave-uniform)
+  const int64_t pc = has ? per : NP - 1;
+
+  // 1. x of the group this lane quarter encodes: group gq = 4 wave + q of
+  //    the workgroup's 5 WP (period slot gq / 5, group gq % 5); every wave
+  //    loads (the rest re-read group 0), so that the load counts are uniform
+  const int gq = 4 * wave + kg;
+  const int eps = gq / kPeriodGroups, eg = gq % kPeriodGroups;
+  const int64_t egg = (sl * WP + eps) * kPeriodGroups + eg;
+  const bool enc = gq < kPeriodGroups * WP;
+  const bool xval = enc && egg < a.G;
+  const uint4 xraw = *reinterpret_cast<const uint4*>(a.x + (xval ? egg : 0) * kGroup + 8 * col);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. scales: lane (col, q) of half h, block b takes row 16 b + col, group
+  //    2 h + q of the period (q < 3); then the weights: chunk 4 h + kg of
+  //    row 16 b + col (chunks past the row re-read the last one)
+  const uint16_t* sbase = reinterpret_cast<const uint16_t*>(a.packed + a.scale_offset) + tile * a.G * kTile;
+  uint32_t sraw[2][kBlocks];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t g = pc * kPeriodGroups + 2 * h + (kg < 3 ? kg : 2);
+    const uint16_t* srow = sbase + (g < a.G ? g : a.G - 1) * kTile;
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) sraw[h][b] = ld_scale_pair(srow + 16 * b, col);
+  }
+  // (the second half's weights are issued after the barrier, between the
+  // first half's matrix operations: a wave that queues loads waits until the
+  // CU has room for them, and its table and encoding work should not wait)
+  uint4 w[2][kBlocks];
+  const uint4* wsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int64_t c = pc * kPeriodChunks + 4 * h + kg;
+    c = c < a.C ? c : a.C - 1;
+    wsrc[h] = reinterpret_cast<const uint4*>(a.packed) + (tile * a.C + c) * kTile + col;
+  }
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) w[0][b] = ld_stream(wsrc[0] + 16 * b);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the table: thread t writes copies 16 (t & 1) .. of entry t / 2
+  {
+    const int e = threadIdx.x >> 1;
+    const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
+#pragma unroll
+    for (int q = 0; q < kLutCopies32 / 8; ++q)
+      reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (threadIdx.x & 1) * (kLutCopies32 / 8) + q] =
+          make_uint4(v, v, v, v);
+  }
+  // the zero row of every unit
+  if (threadIdx.x < 64 * WP)
+    *reinterpret_cast<uint4*>(lds + hole_addr((threadIdx.x / 64) * kPtqRowsPerPeriod + 10 * ((threadIdx.x / 8) % 8) +
+                                              9) + 16 * (threadIdx.x % 8)) = make_uint4(0, 0, 0, 0);
+  // 4. encode: the lanes of group (eps, eg) clear the rows of its slots (slot
+  //    eg of half 0 for eg <= 2, slot eg - 2 of half 1 for eg >= 2: 4 units x
+  //    3 planes each), then write its digits: trit P = 128 eg + 8 col + i of
+  //    the period goes to half h = P / 320, piece j = (P - 320 h) / 10, byte
+  //    pr = (P - 320 h) % 10 of it (bytes 0-4 and 8-12)
+  if (enc) {
+    const int prow = eps * kPtqRowsPerPeriod;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s = eg - 2 * h;
+      if (s < 0 || s > 2) continue;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const int i = col + 16 * k, row = i / 8, u = row / 3, d = row % 3;
+        *reinterpret_cast<uint4*>(lds + hole_addr(prow + 10 * (4 * h + u) + 3 * d + s) + 16 * (i % 8)) =
+            make_uint4(0, 0, 0, 0);
+      }
+    }
+    const BlockCode16 c = encode_block16(xval ? xraw : make_uint4(0, 0, 0, 0), a.rotate, col);
+    uint32_t wd[3][2];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      wd[d][0] = e4m3_word(c.d[d][0], c.d[d][1], c.d[d][2], c.d[d][3]);
+      wd[d][1] = e4m3_word(c.d[d][4], c.d[d][5], c.d[d][6], c.d[d][7]);
+    }
+    wave_lds_sync();  // (the clears land before the digits)
+    const int P0 = kGroup * eg + 8 * col;
+    const int h = P0 / 320, s = eg - 2 * h, Q0 = P0 - 320 * h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int Q = Q0 + i, jp = Q / 10, pr = Q % 10;
+      const int hf = jp >> 4, r = jp & 15, u = (r >> 1) & 3, kgA = 2 * (r >> 3) + (r & 1);
+      const int at = 32 * kgA + 16 * hf + pr + (pr >= 5 ? 3 : 0);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        const int q = 3 * d + s;
+        lds[hole_addr(prow + 10 * (4 * h + u) + q) + ((at + 16 * q) & 127)] = (char)(wd[d][i >> 2] >> (8 * (i & 3)));
+      }
+    }
+    if (col == 0) {
+      int* meta = reinterpret_cast<int*>(lds + hole_addr(prow + kPtqMetaRow));
+      meta[eg] = c.e;
+      reinterpret_cast<float*>(meta)[kPeriodGroups + eg] = c.corr != c.corr ? c.corr : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // 5. per half: four chained operations per row block, then lane (col,
+  //    s < 3) scales its group's sum.  The operands of step k + 1 (its A
+  //    columns and table words) are fetched before the operations of step k
+  //    are issued, so that LDS latency overlaps the matrix cores.
+  float acc[kBlocks] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (has) {
+    const int arow = lane & 15, as = arow >> 2, ad = arow & 3;
+    const bool aon = as < 3 && ad < 3;
+    const int aq = aon ? 3 * ad + as : 9, rot = aon ? aq : (arow < 8 ? 2 : 1);
+    const uint32_t arow0 = hole_addr(ps * kPtqRowsPerPeriod + aq);
+    const uint32_t aoff0 = (32 * kg + 16 * rot) & 127, aoff1 = (32 * kg + 16 + 16 * rot) & 127;
+    const int* meta = reinterpret_cast<const int*>(lds + hole_addr(ps * kPtqRowsPerPeriod + kPtqMetaRow));
+    const uint32_t loff = lut_lane_off(lane);
+    int sa[2];
+    float fl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sa[h] = aon ? 123 + meta[2 * h + as] - 5 * ad : 127;
+      fl[h] = kg < 3 ? reinterpret_cast<const float*>(meta)[kPeriodGroups + 2 * h + kg] : 0.0f;
+    }
+    i32x8 A[2];
+    i32x4 B[2][kBlocks];
+    auto fetch = [&](int k, i32x8& Ak, i32x4 (&Bk)[kBlocks]) {
+      const int h = k >> 2, u = k & 3;
+      const char* ar = lds + arow0 + 10 * k * kLutRowBytes;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(ar + aoff0);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(ar + aoff1);
+      Ak = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) {
+        const uint32_t wd = u == 0 ? w[h][b].x : u == 1 ? w[h][b].y : u == 2 ? w[h][b].z : w[h][b].w;
+        Bk[b] = i32x4{*reinterpret_cast<const int*>(lds + lut_addr<0>(wd, loff)),
+                      *reinterpret_cast<const int*>(lds + lut_addr<1>(wd, loff)),
+                      *reinterpret_cast<const int*>(lds + lut_addr<2>(wd, loff)),
+                      *reinterpret_cast<const int*>(lds + lut_addr<3>(wd, loff))};
+      }
+    };
+    f32x4 D[kBlocks];
+    fetch(0, A[0], B[0]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int cur = k & 1, h = k >> 2, u = k & 3;
+      if (k < 4) w[1][k] = ld_stream(wsrc[1] + 16 * k);
+      if (k + 1 < 8 && k != 3) fetch(k + 1, A[cur ^ 1], B[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) {
+        const i32x8 Bv = {B[cur][b][0], B[cur][b][1], B[cur][b][2], B[cur][b][3], 0, 0, 0, 0};
+        const f32x4 C = u == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : D[b];
+        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[cur], Bv, C, 0, 4, 0, sa[h], 0, 127);
+      }
+      if (k == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(4, A[0], B[0]);  // (waits for the second half's weights)
+      }
+      if (u == 3) {
+        const bool gon = kg < 3 && pc * kPeriodGroups + 2 * h + kg < a.G;
+#pragma unroll
+        for (int b = 0; b < kBlocks; ++b) {
+          const float s = gon ? scale_half(sraw[h][b], col) : 0.0f;
+          acc[b] = fmaf(s, (D[b][0] + D[b][1]) + (D[b][2] + fl[h]), acc[b]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // 6. the wave's rows: its four lane groups' partials (slots) added, then
+  //    the WP waves of a tile in a fixed order
+#pragma unroll
+  for (int b = 0; b < kBlocks; ++b) {
+    pin(acc[b]);
+    acc[b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(acc[b])));
+    acc[b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(acc[b])));
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) {
+      const int r = 16 * b + col;
+      *reinterpret_cast<float*>(lds + hole_addr(kPtqRedRow + 2 * wave + (r >> 5)) + 4 * (r & 31)) = acc[b];
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < WT * kTile; r += 64 * kWaves) {
+    const int t = r / kTile, rl = r % kTile;
+    float v = 0.0f;
+#pragma unroll
+    for (int p = 0; p < WP; ++p)
+      v += *reinterpret_cast<const float*>(lds + hole_addr(kPtqRedRow + 2 * (p * WT + t) + (rl >> 5)) + 4 * (rl & 31));
+    const int64_t ltt = rr * WT + t;
+    if (ltt >= a.NTl) continue;
+    const int64_t lrow = ltt * kTile + rl;
+    const int64_t row = a.tile0 * kTile + lrow;
+    if (row >= a.N) continue;
+    if (a.P == 1)
+      a.y[row] = f2h(v);
+    else
+      add_partial(a.rw, 0, lrow, a.P, v, a.y + row);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // plan and launch
 // ---------------------------------------------------------------------------
 constexpr int64_t kTargetWgs = 160;  // workgroups per launch the slicing aims at
@@ -536,18 +803,24 @@ K1Split k1_split(int64_t units, int64_t umax, int64_t RR) {
   return K1Split{ceil_div(units, GW), GW};
 }
 
+// PTQ1_0 one-token kernel: periods per workgroup.
+constexpr int kPtqWp = 1;
+
 }  // namespace
 
 namespace bgg {
 
 bool mxv_supported(const bgg_weights_desc* d, int64_t M) {
   // (K short enough for the row words' arrival count at the widest ranges)
+  if (d->format == BGG_FMT_PTQ1_0)
+    return M == 1 && ceil_div(ceil_div(d->groups, kPeriodGroups), kPtqWp) <= kMaxSlices;
   return d->format == BGG_FMT_PQ2_0 && M >= 1 && M <= 4 && d->groups <= (M == 1 ? 24 : kPqGsMax) * kMaxSlices;
 }
 
 uint64_t mxv_workspace_bytes() { return 2 * kRowWordBytes; }
 
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
+  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv1_ptq1<%d>", kPtqWp);
   if (M == 1) return snprintf(out, cap, "k_mxv1_pq2<5, %d>", mxv1_tpw(d));
   return snprintf(out, cap, "k_mxv_pq2<%d>", kPqGsMax);
 }
@@ -567,6 +840,23 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
   a.rw = row_words_of(workspace);
   a.y = (uint16_t*)y;
   const int64_t NT = d->row_tiles;
+  if (d->format == BGG_FMT_PTQ1_0) {
+    // one token: workgroups of 8 / kPtqWp tiles x kPtqWp periods
+    constexpr int WT = kWaves / kPtqWp;
+    const int64_t RRall = ceil_div(NT, WT);
+    a.P = (int)ceil_div(ceil_div(a.G, kPeriodGroups), kPtqWp);
+    if (a.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
+    a.GS = kPtqWp;
+    const int64_t rr_per = a.P > 1 ? kRowWordRows / (WT * kTile) : RRall;
+    for (int64_t r0 = 0; r0 < RRall; r0 += rr_per) {
+      a.RR = std::min(rr_per, RRall - r0);
+      a.tile0 = r0 * WT;
+      a.NTl = std::min<int64_t>(a.RR * WT, NT - a.tile0);
+      const dim3 grid((unsigned)(a.RR * a.P)), block(64 * kWaves);
+      hipLaunchKernelGGL((k_mxv1_ptq1<kPtqWp>), grid, block, 0, st, a);
+    }
+    return hip_check("bgg_ternary_gemv");
+  }
   if (M == 1) {
     // one token: workgroups of TPW tiles x one K range of up to 8 x 5
     // groups (8 x 3 beyond K = 5120, where three groups per wave stream
