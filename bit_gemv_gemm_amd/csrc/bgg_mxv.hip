@@ -429,20 +429,11 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // 4. the second half of the codes
-#pragma unroll
-  for (int g = kHalf; g < GPW; ++g)
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const u32x2* wsrc = reinterpret_cast<const u32x2*>(a.packed) +
-                          ((tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
-#pragma unroll
-      for (int b = 0; b < kBlocks; ++b)
-        w[t][b][g] = __builtin_nontemporal_load(wsrc + (int64_t)(g < ngl ? g : ngl - 1) * (4 * kTile) + b * 32);
-    }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 5. MFMAs: A lanes of rows 0-2 read their digits, the rest are zero
+  // 4. MFMAs: A lanes of rows 0-2 read their digits, the rest are zero.
+  //    The second half of the codes is issued in the first iterations, one
+  //    group per iteration ahead of that iteration's matrix operations: a
+  //    wave that queues loads waits until the CU has room for them, and the
+  //    first groups' operations need not wait with it.
   float acc[TPW][kBlocks];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -452,6 +443,18 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
   const int arow = lane & 15;
 #pragma unroll
   for (int g = 0; g < GPW; ++g) {
+    if (kHalf + g < GPW) {
+      const int gh = kHalf + g;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const u32x2* wsrc = reinterpret_cast<const u32x2*>(a.packed) +
+                            ((tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
+#pragma unroll
+        for (int b = 0; b < kBlocks; ++b)
+          w[t][b][gh] = __builtin_nontemporal_load(wsrc + (int64_t)(gh < ngl ? gh : ngl - 1) * (4 * kTile) + b * 32);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (g < ng) {
       uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
       int sa = 127;
@@ -483,7 +486,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
     }
   }
 
-  // 6. the waves' partial rows, added in wave order
+  // 5. the waves' partial rows, added in wave order
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
