@@ -207,6 +207,95 @@ class Stack:
                                  bgg.BGG_ROTATE_INPUT, self.ws, st)
 
 
+def sister_bench(args, bgg, torch, dev, capture):
+    """The projection matrices (gate_up 17408x5120, down 5120x17408) in the
+    sister formats Q1_0 (sign bits, scale per 128) and Q2_0_G64 (2-bit codes,
+    scale per 64), at M = 1 and M = 16: microseconds per bgg_ternary_gemv
+    call (prepare + matrix-core run) from HIP events around a graph of
+    back-to-back calls that cycle through the weight copies, and GB/s of
+    the format's packed bytes."""
+    import synth
+    w = synth.WORKLOADS["projection"]
+    seed = w["seed"]
+    reps = args.kernel_reps
+    out = {}
+    for fmt in ("Q1_0", "Q2_0_G64"):
+        rows = []
+        for mat in w["matrices"]:
+            T, S = synth.workload_matrix(mat, seed, fmt)
+            d = bgg.bgg_describe(fmt, mat.n, mat.k)
+            host = bgg.bgg_pack_weights(d, T, S)
+            del T, S
+            copies = [bgg.upload(host, dev) for _ in range(args.copies)]
+            x = torch.from_numpy(synth.workload_x(seed, 16, mat.k)).to(dev)
+            y = torch.empty((16, mat.n), dtype=torch.float16, device=dev)
+            ws = bgg.workspace(bgg.bgg_gemv_workspace_size(d, 16), dev)
+            for M in (1, 16):
+                g = capture(lambda st, M=M: [
+                    bgg.bgg_ternary_gemv(d, copies[r % args.copies], x, y, M, bgg.BGG_ROTATE_INPUT,
+                                         ws, st) for r in range(reps)])
+                g.replay()
+                cur = torch.cuda.current_stream()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(cur)
+                g.replay()
+                b.record(cur)
+                b.synchronize()
+                us = a.elapsed_time(b) * 1e3 / reps
+                rows.append(dict(matrix=mat.name, n=mat.n, k=mat.k, m=M,
+                                 kernel=bgg.bgg_gemv_kernel_name(d, M),
+                                 bytes_per_call=int(d.format_bytes), avg_us=round(us, 3),
+                                 gbs=round(d.format_bytes / us / 1e3, 1)))
+                del g
+            del copies
+        step = {}
+        for M in (1, 16):
+            r = [e for e in rows if e["m"] == M]
+            tot_us = sum(e["avg_us"] for e in r)
+            step[f"m{M}"] = dict(us=round(tot_us, 2),
+                                 gbs=round(sum(e["bytes_per_call"] for e in r) / tot_us / 1e3, 1))
+        out[fmt] = dict(calls=rows, gate_up_plus_down=step)
+        log(f"sister {fmt}: " + ", ".join(f"{e['matrix']} M={e['m']} {e['avg_us']:.2f}us "
+                                          f"{e['gbs']:.0f}GB/s" for e in rows))
+    return out
+
+
+def ternarize_bench(args, bgg, torch, dev):
+    """The offline front end on the projection shapes: float32 weights ->
+    trits and fp16 scales (bgg_rotate_ternarize), HIP events around 10
+    back-to-back calls after 3 warm-up calls; GB/s of the algorithmic bytes
+    (4 read + 1 written per weight, 2 written per 128-block)."""
+    import synth
+    w = synth.WORKLOADS["projection"]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for mat in w["matrices"]:
+        W = torch.from_numpy(synth.float_weights(w["seed"], mat.matrix_id, mat.n, mat.k)).to(dev)
+        T = torch.empty((mat.n, mat.k), dtype=torch.int8, device=dev)
+        S = torch.empty((mat.n, mat.k // 128), dtype=torch.float16, device=dev)
+        for _ in range(3):
+            bgg.bgg_rotate_ternarize(W, mat.n, mat.k, T, S, stream)
+        reps = 10
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            bgg.bgg_rotate_ternarize(W, mat.n, mat.k, T, S, stream)
+        b.record(stream)
+        b.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = mat.n * mat.k * 5 + mat.n * (mat.k // 128) * 2
+        rows.append(dict(matrix=mat.name, n=mat.n, k=mat.k, avg_us=round(us, 1), bytes=nbytes,
+                         gbs=round(nbytes / us / 1e3, 1),
+                         frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)))
+        del W, T, S
+    log("ternarize: " + ", ".join(f"{r['matrix']} {r['avg_us']}us {r['gbs']}GB/s" for r in rows))
+    best = max(r["gbs"] for r in rows)
+    return dict(kernel="k_rotate_ternarize", workload="float32 weights of the projection shapes "
+                "-> trits + fp16 scales (rotate, mean-magnitude scale, nearest trit)",
+                shapes=rows, roofline=dict(bound="hbm", achieved=best, peak=HBM_PEAK_GBS,
+                                           unit="GB/s", frac=round(best / HBM_PEAK_GBS, 4)))
+
+
 def stack_breakdown(bgg, torch, stack, capture, reps_layers):
     """Average launch time of each projection of one layer (a graph of
     back-to-back calls of that projection over the stack's layers, HIP
