@@ -564,11 +564,11 @@ constexpr int kPtqRedRow = 192;
 
 __device__ __forceinline__ uint32_t hole_addr(int row) { return (uint32_t)row * kLutRowBytes + 128u; }
 
-template <int WP>
-__global__ void __launch_bounds__(64 * kWaves) k_mxv1_ptq1(MxvArgs a) {
-  constexpr int WT = kWaves / WP;
-  static_assert(WP >= 1 && WP <= 2 && kWaves % WP == 0, "one or two periods per workgroup");
-  static_assert(kPeriodGroups * WP <= 4 * kWaves, "one pass encodes every group");
+template <int NW, int WP>
+__global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
+  constexpr int WT = NW / WP;
+  static_assert(WP >= 1 && WP <= 2 && NW % WP == 0 && NW <= 8, "one or two periods per workgroup");
+  static_assert(kPeriodGroups * WP <= 4 * NW, "one pass encodes every group");
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutRowBytes / 4];
   char* const lds = reinterpret_cast<char*>(lut);
 
@@ -622,14 +622,24 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_ptq1(MxvArgs a) {
   for (int b = 0; b < kBlocks; ++b) w[0][b] = ld_stream(wsrc[0] + 16 * b);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. the table: thread t writes copies 16 (t & 1) .. of entry t / 2
-  {
+  // 3. the table: with 512 threads, thread t writes copies 16 (t & 1) .. of
+  //    entry t / 2; with fewer, every copy of entries t, t + 64 NW, ...
+  if (NW == 8) {
     const int e = threadIdx.x >> 1;
     const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
 #pragma unroll
     for (int q = 0; q < kLutCopies32 / 8; ++q)
       reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (threadIdx.x & 1) * (kLutCopies32 / 8) + q] =
           make_uint4(v, v, v, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 256 / (64 * NW); ++k) {
+      const int e = threadIdx.x + 64 * NW * k;
+      const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
+#pragma unroll
+      for (int q = 0; q < kLutCopies32 / 4; ++q)
+        reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + q] = make_uint4(v, v, v, v);
+    }
   }
   // the zero row of every unit
   if (threadIdx.x < 64 * WP)
@@ -765,7 +775,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_ptq1(MxvArgs a) {
     }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < WT * kTile; r += 64 * kWaves) {
+  for (int r = threadIdx.x; r < WT * kTile; r += 64 * NW) {
     const int t = r / kTile, rl = r % kTile;
     float v = 0.0f;
 #pragma unroll
@@ -806,8 +816,18 @@ K1Split k1_split(int64_t units, int64_t umax, int64_t RR) {
   return K1Split{ceil_div(units, GW), GW};
 }
 
-// PTQ1_0 one-token kernel: periods per workgroup.
+// PTQ1_0 one-token kernel: periods per workgroup, and waves per workgroup:
+// the most (8, 4 or 2) that still give kPtqMinWgs workgroups.  Its matrix
+// phase is bound by the CU's LDS instruction rate (table lookups), so a
+// small projection runs faster on more CUs with fewer waves each.
 constexpr int kPtqWp = 1;
+constexpr int64_t kPtqMinWgs = 160;
+int ptq1_waves(const bgg_weights_desc* d) {
+  const int64_t P = ceil_div(ceil_div(d->groups, kPeriodGroups), kPtqWp);
+  for (int nw : {8, 4})
+    if (ceil_div(d->row_tiles, nw / kPtqWp) * P >= kPtqMinWgs) return nw;
+  return 2;
+}
 
 }  // namespace
 
@@ -823,7 +843,7 @@ bool mxv_supported(const bgg_weights_desc* d, int64_t M) {
 uint64_t mxv_workspace_bytes() { return 2 * kRowWordBytes; }
 
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
-  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv1_ptq1<%d>", kPtqWp);
+  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv1_ptq1<%d, %d>", ptq1_waves(d), kPtqWp);
   if (M == 1) return snprintf(out, cap, "k_mxv1_pq2<5, %d>", mxv1_tpw(d));
   return snprintf(out, cap, "k_mxv_pq2<%d>", kPqGsMax);
 }
@@ -844,8 +864,9 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
   a.y = (uint16_t*)y;
   const int64_t NT = d->row_tiles;
   if (d->format == BGG_FMT_PTQ1_0) {
-    // one token: workgroups of 8 / kPtqWp tiles x kPtqWp periods
-    constexpr int WT = kWaves / kPtqWp;
+    // one token: workgroups of nw / kPtqWp tiles x kPtqWp periods
+    const int nw = ptq1_waves(d);
+    const int WT = nw / kPtqWp;
     const int64_t RRall = ceil_div(NT, WT);
     a.P = (int)ceil_div(ceil_div(a.G, kPeriodGroups), kPtqWp);
     if (a.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
@@ -855,8 +876,13 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
       a.RR = std::min(rr_per, RRall - r0);
       a.tile0 = r0 * WT;
       a.NTl = std::min<int64_t>(a.RR * WT, NT - a.tile0);
-      const dim3 grid((unsigned)(a.RR * a.P)), block(64 * kWaves);
-      hipLaunchKernelGGL((k_mxv1_ptq1<kPtqWp>), grid, block, 0, st, a);
+      const dim3 grid((unsigned)(a.RR * a.P)), block(64 * nw);
+      if (nw == 8)
+        hipLaunchKernelGGL((k_mxv1_ptq1<8, kPtqWp>), grid, block, 0, st, a);
+      else if (nw == 4)
+        hipLaunchKernelGGL((k_mxv1_ptq1<4, kPtqWp>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((k_mxv1_ptq1<2, kPtqWp>), grid, block, 0, st, a);
     }
     return hip_check("bgg_ternary_gemv");
   }
