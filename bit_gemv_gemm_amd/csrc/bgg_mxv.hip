@@ -624,13 +624,15 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
 
   // 3. the table: with 512 threads, thread t writes copies 16 (t & 1) .. of
   //    entry t / 2; with fewer, every copy of entries t, t + 64 NW, ...
+  //    (the 16-byte pieces of a row in an order rotated by the entry, so that
+  //    the lanes of one store, 256 bytes apart, spread over the banks)
   if (NW == 8) {
     const int e = threadIdx.x >> 1;
     const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
 #pragma unroll
     for (int q = 0; q < kLutCopies32 / 8; ++q)
-      reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (threadIdx.x & 1) * (kLutCopies32 / 8) + q] =
-          make_uint4(v, v, v, v);
+      reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (threadIdx.x & 1) * (kLutCopies32 / 8) +
+                                    ((q + e) & (kLutCopies32 / 8 - 1))] = make_uint4(v, v, v, v);
   } else {
 #pragma unroll
     for (int k = 0; k < 256 / (64 * NW); ++k) {
@@ -638,7 +640,8 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
       const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
 #pragma unroll
       for (int q = 0; q < kLutCopies32 / 4; ++q)
-        reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + q] = make_uint4(v, v, v, v);
+        reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + ((q + e) & (kLutCopies32 / 4 - 1))] =
+            make_uint4(v, v, v, v);
     }
   }
   // the zero row of every unit
