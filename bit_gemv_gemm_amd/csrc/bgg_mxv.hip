@@ -807,14 +807,19 @@ int mxv1_tpw(const bgg_weights_desc* d) { return d->row_tiles >= 2 * 128 ? 2 : 1
 // One-token kernel: how many K ranges (each a row-word arrival; a range
 // costs the returning atomics at the end, about 2-3 us of tail) for `units`
 // groups of K of which a workgroup takes at most `umax`:
-// as few as keep a range within umax and give at least kMinWgs workgroups.
+// as few as keep a range within umax and give at least min_wgs workgroups
+// (160 for one-tile workgroups, measured: q 6.2 -> 5.8 us, k/v 4.5 -> 4.1;
+// 96 for two-tile ones, whose projections would otherwise split K: gate/up
+// 9.0 -> 12.1 us with 160).
 struct K1Split {
   int64_t P, GW;
 };
-K1Split k1_split(int64_t units, int64_t umax, int64_t RR) {
-  constexpr int64_t kMinWgs = 96;
-  int64_t P = std::max(ceil_div(units, umax), ceil_div(kMinWgs, RR));
-  P = std::min(P, units);
+K1Split k1_split(int64_t units, int64_t umax, int64_t RR, int64_t min_wgs) {
+  int64_t P = std::max(ceil_div(units, umax), ceil_div(min_wgs, RR));
+  // (at most one range per group, and no more ranges than the row words
+  // count; ceil(units / umax) itself stays within that for every K the
+  // kernel takes)
+  P = std::min({P, units, (int64_t)kMaxSlices});
   const int64_t GW = ceil_div(units, P);
   return K1Split{ceil_div(units, GW), GW};
 }
@@ -896,7 +901,7 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
     const int tpw = mxv1_tpw(d);
     const int64_t RR = ceil_div(NT, tpw);
     constexpr int kGpw = 5;
-    const K1Split sp = k1_split(a.G, a.G <= kWaves * kGpw ? kWaves * kGpw : 24, RR);
+    const K1Split sp = k1_split(a.G, a.G <= kWaves * kGpw ? kWaves * kGpw : 24, RR, tpw == 2 ? 96 : 160);
     if (sp.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
     a.GS = (int)sp.GW;
     a.P = (int)sp.P;

@@ -321,11 +321,14 @@ def test_gemv_tokens_do_not_mix(env, fmt, N, K):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K,M", [(1, 128, 16), (1, 640, 2), (65, 256, 5), (64, 128, 16),
-                                   (4097, 640, 2), (130, 1152, 16), (300, 5248, 9)])
+                                   (4097, 640, 2), (130, 1152, 16), (300, 5248, 9),
+                                   (1, 17408, 1), (64, 8192, 1)])
 def test_gemv_matrix_core_edges(env, fmt, N, K, M):
     """Matrix-core GEMV edge shapes: one row, one 128-group, ragged tiles
     (65 rows; 4097 rows = 64 tiles and one row), K not a multiple of the
-    PTQ1_0 period (5248 = 8 periods and one group); every output checked.
+    PTQ1_0 period (5248 = 8 periods and one group), and one row tile with a
+    long K, which the one-token kernels cut into the most K ranges (up to
+    the 63 the row words count); every output checked.
     With a single output per token the per-row bar would divide by one dot
     product, which can nearly cancel (-9e-5 for one token here); such
     shapes are held to the same bar pooled over all tokens."""
