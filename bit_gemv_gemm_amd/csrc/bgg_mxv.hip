@@ -1,11 +1,12 @@
 // Decode-time GEMV y[M][N] = x'[M][K] . (S*T)[N][K]^T on the gfx950 matrix
-// cores, for the PQ2_0 packing and 1 <= M <= 4 tokens: one launch per call,
-// which also applies the block-128 Walsh-Hadamard transform to x.
+// cores, for 1 <= M <= 4 tokens (PQ2_0) or 1 <= M <= 2 (PTQ1_0): one launch
+// per call, which also applies the block-128 Walsh-Hadamard transform to x.
 //
 // What is computed: allhereai.com/news/1346 ("27B 模型压到 5.95GB…"), method
 // paragraph (trits, one FP16 scale per 128 weights, block-Hadamard-rotated
 // storage), runtime paragraph (the activations get the matching transform at
-// run time) and packing paragraph (PQ2_0: one trit per 2-bit slot);
+// run time) and packing paragraph (PQ2_0: one trit per 2-bit slot; PTQ1_0:
+// five trits per byte);
 // 10100.com/article/156675786 ("Bonsai 2，把27B压进6个G"), section 它怎么做到的.
 //
 // Work split (one MI355X: 256 CUs, 64-lane waves):
@@ -17,6 +18,9 @@
 //   * two to four tokens (k_mxv_pq2): wave w owns one 64-row tile and all 8
 //     waves work on the same K slice, so the slice's activations are
 //     transformed and encoded once per 512 rows and shared through LDS;
+//   * PTQ1_0 (k_mxv_ptq1, one or two tokens): the same split with one
+//     period of K per workgroup; the bytes become fp4 operands through an
+//     LDS table (described with the kernel);
 //   * every wave issues all of its weight loads before it waits for
 //     anything (the x loads of its encode share go first, so that encoding
 //     waits for x only);
@@ -173,6 +177,88 @@ __device__ __forceinline__ uint32_t e4m3_word(float a, float b, float c, float d
   // v_cvt_pk_fp8_f32 (OCP e4m3 on gfx950; the digits are exact e4m3 values)
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// v of lane l ^ m across the whole wave (m = 1 .. 32): DPP within 16-lane
+// rows, a swizzle within 32 lanes (bit-mask mode: and 31, xor 16), a
+// permute across the halves.
+template <int m>
+__device__ __forceinline__ float xor64_f(float v, int lane) {
+  if constexpr (m <= 8) return xor16_f<m>(v);
+  else if constexpr (m == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  else return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
+}
+template <int m>
+__device__ __forceinline__ void fwht64_stage(float (&v)[2], int lane) {
+  const float sgn = (lane & m) ? -1.0f : 1.0f;
+  const float p0 = xor64_f<m>(v[0], lane), p1 = xor64_f<m>(v[1], lane);
+  v[0] = fmaf(sgn, v[0], p0);  // low lane: v + p; high lane: p - v
+  v[1] = fmaf(sgn, v[1], p1);
+}
+template <int m>
+__device__ __forceinline__ float max64_step(float a, int lane) { return fmaxf(a, xor64_f<m>(a, lane)); }
+template <int m>
+__device__ __forceinline__ float sum64_step(float a, int lane) { return a + xor64_f<m>(a, lane); }
+
+// The same encoding as encode_block16 with one 128-block per wave, lane l
+// holding positions 2 l and 2 l + 1 (raw: their two fp16 values).  The
+// butterflies run over the strides in the same order (1 within the lane,
+// then 2 .. 64 across lanes), so the codes are the same bits.
+struct BlockCode64 {
+  float d[3][2];
+  float corr;
+  int e;
+};
+__device__ __forceinline__ BlockCode64 encode_block64(uint32_t raw, int rotate, int lane) {
+  float v[2] = {h2f((uint16_t)(raw & 0xFFFF)), h2f((uint16_t)(raw >> 16))};
+  if (rotate) {
+    const float a = v[0] + v[1], b = v[0] - v[1];
+    v[0] = a;
+    v[1] = b;
+    fwht64_stage<1>(v, lane);
+    fwht64_stage<2>(v, lane);
+    fwht64_stage<4>(v, lane);
+    fwht64_stage<8>(v, lane);
+    fwht64_stage<16>(v, lane);
+    fwht64_stage<32>(v, lane);
+  }
+  const float norm = rotate ? kHadamardNorm : 1.0f;
+  const float a0 = fabsf(v[0]), a1 = fabsf(v[1]);
+  float amax = fmaxf(a0 < INFINITY ? a0 : INFINITY, a1 < INFINITY ? a1 : INFINITY);  // NaN counts as inf
+  amax = max64_step<1>(amax, lane);
+  amax = max64_step<2>(amax, lane);
+  amax = max64_step<4>(amax, lane);
+  amax = max64_step<8>(amax, lane);
+  amax = max64_step<16>(amax, lane);
+  amax = max64_step<32>(amax, lane);
+  amax *= norm;  // max |x'| (inf for a non-finite block)
+  BlockCode64 r;
+  const bool nf = !(amax < INFINITY);
+  const bool ok = !nf && amax > 0.0f;
+  int e = 0;
+  if (ok) frexpf(amax, &e);  // amax = f 2^e, f in [0.5, 1): |x'| < 2^e
+  const float up = ok ? ldexpf(norm, 14 - e) : 0.0f;
+  float qs = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float q = rintf(v[j] * up);          // |q| <= 2^14 (0 for a non-finite block)
+    qs += q;
+    const float d0 = rintf(q * 0x1p-10f);       // [-16, 16]
+    const float r1 = fmaf(-1024.0f, d0, q);     // [-512, 512], exact
+    const float d1 = rintf(r1 * 0x1p-5f);       // [-16, 16]
+    r.d[0][j] = d0;
+    r.d[1][j] = d1;
+    r.d[2][j] = fmaf(-32.0f, d1, r1);           // [-16, 16], exact
+  }
+  qs = sum64_step<1>(qs, lane);  // integers below 2^21: exact
+  qs = sum64_step<2>(qs, lane);
+  qs = sum64_step<4>(qs, lane);
+  qs = sum64_step<8>(qs, lane);
+  qs = sum64_step<16>(qs, lane);
+  qs = sum64_step<32>(qs, lane);
+  r.e = ok ? e : 0;
+  r.corr = nf ? __builtin_nanf("") : qs * ldexpf(1.0f, r.e - 14);
+  return r;
 }
 
 // A-operand placement (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4): lane
@@ -518,12 +604,17 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// PTQ1_0, one token: k_mxv1_ptq1<WP>.  A workgroup takes WT = 8 / WP 64-row
-// tiles and WP periods of K (a period is 640 trits = 5 groups = 128 row
-// bytes = 8 chunks); wave w multiplies tile w % WT of period w / WT.  After
-// issuing its loads every wave writes its share of the byte table, and the
-// first waves encode the workgroup's activations straight into matrix-core
-// operands in LDS; one barrier, then the waves multiply.
+// PTQ1_0, one or two tokens: k_mxv_ptq1<NW, MT>.  A workgroup of NW waves
+// takes NW 64-row tiles (one per wave) and one period of K (640 trits = 5
+// groups = 128 row bytes = 8 chunks).  After issuing its loads every wave
+// writes its share of the byte table, and the lanes of the first waves
+// encode the MT tokens' activations straight into matrix-core operands in
+// LDS; one barrier, then the waves multiply.  The table words (B) serve
+// every token: a token adds four matrix operations per step and two LDS
+// reads, not table lookups.  (Three and more tokens take the two-step
+// kernels, whose cost hardly depends on the token count: here the encoding,
+// the matrix phase and the row stores of a workgroup all grow with it, and
+// from two tokens on a CU holds only one workgroup, for its registers.)
 //
 // Weights (B, fp4): lane (col, kg) loads chunk 4 h + kg of row 16 b + col
 // for each half h of the period (one 16-byte load); dword u of it feeds
@@ -533,22 +624,23 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 // 32 kg + 8 r + n of operation (h, u) is trit 80 (4 h + kg) + 20 u + 5 r + n
 // of the period.
 //
-// Activations (A, fp8): lane (row i, kgA) bytes 0-15 are K 16 kgA .. +15,
-// i.e. the ten trits of piece j = 32 h + 8 (kgA >> 1) + 2 u + (kgA & 1) of
-// the period (trits 10 j .. 10 j + 4 in bytes 0-4, 10 j + 5 .. 10 j + 9 in
-// bytes 8-12, the rest zero), bytes 16-31 those of piece j + 16.  A half of
-// a period spans three groups, 2 h .. 2 h + 2: row 4 s + d (s, d < 3)
-// carries digit d of the trits of group 2 h + s and zero elsewhere, with
-// that group's E8M0 scale 2^(e - 14 + 10 - 5 d).  The four operations u of
-// (h, b) chain their accumulators; output lane (col, s < 3) then holds in
-// its rows 4 s .. 4 s + 2 the digit sums of group 2 h + s for weight row
+// Activations (A, fp8), per token: lane (row i, kgA) bytes 0-15 are K
+// 16 kgA .. +15, i.e. the ten trits of piece j = 32 h + 8 (kgA >> 1) + 2 u +
+// (kgA & 1) of the period (trits 10 j .. 10 j + 4 in bytes 0-4, 10 j + 5 ..
+// 10 j + 9 in bytes 8-12, the rest zero), bytes 16-31 those of piece j + 16.
+// A half of a period spans three groups, 2 h .. 2 h + 2: row 4 s + d (s, d
+// < 3) carries digit d of the trits of group 2 h + s and zero elsewhere,
+// with that group's E8M0 scale 2^(e - 14 + 10 - 5 d).  The four operations
+// u of (h, b) chain their accumulators; output lane (col, s < 3) then holds
+// in its rows 4 s .. 4 s + 2 the digit sums of group 2 h + s for weight row
 // 16 b + col, which add up exactly (multiples of 2^(e-14) below 2^21 of
 // them); the group's fp16 scale multiplies the sum into an fp32 accumulator
 // (group 2 of a period, cut by the half boundary, once per half).
 //
 // LDS: the e2m1 table, 256 rows of 256 bytes (bytes 0-127 of row v hold 32
-// copies of entry v), and in the free upper halves ("hole rows" of 128 bytes
-// at row * 256 + 128), per period slot p, rows from 96 p:
+// copies of entry v), and operand areas of 81 "hole rows" of 128 bytes per
+// token in the free upper halves of the table rows: token 0 in rows 0-80,
+// token 1 in rows 96-176.  In a token's area:
 //   * A operands: unit U = 4 h + u in rows 10 U .. 10 U + 8: row
 //     q = 3 d + s holds digit plane d of slot s, the half hf of lane group
 //     kgA in the 16 bytes at (32 kgA + 16 hf + 16 q) mod 128 -- rotated by
@@ -556,43 +648,58 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 //     stays zero and serves the lanes of the unused rows (s = 3 or d = 3),
 //     rotated by 2 (rows 0-7 of A) or 1 (rows 8-15) for the same reason;
 //   * row 80: the groups' exponents e (5 ints) and NaN terms (5 floats).
-// Rows 192 .. 207 take the waves' partial rows for the final reduction.
+// The upper halves of table rows 192 .. 223 take the waves' partial rows
+// for the final stores.
 // ---------------------------------------------------------------------------
-constexpr int kPtqRowsPerPeriod = 96;
 constexpr int kPtqMetaRow = 80;
 constexpr int kPtqRedRow = 192;
+constexpr int kPtqMaxTokens = 2;
 
+// LDS byte address of row `row` of token m's operand area.
+__device__ __forceinline__ uint32_t tok_addr(int m, int row) {
+  return (uint32_t)(96 * m + row) * kLutRowBytes + 128u;
+}
 __device__ __forceinline__ uint32_t hole_addr(int row) { return (uint32_t)row * kLutRowBytes + 128u; }
 
-template <int NW, int WP>
-__global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
-  constexpr int WT = NW / WP;
-  static_assert(WP >= 1 && WP <= 2 && NW % WP == 0 && NW <= 8, "one or two periods per workgroup");
-  static_assert(kPeriodGroups * WP <= 4 * NW, "one pass encodes every group");
+template <int NW, int MT>
+__global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
+  static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
+  static_assert(MT >= 1 && MT <= kPtqMaxTokens, "one or two tokens");
+  static_assert(kPtqRedRow + 2 * MT * NW <= 256, "partial rows fit the table's upper halves");
+  constexpr int kEnc = kPeriodGroups * MT;             // blocks to encode
+  // encoding: one block per wave per pass ("wide") where that takes at most
+  // two passes, else one block per 16-lane quarter (fewer, longer passes)
+  constexpr bool kWide = (kEnc + NW - 1) / NW <= 2;
+  constexpr int kPasses = kWide ? (kEnc + NW - 1) / NW : (kEnc + 4 * NW - 1) / (4 * NW);
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutRowBytes / 4];
   char* const lds = reinterpret_cast<char*>(lut);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
-  const int64_t rr = blockIdx.x % a.RR, sl = blockIdx.x / a.RR;
-  const int64_t NP = ceil_div(a.G, kPeriodGroups);
-  const int ti = wave % WT, ps = wave / WT;
-  const int64_t lt = rr * WT + ti;
+  const int64_t rr = blockIdx.x % a.RR, sl = blockIdx.x / a.RR;  // row range, period
+  const int64_t lt = rr * NW + wave;
   const int64_t tile = a.tile0 + (lt < a.NTl ? lt : a.NTl - 1);
-  const int64_t per = sl * WP + ps;  // this wave's period
-  const bool has = per < NP;        // (wave-uniform)
-  const int64_t pc = has ? per : NP - 1;
 
-  // 1. x of the group this lane quarter encodes: group gq = 4 wave + q of
-  //    the workgroup's 5 WP (period slot gq / 5, group gq % 5); every wave
-  //    loads (the rest re-read group 0), so that the load counts are uniform
-  const int gq = 4 * wave + kg;
-  const int eps = gq / kPeriodGroups, eg = gq % kPeriodGroups;
-  const int64_t egg = (sl * WP + eps) * kPeriodGroups + eg;
-  const bool enc = gq < kPeriodGroups * WP;
-  const bool xval = enc && egg < a.G;
-  const uint4 xraw = *reinterpret_cast<const uint4*>(a.x + (xval ? egg : 0) * kGroup + 8 * col);
+  // 1. x of the blocks this thread encodes.  Wide form: pass p, block
+  //    gb = NW p + wave (token gb / 5, group gb % 5 of the period), two values
+  //    per lane; quarter form: block gb = 4 NW p + 4 wave + kg, eight values
+  //    per lane.  Every wave loads (the rest re-read token 0's group 0), so
+  //    that the load counts are uniform.
+  uint32_t xw[kWide ? kPasses : 1];
+  uint4 xq[kWide ? 1 : kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int gb = kWide ? NW * p + wave : 4 * NW * p + 4 * wave + kg;
+    const int m = gb / kPeriodGroups;
+    const int64_t egg = sl * kPeriodGroups + gb % kPeriodGroups;
+    const bool xval = gb < kEnc && egg < a.G;
+    const uint16_t* xs = a.x + (xval ? m * a.K + egg * kGroup : 0);
+    if constexpr (kWide)
+      xw[p] = *reinterpret_cast<const uint32_t*>(xs + 2 * lane);
+    else
+      xq[p] = *reinterpret_cast<const uint4*>(xs + 8 * col);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. scales: lane (col, q) of half h, block b takes row 16 b + col, group
@@ -602,7 +709,7 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
   uint32_t sraw[2][kBlocks];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int64_t g = pc * kPeriodGroups + 2 * h + (kg < 3 ? kg : 2);
+    const int64_t g = sl * kPeriodGroups + 2 * h + (kg < 3 ? kg : 2);
     const uint16_t* srow = sbase + (g < a.G ? g : a.G - 1) * kTile;
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) sraw[h][b] = ld_scale_pair(srow + 16 * b, col);
@@ -614,7 +721,7 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
   const uint4* wsrc[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    int64_t c = pc * kPeriodChunks + 4 * h + kg;
+    int64_t c = sl * kPeriodChunks + 4 * h + kg;
     c = c < a.C ? c : a.C - 1;
     wsrc[h] = reinterpret_cast<const uint4*>(a.packed) + (tile * a.C + c) * kTile + col;
   }
@@ -644,85 +751,116 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
             make_uint4(v, v, v, v);
     }
   }
-  // the zero row of every unit
-  if (threadIdx.x < 64 * WP)
-    *reinterpret_cast<uint4*>(lds + hole_addr((threadIdx.x / 64) * kPtqRowsPerPeriod + 10 * ((threadIdx.x / 8) % 8) +
-                                              9) + 16 * (threadIdx.x % 8)) = make_uint4(0, 0, 0, 0);
-  // 4. encode: the lanes of group (eps, eg) clear the rows of its slots (slot
+  // the zero row of every unit of every token
+  for (int t = threadIdx.x; t < 64 * MT; t += 64 * NW)
+    *reinterpret_cast<uint4*>(lds + tok_addr(t / 64, 10 * ((t / 8) % 8) + 9) + 16 * (t % 8)) =
+        make_uint4(0, 0, 0, 0);
+  // 4. encode: the lanes of block (m, eg) clear the rows of its slots (slot
   //    eg of half 0 for eg <= 2, slot eg - 2 of half 1 for eg >= 2: 4 units x
-  //    3 planes each), then write its digits: trit P = 128 eg + 8 col + i of
-  //    the period goes to half h = P / 320, piece j = (P - 320 h) / 10, byte
-  //    pr = (P - 320 h) % 10 of it (bytes 0-4 and 8-12)
-  if (enc) {
-    const int prow = eps * kPtqRowsPerPeriod;
+  //    3 planes each, 96 pieces of 16 bytes per half), then write its
+  //    digits: trit P = 128 eg + V l + j of the period (lane l of the
+  //    block's L lanes, V = 128 / L values each) goes to half h = P / 320,
+  //    piece jp = (P - 320 h) / 10, byte pr = (P - 320 h) % 10 of it (bytes
+  //    0-4 and 8-12)
+  constexpr int L = kWide ? 64 : 16, V = kGroup / L;
+  const int bl = kWide ? lane : col;  // lane within the block
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int gb = kWide ? NW * p + wave : 4 * NW * p + 4 * wave + kg;
+    if (gb >= kEnc) continue;
+    const int m = gb / kPeriodGroups, eg = gb % kPeriodGroups;
+    const bool xval = sl * kPeriodGroups + eg < a.G;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int s = eg - 2 * h;
       if (s < 0 || s > 2) continue;
 #pragma unroll
-      for (int k = 0; k < 6; ++k) {
-        const int i = col + 16 * k, row = i / 8, u = row / 3, d = row % 3;
-        *reinterpret_cast<uint4*>(lds + hole_addr(prow + 10 * (4 * h + u) + 3 * d + s) + 16 * (i % 8)) =
-            make_uint4(0, 0, 0, 0);
+      for (int k = 0; k < (96 + L - 1) / L; ++k) {
+        const int i = bl + L * k, row = i / 8, u = row / 3, d = row % 3;
+        if (i < 96)
+          *reinterpret_cast<uint4*>(lds + tok_addr(m, 10 * (4 * h + u) + 3 * d + s) + 16 * (i % 8)) =
+              make_uint4(0, 0, 0, 0);
       }
     }
-    const BlockCode16 c = encode_block16(xval ? xraw : make_uint4(0, 0, 0, 0), a.rotate, col);
-    uint32_t wd[3][2];
+    uint32_t wd[3][V / 4 > 0 ? V / 4 : 1];
+    int ce;
+    float ccorr;
+    if constexpr (kWide) {
+      const BlockCode64 c = encode_block64(xval ? xw[p] : 0u, a.rotate, lane);
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      wd[d][0] = e4m3_word(c.d[d][0], c.d[d][1], c.d[d][2], c.d[d][3]);
-      wd[d][1] = e4m3_word(c.d[d][4], c.d[d][5], c.d[d][6], c.d[d][7]);
+      for (int d = 0; d < 3; ++d) wd[d][0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c.d[d][0], c.d[d][1], 0, false);
+      ce = c.e;
+      ccorr = c.corr;
+    } else {
+      const BlockCode16 c = encode_block16(xval ? xq[p] : make_uint4(0, 0, 0, 0), a.rotate, col);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        wd[d][0] = e4m3_word(c.d[d][0], c.d[d][1], c.d[d][2], c.d[d][3]);
+        wd[d][1] = e4m3_word(c.d[d][4], c.d[d][5], c.d[d][6], c.d[d][7]);
+      }
+      ce = c.e;
+      ccorr = c.corr;
     }
     wave_lds_sync();  // (the clears land before the digits)
-    const int P0 = kGroup * eg + 8 * col;
+    const int P0 = kGroup * eg + V * bl;
     const int h = P0 / 320, s = eg - 2 * h, Q0 = P0 - 320 * h;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int Q = Q0 + i, jp = Q / 10, pr = Q % 10;
+    for (int j = 0; j < V; ++j) {
+      const int Q = Q0 + j, jp = Q / 10, pr = Q % 10;
       const int hf = jp >> 4, r = jp & 15, u = (r >> 1) & 3, kgA = 2 * (r >> 3) + (r & 1);
       const int at = 32 * kgA + 16 * hf + pr + (pr >= 5 ? 3 : 0);
 #pragma unroll
       for (int d = 0; d < 3; ++d) {
         const int q = 3 * d + s;
-        lds[hole_addr(prow + 10 * (4 * h + u) + q) + ((at + 16 * q) & 127)] = (char)(wd[d][i >> 2] >> (8 * (i & 3)));
+        lds[tok_addr(m, 10 * (4 * h + u) + q) + ((at + 16 * q) & 127)] = (char)(wd[d][j >> 2] >> (8 * (j & 3)));
       }
     }
-    if (col == 0) {
-      int* meta = reinterpret_cast<int*>(lds + hole_addr(prow + kPtqMetaRow));
-      meta[eg] = c.e;
-      reinterpret_cast<float*>(meta)[kPeriodGroups + eg] = c.corr != c.corr ? c.corr : 0.0f;
+    if (bl == 0) {
+      int* meta = reinterpret_cast<int*>(lds + tok_addr(m, kPtqMetaRow));
+      meta[eg] = ce;
+      reinterpret_cast<float*>(meta)[kPeriodGroups + eg] = ccorr != ccorr ? ccorr : 0.0f;
     }
   }
   __syncthreads();
 
-  // 5. per half: four chained operations per row block, then lane (col,
-  //    s < 3) scales its group's sum.  The operands of step k + 1 (its A
-  //    columns and table words) are fetched before the operations of step k
-  //    are issued, so that LDS latency overlaps the matrix cores.
-  float acc[kBlocks] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (has) {
+  // 5. per half: four chained operations per row block and token, then lane
+  //    (col, s < 3) scales its group's sums.  The operands of step k + 1 (the
+  //    tokens' A columns and the table words) are fetched before the
+  //    operations of step k are issued, so that LDS latency overlaps the
+  //    matrix cores.
+  float acc[MT][kBlocks];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) acc[m][b] = 0.0f;
+  {
     const int arow = lane & 15, as = arow >> 2, ad = arow & 3;
     const bool aon = as < 3 && ad < 3;
     const int aq = aon ? 3 * ad + as : 9, rot = aon ? aq : (arow < 8 ? 2 : 1);
-    const uint32_t arow0 = hole_addr(ps * kPtqRowsPerPeriod + aq);
     const uint32_t aoff0 = (32 * kg + 16 * rot) & 127, aoff1 = (32 * kg + 16 + 16 * rot) & 127;
-    const int* meta = reinterpret_cast<const int*>(lds + hole_addr(ps * kPtqRowsPerPeriod + kPtqMetaRow));
     const uint32_t loff = lut_lane_off(lane);
-    int sa[2];
-    float fl[2];
+    int sa[MT][2];
+    float fl[MT][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sa[h] = aon ? 123 + meta[2 * h + as] - 5 * ad : 127;
-      fl[h] = kg < 3 ? reinterpret_cast<const float*>(meta)[kPeriodGroups + 2 * h + kg] : 0.0f;
+    for (int m = 0; m < MT; ++m) {
+      const int* meta = reinterpret_cast<const int*>(lds + tok_addr(m, kPtqMetaRow));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sa[m][h] = aon ? 123 + meta[2 * h + as] - 5 * ad : 127;
+        fl[m][h] = kg < 3 ? reinterpret_cast<const float*>(meta)[kPeriodGroups + 2 * h + kg] : 0.0f;
+      }
     }
-    i32x8 A[2];
+    i32x8 A[2][MT];
     i32x4 B[2][kBlocks];
-    auto fetch = [&](int k, i32x8& Ak, i32x4 (&Bk)[kBlocks]) {
+    auto fetch = [&](int k, i32x8 (&Ak)[MT], i32x4 (&Bk)[kBlocks]) {
       const int h = k >> 2, u = k & 3;
-      const char* ar = lds + arow0 + 10 * k * kLutRowBytes;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(ar + aoff0);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(ar + aoff1);
-      Ak = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const char* ar = lds + tok_addr(m, aq) + 10 * k * kLutRowBytes;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ar + aoff0);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ar + aoff1);
+        Ak[m] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
         const uint32_t wd = u == 0 ? w[h][b].x : u == 1 ? w[h][b].y : u == 2 ? w[h][b].z : w[h][b].w;
@@ -732,7 +870,7 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
                       *reinterpret_cast<const int*>(lds + lut_addr<3>(wd, loff))};
       }
     };
-    f32x4 D[kBlocks];
+    f32x4 D[MT][kBlocks];
     fetch(0, A[0], B[0]);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -743,19 +881,24 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
         const i32x8 Bv = {B[cur][b][0], B[cur][b][1], B[cur][b][2], B[cur][b][3], 0, 0, 0, 0};
-        const f32x4 C = u == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : D[b];
-        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[cur], Bv, C, 0, 4, 0, sa[h], 0, 127);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const f32x4 C = u == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : D[m][b];
+          D[m][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[cur][m], Bv, C, 0, 4, 0, sa[m][h], 0, 127);
+        }
       }
       if (k == 3) {
         __builtin_amdgcn_sched_barrier(0);
         fetch(4, A[0], B[0]);  // (waits for the second half's weights)
       }
       if (u == 3) {
-        const bool gon = kg < 3 && pc * kPeriodGroups + 2 * h + kg < a.G;
+        const bool gon = kg < 3 && sl * kPeriodGroups + 2 * h + kg < a.G;
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
           const float s = gon ? scale_half(sraw[h][b], col) : 0.0f;
-          acc[b] = fmaf(s, (D[b][0] + D[b][1]) + (D[b][2] + fl[h]), acc[b]);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m][b] = fmaf(s, (D[m][b][0] + D[m][b][1]) + (D[m][b][2] + fl[m][h]), acc[m][b]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -763,37 +906,50 @@ __global__ void __launch_bounds__(64 * NW) k_mxv1_ptq1(MxvArgs a) {
   }
 
   // 6. the wave's rows: its four lane groups' partials (slots) added, then
-  //    the WP waves of a tile in a fixed order
+  //    stored through LDS so that every thread of the workgroup stores
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    pin(acc[b]);
-    acc[b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(acc[b])));
-    acc[b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(acc[b])));
-  }
-  if (kg == 0) {
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) {
-      const int r = 16 * b + col;
-      *reinterpret_cast<float*>(lds + hole_addr(kPtqRedRow + 2 * wave + (r >> 5)) + 4 * (r & 31)) = acc[b];
+      pin(acc[m][b]);
+      acc[m][b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(acc[m][b])));
+      acc[m][b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(acc[m][b])));
     }
+  if (kg == 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int b = 0; b < kBlocks; ++b) {
+        const int r = 16 * b + col;
+        *reinterpret_cast<float*>(lds + hole_addr(kPtqRedRow + 2 * (MT * wave + m) + (r >> 5)) + 4 * (r & 31)) =
+            acc[m][b];
+      }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < WT * kTile; r += 64 * NW) {
-    const int t = r / kTile, rl = r % kTile;
-    float v = 0.0f;
+  // thread t stores row t % 64 of tile t / 64 for every token (MT rows; with
+  // K split, all MT row-word arrivals are issued before any is checked)
+  const int t = threadIdx.x >> 6, rl = threadIdx.x & 63;
+  const int64_t ltt = rr * NW + t;
+  const int64_t lrow = ltt * kTile + rl;
+  const int64_t row = a.tile0 * kTile + lrow;
+  if (ltt >= a.NTl || row >= a.N) return;
+  float v[MT];
 #pragma unroll
-    for (int p = 0; p < WP; ++p)
-      v += *reinterpret_cast<const float*>(lds + hole_addr(kPtqRedRow + 2 * (p * WT + t) + (rl >> 5)) + 4 * (rl & 31));
-    const int64_t ltt = rr * WT + t;
-    if (ltt >= a.NTl) continue;
-    const int64_t lrow = ltt * kTile + rl;
-    const int64_t row = a.tile0 * kTile + lrow;
-    if (row >= a.N) continue;
-    if (a.P == 1)
-      a.y[row] = f2h(v);
-    else
-      add_partial(a.rw, 0, lrow, a.P, v, a.y + row);
+  for (int m = 0; m < MT; ++m)
+    v[m] = *reinterpret_cast<const float*>(lds + hole_addr(kPtqRedRow + 2 * (MT * t + m) + (rl >> 5)) +
+                                           4 * (rl & 31));
+  if (a.P == 1) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a.y[(int64_t)m * a.N + row] = f2h(v[m]);
+    return;
   }
+  uint64_t term[MT], old[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) term[m] = partial_term(a.rw, m, lrow, v[m]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) old[m] = arrive(a.rw, m, lrow, term[m]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) finish_row(a.rw, m, lrow, a.P, old[m], term[m], a.y + (int64_t)m * a.N + row);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,17 +980,25 @@ K1Split k1_split(int64_t units, int64_t umax, int64_t RR, int64_t min_wgs) {
   return K1Split{ceil_div(units, GW), GW};
 }
 
-// PTQ1_0 one-token kernel: periods per workgroup, and waves per workgroup:
-// the most (8, 4 or 2) that still give kPtqMinWgs workgroups.  Its matrix
-// phase is bound by the CU's LDS instruction rate (table lookups), so a
-// small projection runs faster on more CUs with fewer waves each.
-constexpr int kPtqWp = 1;
+// PTQ1_0 kernel: waves per workgroup, the most (8, 4 or 2) that still give
+// kPtqMinWgs workgroups.  Its matrix phase is bound by the CU's LDS
+// instruction rate (table lookups), so a small projection runs faster on
+// more CUs with fewer waves each.
 constexpr int64_t kPtqMinWgs = 160;
 int ptq1_waves(const bgg_weights_desc* d) {
-  const int64_t P = ceil_div(ceil_div(d->groups, kPeriodGroups), kPtqWp);
+  const int64_t P = ceil_div(d->groups, kPeriodGroups);
   for (int nw : {8, 4})
-    if (ceil_div(d->row_tiles, nw / kPtqWp) * P >= kPtqMinWgs) return nw;
+    if (ceil_div(d->row_tiles, nw) * P >= kPtqMinWgs) return nw;
   return 2;
+}
+
+template <int NW>
+void launch_ptq1(int M, dim3 grid, hipStream_t st, const MxvArgs& a) {
+  const dim3 block(64 * NW);
+  if (M == 1)
+    hipLaunchKernelGGL((k_mxv_ptq1<NW, 1>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_mxv_ptq1<NW, 2>), grid, block, 0, st, a);
 }
 
 }  // namespace
@@ -844,14 +1008,14 @@ namespace bgg {
 bool mxv_supported(const bgg_weights_desc* d, int64_t M) {
   // (K short enough for the row words' arrival count at the widest ranges)
   if (d->format == BGG_FMT_PTQ1_0)
-    return M == 1 && ceil_div(ceil_div(d->groups, kPeriodGroups), kPtqWp) <= kMaxSlices;
+    return M >= 1 && M <= kPtqMaxTokens && ceil_div(d->groups, kPeriodGroups) <= kMaxSlices;
   return d->format == BGG_FMT_PQ2_0 && M >= 1 && M <= 4 && d->groups <= (M == 1 ? 24 : kPqGsMax) * kMaxSlices;
 }
 
 uint64_t mxv_workspace_bytes() { return 2 * kRowWordBytes; }
 
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
-  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv1_ptq1<%d, %d>", ptq1_waves(d), kPtqWp);
+  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv_ptq1<%d, %d>", ptq1_waves(d), (int)M);
   if (M == 1) return snprintf(out, cap, "k_mxv1_pq2<5, %d>", mxv1_tpw(d));
   return snprintf(out, cap, "k_mxv_pq2<%d>", kPqGsMax);
 }
@@ -872,25 +1036,24 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
   a.y = (uint16_t*)y;
   const int64_t NT = d->row_tiles;
   if (d->format == BGG_FMT_PTQ1_0) {
-    // one token: workgroups of nw / kPtqWp tiles x kPtqWp periods
+    // workgroups of nw tiles x one period
     const int nw = ptq1_waves(d);
-    const int WT = nw / kPtqWp;
-    const int64_t RRall = ceil_div(NT, WT);
-    a.P = (int)ceil_div(ceil_div(a.G, kPeriodGroups), kPtqWp);
+    const int64_t RRall = ceil_div(NT, nw);
+    a.P = (int)ceil_div(a.G, kPeriodGroups);
     if (a.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
-    a.GS = kPtqWp;
-    const int64_t rr_per = a.P > 1 ? kRowWordRows / (WT * kTile) : RRall;
+    a.GS = 1;
+    const int64_t rr_per = a.P > 1 ? kRowWordRows / (nw * kTile) : RRall;
     for (int64_t r0 = 0; r0 < RRall; r0 += rr_per) {
       a.RR = std::min(rr_per, RRall - r0);
-      a.tile0 = r0 * WT;
-      a.NTl = std::min<int64_t>(a.RR * WT, NT - a.tile0);
-      const dim3 grid((unsigned)(a.RR * a.P)), block(64 * nw);
+      a.tile0 = r0 * nw;
+      a.NTl = std::min<int64_t>(a.RR * nw, NT - a.tile0);
+      const dim3 grid((unsigned)(a.RR * a.P));
       if (nw == 8)
-        hipLaunchKernelGGL((k_mxv1_ptq1<8, kPtqWp>), grid, block, 0, st, a);
+        launch_ptq1<8>((int)M, grid, st, a);
       else if (nw == 4)
-        hipLaunchKernelGGL((k_mxv1_ptq1<4, kPtqWp>), grid, block, 0, st, a);
+        launch_ptq1<4>((int)M, grid, st, a);
       else
-        hipLaunchKernelGGL((k_mxv1_ptq1<2, kPtqWp>), grid, block, 0, st, a);
+        launch_ptq1<2>((int)M, grid, st, a);
     }
     return hip_check("bgg_ternary_gemv");
   }
