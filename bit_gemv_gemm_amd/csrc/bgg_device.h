@@ -246,11 +246,26 @@ inline bgg_status hip_check(const char* what) {
   return BGG_OK;
 }
 
-// The matrix-core GEMV of bgg_mxv.hip (PQ2_0, 1..4 tokens, one launch that
-// also transforms x): whether it serves (format, M), the workspace bytes it
-// uses at the start of a GEMV workspace (row words that every launch leaves
-// zero), the name of the kernel it launches (snprintf's return), and the
-// launch.
+// Compute units of the current device (cached per device; 256 if the
+// runtime cannot tell).
+inline int64_t device_cus() {
+  static int64_t cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The matrix-core GEMV of bgg_mxv.hip (one launch that also transforms x;
+// PQ2_0 for 1..4 tokens, PTQ1_0 for 1..2): whether it serves (format, M),
+// the workspace bytes it uses at the start of a GEMV workspace (row words
+// that every launch leaves zero), the name of the kernel it launches
+// (snprintf's return), and the launch.
 bool mxv_supported(const bgg_weights_desc* d, int64_t M);
 uint64_t mxv_workspace_bytes();
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap);

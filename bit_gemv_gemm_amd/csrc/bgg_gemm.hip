@@ -391,20 +391,6 @@ __global__ void __launch_bounds__(256, 2)
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Compute units of the current device (cached per device).
-int64_t gemm_device_cus() {
-  static int64_t cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // K split in two when the output blocks fill the resident workgroup slots
 // (two per CU) much less evenly than twice as many would: the last, partly
 // empty round of workgroups (e.g. 640 blocks on 512 slots for 4096 tokens x
@@ -415,7 +401,7 @@ bool gemm_split(const bgg_weights_desc* d, int64_t M) {
   if (steps < 8) return false;
   const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
   const double wgs = (double)((d->N + kBN - 1) / kBN) * (double)((mc + kBM - 1) / kBM);
-  const double waves = wgs / (double)(2 * gemm_device_cus());
+  const double waves = wgs / (double)(2 * bgg::device_cus());
   const double eff1 = waves / std::ceil(waves), eff2 = 2 * waves / std::ceil(2 * waves);
   return eff2 > 1.15 * eff1;
 }

@@ -1329,20 +1329,6 @@ int64_t gemv_mma_min_tokens(int format) {
   return format == BGG_FMT_Q1_0 || format == BGG_FMT_Q2_0_G64 ? 1 : 2;
 }
 
-// Compute units of the current device (cached per device).
-int64_t device_cus() {
-  static int64_t cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // Wave counts the K split aims at (measured on the projection shapes).
 constexpr int64_t kTargetWaves = 2048;     // the split of K aims at this many waves
 constexpr int64_t kMinSingleWaves = 1024;  // one workgroup per tile from this many waves

@@ -663,13 +663,13 @@ __device__ __forceinline__ uint32_t hole_addr(int row) { return (uint32_t)row * 
 
 template <int NW, int MT>
 __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
-  static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
+  static_assert(NW >= 2 && NW <= 16, "2 to 16 waves");
   static_assert(MT >= 1 && MT <= kPtqMaxTokens, "one or two tokens");
   static_assert(kPtqRedRow + 2 * MT * NW <= 256, "partial rows fit the table's upper halves");
   constexpr int kEnc = kPeriodGroups * MT;             // blocks to encode
-  // encoding: one block per wave per pass ("wide") where that takes at most
-  // two passes, else one block per 16-lane quarter (fewer, longer passes)
-  constexpr bool kWide = (kEnc + NW - 1) / NW <= 2;
+  // encoding: one block per wave ("wide") where the waves take every block
+  // in one pass, else one block per 16-lane quarter (fewer, longer passes)
+  constexpr bool kWide = kEnc <= NW;
   constexpr int kPasses = kWide ? (kEnc + NW - 1) / NW : (kEnc + 4 * NW - 1) / (4 * NW);
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutRowBytes / 4];
   char* const lds = reinterpret_cast<char*>(lut);
@@ -729,27 +729,17 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
   for (int b = 0; b < kBlocks; ++b) w[0][b] = ld_stream(wsrc[0] + 16 * b);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. the table: with 512 threads, thread t writes copies 16 (t & 1) .. of
-  //    entry t / 2; with fewer, every copy of entries t, t + 64 NW, ...
-  //    (the 16-byte pieces of a row in an order rotated by the entry, so that
-  //    the lanes of one store, 256 bytes apart, spread over the banks)
-  if (NW == 8) {
-    const int e = threadIdx.x >> 1;
+  // 3. the table: job j = t, t + 64 NW, ... < 512 writes copies 16 (j & 1) ..
+  //    16 (j & 1) + 15 of entry j / 2 (the 16-byte pieces of a row in an
+  //    order rotated by the entry, so that the lanes of one store, 256 bytes
+  //    apart, spread over the banks)
+  for (int j = threadIdx.x; j < 512; j += 64 * NW) {
+    const int e = j >> 1;
     const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
 #pragma unroll
     for (int q = 0; q < kLutCopies32 / 8; ++q)
-      reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (threadIdx.x & 1) * (kLutCopies32 / 8) +
+      reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + (j & 1) * (kLutCopies32 / 8) +
                                     ((q + e) & (kLutCopies32 / 8 - 1))] = make_uint4(v, v, v, v);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 256 / (64 * NW); ++k) {
-      const int e = threadIdx.x + 64 * NW * k;
-      const uint32_t v = ptq1_lut_entry<kLutE2m1>((uint32_t)e);
-#pragma unroll
-      for (int q = 0; q < kLutCopies32 / 4; ++q)
-        reinterpret_cast<uint4*>(lut)[e * (kLutRowBytes / 16) + ((q + e) & (kLutCopies32 / 4 - 1))] =
-            make_uint4(v, v, v, v);
-    }
   }
   // the zero row of every unit of every token
   for (int t = threadIdx.x; t < 64 * MT; t += 64 * NW)
@@ -980,25 +970,39 @@ K1Split k1_split(int64_t units, int64_t umax, int64_t RR, int64_t min_wgs) {
   return K1Split{ceil_div(units, GW), GW};
 }
 
-// PTQ1_0 kernel: waves per workgroup, the most (8, 4 or 2) that still give
-// kPtqMinWgs workgroups.  Its matrix phase is bound by the CU's LDS
-// instruction rate (table lookups), so a small projection runs faster on
-// more CUs with fewer waves each.
-constexpr int64_t kPtqMinWgs = 160;
-int ptq1_waves(const bgg_weights_desc* d) {
-  const int64_t P = ceil_div(d->groups, kPeriodGroups);
-  for (int nw : {8, 4})
-    if (ceil_div(d->row_tiles, nw) * P >= kPtqMinWgs) return nw;
-  return 2;
+// PTQ1_0 kernel: waves (row tiles) per workgroup, the fewest from kPtqMinWaves
+// (5 for one token: the five blocks of a period are encoded in one pass; 3
+// for two) that leave at most one workgroup per CU.  A CU that holds two
+// workgroups takes them in about 1.3x the time of one and so sets the
+// launch's end (measured: gate/up 17408x5120 at one token 9.4 us with 8
+// waves = 272 workgroups on 256 CUs, 8.0 us with 9 waves = 248; at two
+// tokens 16.3 and 11.5 us; q 6144x5120 6.8 us with 4 waves, 6.6 with 5).
+constexpr int kPtqMaxWaves[3] = {0, 16, 12};  // (two tokens: registers for 3 waves per SIMD)
+constexpr int kPtqMinWaves[3] = {0, 5, 3};
+int ptq1_waves(const bgg_weights_desc* d, int64_t M) {
+  const int64_t P = ceil_div(d->groups, kPeriodGroups), cus = device_cus();
+  for (int nw = kPtqMinWaves[M]; nw < kPtqMaxWaves[M]; ++nw)
+    if (ceil_div(d->row_tiles, nw) * P <= cus) return nw;
+  return kPtqMaxWaves[M];
 }
 
 template <int NW>
 void launch_ptq1(int M, dim3 grid, hipStream_t st, const MxvArgs& a) {
   const dim3 block(64 * NW);
-  if (M == 1)
-    hipLaunchKernelGGL((k_mxv_ptq1<NW, 1>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((k_mxv_ptq1<NW, 2>), grid, block, 0, st, a);
+  if (M == 1) {
+    if constexpr (NW >= kPtqMinWaves[1]) hipLaunchKernelGGL((k_mxv_ptq1<NW, 1>), grid, block, 0, st, a);
+  } else {
+    if constexpr (NW <= kPtqMaxWaves[2]) hipLaunchKernelGGL((k_mxv_ptq1<NW, 2>), grid, block, 0, st, a);
+  }
+}
+template <int NW>
+void launch_ptq1_nw(int nw, int M, dim3 grid, hipStream_t st, const MxvArgs& a) {
+  if constexpr (NW <= 16) {
+    if (nw == NW)
+      launch_ptq1<NW>(M, grid, st, a);
+    else
+      launch_ptq1_nw<NW + 1>(nw, M, grid, st, a);
+  }
 }
 
 }  // namespace
@@ -1015,7 +1019,7 @@ bool mxv_supported(const bgg_weights_desc* d, int64_t M) {
 uint64_t mxv_workspace_bytes() { return 2 * kRowWordBytes; }
 
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
-  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv_ptq1<%d, %d>", ptq1_waves(d), (int)M);
+  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv_ptq1<%d, %d>", ptq1_waves(d, M), (int)M);
   if (M == 1) return snprintf(out, cap, "k_mxv1_pq2<5, %d>", mxv1_tpw(d));
   return snprintf(out, cap, "k_mxv_pq2<%d>", kPqGsMax);
 }
@@ -1037,7 +1041,9 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
   const int64_t NT = d->row_tiles;
   if (d->format == BGG_FMT_PTQ1_0) {
     // workgroups of nw tiles x one period
-    const int nw = ptq1_waves(d);
+    const int nw = ptq1_waves(d, M);
+    if (nw < kPtqMinWaves[M] || nw > kPtqMaxWaves[M])  // (the rule stays within the instantiated counts)
+      return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: no kernel for %d waves", nw);
     const int64_t RRall = ceil_div(NT, nw);
     a.P = (int)ceil_div(a.G, kPeriodGroups);
     if (a.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
@@ -1048,12 +1054,7 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
       a.tile0 = r0 * nw;
       a.NTl = std::min<int64_t>(a.RR * nw, NT - a.tile0);
       const dim3 grid((unsigned)(a.RR * a.P));
-      if (nw == 8)
-        launch_ptq1<8>((int)M, grid, st, a);
-      else if (nw == 4)
-        launch_ptq1<4>((int)M, grid, st, a);
-      else
-        launch_ptq1<2>((int)M, grid, st, a);
+      launch_ptq1_nw<kPtqMinWaves[2]>(nw, (int)M, grid, st, a);
     }
     return hip_check("bgg_ternary_gemv");
   }

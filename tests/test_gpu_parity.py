@@ -365,6 +365,32 @@ def test_gemv_matrix_core_every_token_count(env, fmt):
         assert np.all(relerr(y, ref[:M]) <= TOL), f"M={M}"
 
 
+@pytest.mark.parametrize("N,K,M", [(8064 - 37, 6144, 1), (12864, 6144, 1), (16064 - 5, 6144, 1),
+                                   (24064 + 64, 6144, 1), (4864 - 1, 6144, 2), (9664 + 3, 6144, 2),
+                                   (17664, 6144, 2), (300, 1408, 2)])
+def test_gemv_ptq1_waves_per_workgroup(env, N, K, M):
+    """The PTQ1_0 one- and two-token kernel takes as many row tiles per
+    workgroup (one per wave) as keep one workgroup per CU, from 5 (one
+    token) or 3 (two) up to 16 or 12: these shapes select counts across that
+    range (ragged last row ranges included).  Rows of the first and the last
+    row range and a random sample match the oracle."""
+    bgg, torch = env
+    T, S = gen_matrix(141, 2, N, K, fmt="PTQ1_0")
+    d = Dev(bgg, torch, "PTQ1_0", T, S)
+    kn = bgg.bgg_gemv_kernel_name(d.desc, M)
+    say(f"gemv PTQ1_0 N={N} K={K} M={M}: {kn}")
+    nw = int(kn.split("<")[1].split(",")[0])
+    assert kn.startswith("k_mxv_ptq1<") and (5 if M == 1 else 3) <= nw <= (16 if M == 1 else 12), kn
+    x = synth.activations_f16(141, 3, M, K)
+    y = d.gemv(x)
+    assert not np.isnan(y).any()
+    span = 64 * nw
+    rows = np.unique(np.concatenate([np.arange(min(span, N)), np.arange(max(0, N - span - 64), N),
+                                     np.random.default_rng(9).choice(N, min(N, 256), replace=False)]))
+    ref = oracle_y("PTQ1_0", T[rows], S[rows], x)
+    assert np.all(relerr(y[:, rows], ref) <= TOL)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_workspace_shared_across_shapes(env, fmt):
     """One zero-filled workspace serves calls of different K, N and M in any
