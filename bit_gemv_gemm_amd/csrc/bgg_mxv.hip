@@ -440,6 +440,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
   __shared__ uint8_t sSc[kWaves][GPW][4];   // E8M0 of digits 0-2 (byte 3 unused)
   __shared__ float sCorr[kWaves][GPW];
   __shared__ float red[kWaves][kRows];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[kWaves][TPW][GPW * kTile];  // the wave's scales
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -468,17 +469,15 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
     xraw[p] = *reinterpret_cast<const uint4*>(a.x + (g0 + (gi < ngl ? gi : 0)) * kGroup + 8 * l16);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // 2. scales (lane l: row l of each tile), then the first half of the codes
-  uint32_t sraw[TPW][GPW];
+  // 2. scales: per tile the wave's ngl groups of 64 fp16 scales lie one
+  //    after the other (ngl x 128 bytes), one 16-byte load per lane (lanes
+  //    past the end re-read the first piece); then the first half of the codes
+  static_assert(TPW == 1 || TPW == 2, "one or two tiles");
+  const uint4* sbase = reinterpret_cast<const uint4*>(a.packed + a.scale_offset) + (lane < 8 * ngl ? lane : 0);
+  const uint4 sraw0 = sbase[(tiles[0] * a.G + g0) * 8];
+  const uint4 sraw1 = TPW == 2 ? sbase[(tiles[TPW - 1] * a.G + g0) * 8] : sraw0;
   u32x2 w[TPW][kBlocks][GPW];
   constexpr int kHalf = (GPW + 1) / 2;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const uint16_t* ssrc =
-        reinterpret_cast<const uint16_t*>(a.packed + a.scale_offset) + (tiles[t] * a.G + g0) * kTile + lane;
-#pragma unroll
-    for (int g = 0; g < GPW; ++g) sraw[t][g] = ssrc[(int64_t)(g < ngl ? g : ngl - 1) * kTile];
-  }
 #pragma unroll
   for (int g = 0; g < kHalf; ++g)
 #pragma unroll
@@ -491,6 +490,17 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
     }
   __builtin_amdgcn_sched_barrier(0);
 
+  // the scales into LDS, where each output lane reads its rows' scales:
+  // with one tile after the encoding (which need not wait for them), with
+  // two before it (measured faster; the two tiles' weight registers leave
+  // none to keep the scales through the encoding)
+  auto scales_to_lds = [&]() {
+    if (lane < GPW * 8) {
+      reinterpret_cast<uint4*>(sS[wave][0])[lane] = sraw0;
+      if (TPW == 2) reinterpret_cast<uint4*>(sS[wave][TPW - 1])[lane] = sraw1;
+    }
+  };
+  if (TPW == 2) scales_to_lds();
   // 3. encode the wave's groups: digit rows 0-2 of A
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -515,6 +525,8 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if (TPW == 1) scales_to_lds();
+  wave_lds_sync();
   // 4. MFMAs: A lanes of rows 0-2 read their digits, the rest are zero.
   //    The second half of the codes is issued in the first iterations, one
   //    group per iteration ahead of that iteration's matrix operations: a
@@ -565,7 +577,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
         }
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
-          const float s = h2f((uint16_t)__builtin_amdgcn_ds_bpermute((16 * b + col) << 2, (int)sraw[t][g]));
+          const float s = h2f(sS[wave][t][g * kTile + 16 * b + col]);
           acc[t][b] = fmaf(s, (D[b][0] + D[b][1]) + (D[b][2] - corr), acc[t][b]);
         }
       }
