@@ -476,17 +476,21 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
   const uint4* sbase = reinterpret_cast<const uint4*>(a.packed + a.scale_offset) + (lane < 8 * ngl ? lane : 0);
   const uint4 sraw0 = sbase[(tiles[0] * a.G + g0) * 8];
   const uint4 sraw1 = TPW == 2 ? sbase[(tiles[TPW - 1] * a.G + g0) * 8] : sraw0;
-  u32x2 w[TPW][kBlocks][GPW];
+  // codes: lane (col, kg) loads the whole 16-byte chunk 2 g + (kg >> 1) of
+  // row 16 (2 p + (kg & 1)) + col for block pair p (blocks 2 p, 2 p + 1),
+  // and lanes kg = 0, 1 (2, 3) later swap halves, so that each holds its 8
+  // bytes of both blocks (one load instruction per two blocks)
+  uint4 w[TPW][kBlocks / 2][GPW];
   constexpr int kHalf = (GPW + 1) / 2;
 #pragma unroll
   for (int g = 0; g < kHalf; ++g)
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const u32x2* wsrc = reinterpret_cast<const u32x2*>(a.packed) +
-                          ((tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
+      const uint4* wsrc = reinterpret_cast<const uint4*>(a.packed) +
+                          (tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + 16 * (kg & 1) + col;
 #pragma unroll
-      for (int b = 0; b < kBlocks; ++b)
-        w[t][b][g] = __builtin_nontemporal_load(wsrc + (int64_t)(g < ngl ? g : ngl - 1) * (4 * kTile) + b * 32);
+      for (int p = 0; p < kBlocks / 2; ++p)
+        w[t][p][g] = ld_stream(wsrc + (int64_t)(g < ngl ? g : ngl - 1) * (2 * kTile) + p * 32);
     }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -545,11 +549,11 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
       const int gh = kHalf + g;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const u32x2* wsrc = reinterpret_cast<const u32x2*>(a.packed) +
-                            ((tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
+        const uint4* wsrc = reinterpret_cast<const uint4*>(a.packed) +
+                            (tiles[t] * a.C + 2 * g0 + (kg >> 1)) * kTile + 16 * (kg & 1) + col;
 #pragma unroll
-        for (int b = 0; b < kBlocks; ++b)
-          w[t][b][gh] = __builtin_nontemporal_load(wsrc + (int64_t)(gh < ngl ? gh : ngl - 1) * (4 * kTile) + b * 32);
+        for (int p = 0; p < kBlocks / 2; ++p)
+          w[t][p][gh] = ld_stream(wsrc + (int64_t)(gh < ngl ? gh : ngl - 1) * (2 * kTile) + p * 32);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -567,10 +571,25 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
       const float corr = sCorr[wave][g];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
+        // block 2 p: bytes 0-7 of the chunk on lanes kg = 0, 2, bytes 8-15 on
+        // kg = 1, 3; block 2 p + 1 likewise: the odd lane rows' first halves
+        // trade places with the even rows' second halves
+        // (v_permlane16_swap: odd 16-lane rows of the first operand with even
+        // rows of the second)
+        uint32_t cw[kBlocks][2];
+#pragma unroll
+        for (int p = 0; p < kBlocks / 2; ++p) {
+          const auto s0 = __builtin_amdgcn_permlane16_swap(w[t][p][g].x, w[t][p][g].z, false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(w[t][p][g].y, w[t][p][g].w, false, false);
+          cw[2 * p][0] = s0[0];
+          cw[2 * p][1] = s1[0];
+          cw[2 * p + 1][0] = s0[1];
+          cw[2 * p + 1][1] = s1[1];
+        }
         f32x4 D[kBlocks];
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
-          const uint32_t lo = w[t][b][g].x, hi = w[t][b][g].y;
+          const uint32_t lo = cw[b][0], hi = cw[b][1];
           const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
                            (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
           D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 128);
