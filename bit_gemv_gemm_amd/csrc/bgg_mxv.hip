@@ -296,6 +296,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[GSMAX][64 * 32];
   __shared__ uint8_t sSc[GSMAX][64];
   __shared__ float sCorr[GSMAX][4];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[kWaves][GSMAX * kTile];  // each wave's scales
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -318,26 +319,24 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
       a.x + (int64_t)(xreal ? quarter : 0) * a.K + (g0 + (enc ? wave : 0)) * kGroup + 8 * l16);
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. scales, then the first half of the code loads: codes of rows 16 b +
-  //    col, K 32 kg .. +31 of group g -- chunk 2 g + kg / 2, half kg % 2
-  //    (u32x2 units); a group past the slice re-reads its last
+  // 2. scales: the slice's ng blocks of 64 fp16 scales of the tile lie one
+  //    after the other (ng x 128 bytes), one 16-byte load per lane (lanes
+  //    past the end re-read the first piece); then the first half of the
+  //    code loads: lane (col, kg) loads the whole 16-byte chunk 2 g + kg / 2
+  //    of row 16 (2 p + kg % 2) + col for block pair p (blocks 2 p, 2 p + 1),
+  //    and lanes kg = 0, 1 (2, 3) later swap halves, so that each holds its
+  //    8 bytes of both blocks; a group past the slice re-reads its last
   constexpr int kHalf = (GSMAX + 1) / 2;
-  u32x2 w[GSMAX][kBlocks];
-  uint32_t sraw[GSMAX];
-  const u32x2* wsrc = reinterpret_cast<const u32x2*>(a.packed) +
-                      ((tile * a.C + 2 * g0 + (kg >> 1)) * kTile + col) * 2 + (kg & 1);
-  {
-    const uint16_t* ssrc =
-        reinterpret_cast<const uint16_t*>(a.packed + a.scale_offset) + (tile * a.G + g0) * kTile + lane;
+  uint4 w[GSMAX][kBlocks / 2];
+  const uint4 sraw =
+      reinterpret_cast<const uint4*>(a.packed + a.scale_offset)[(tile * a.G + g0) * 8 + (lane < 8 * ng ? lane : 0)];
+  const uint4* wsrc = reinterpret_cast<const uint4*>(a.packed) +
+                      (tile * a.C + 2 * g0 + (kg >> 1)) * kTile + 16 * (kg & 1) + col;
 #pragma unroll
-    for (int g = 0; g < GSMAX; ++g) sraw[g] = ssrc[(int64_t)(g < ng ? g : ng - 1) * kTile];
+  for (int g = 0; g < kHalf; ++g) {
+    const int gl = g < ng ? g : ng - 1;
 #pragma unroll
-    for (int g = 0; g < kHalf; ++g) {
-      const int gl = g < ng ? g : ng - 1;
-#pragma unroll
-      for (int b = 0; b < kBlocks; ++b)
-        w[g][b] = __builtin_nontemporal_load(wsrc + (int64_t)gl * (4 * kTile) + b * 32);
-    }
+    for (int p = 0; p < kBlocks / 2; ++p) w[g][p] = ld_stream(wsrc + (int64_t)gl * (2 * kTile) + p * 32);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -375,18 +374,12 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
   for (int g = kHalf; g < GSMAX; ++g) {
     const int gl = g < ng ? g : ng - 1;
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
-      w[g][b] = __builtin_nontemporal_load(wsrc + (int64_t)gl * (4 * kTile) + b * 32);
+    for (int p = 0; p < kBlocks / 2; ++p) w[g][p] = ld_stream(wsrc + (int64_t)gl * (2 * kTile) + p * 32);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 5. the scales of rows 16 b + col (lane l loaded row l)
-  float sc[GSMAX][kBlocks];
-#pragma unroll
-  for (int g = 0; g < GSMAX; ++g)
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
-      sc[g][b] = h2f((uint16_t)__builtin_amdgcn_ds_bpermute((16 * b + col) << 2, (int)sraw[g]));
+  // 5. the scales into LDS, where lane (col, kg) reads those of rows 16 b + col
+  if (lane < GSMAX * 8) reinterpret_cast<uint4*>(sS[wave])[lane] = sraw;
   __syncthreads();
 
   // 6. one MFMA per group and row block, the four of a group issued together
@@ -401,17 +394,30 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       const int sa = sSc[g][lane];
       const float corr = sCorr[g][kg];
+      // block 2 p: bytes 0-7 of the chunk on lanes kg = 0, 2, bytes 8-15 on
+      // kg = 1, 3; block 2 p + 1 likewise (v_permlane16_swap: odd 16-lane
+      // rows of the first operand with even rows of the second)
+      uint32_t cw[kBlocks][2];
+#pragma unroll
+      for (int p = 0; p < kBlocks / 2; ++p) {
+        const auto s0 = __builtin_amdgcn_permlane16_swap(w[g][p].x, w[g][p].z, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(w[g][p].y, w[g][p].w, false, false);
+        cw[2 * p][0] = s0[0];
+        cw[2 * p][1] = s1[0];
+        cw[2 * p + 1][0] = s0[1];
+        cw[2 * p + 1][1] = s1[1];
+      }
       f32x4 D[kBlocks];
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
-        const uint32_t lo = w[g][b].x, hi = w[g][b].y;
+        const uint32_t lo = cw[b][0], hi = cw[b][1];
         const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
                          (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
         D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 128);
       }
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b)
-        acc[b] = fmaf(sc[g][b], (D[b][0] + D[b][1]) + (D[b][2] - corr), acc[b]);
+        acc[b] = fmaf(h2f(sS[wave][g * kTile + 16 * b + col]), (D[b][0] + D[b][1]) + (D[b][2] - corr), acc[b]);
     }
   }
 
