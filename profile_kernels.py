@@ -13,6 +13,12 @@ takes seconds.
                               --calib MiB (known bytes for FETCH_SIZE /
                               WRITE_SIZE)
 
+With --decode-layer it runs instead one layer of the 64-layer decode step
+(q, k, v, o, gate, up, down at one token, both packings, each call on its
+own weight copy) --reps times, plus the calibration: every decode kernel
+then gets the same mix of shapes per dispatch as in the step, so its
+per-dispatch counters compare with the step's bytes per launch.
+
 Each workload runs --reps times over --copies weight copies (so the weights
 come from HBM).  Inputs are the benchmark's seeded synthetic ones.
 """
@@ -32,6 +38,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=24)
     ap.add_argument("--calib", type=int, default=256, metavar="MIB")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--decode-layer", action="store_true")
     args = ap.parse_args()
 
     import torch
@@ -42,6 +49,10 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.decode_layer:
+        decode_layer(args, torch, bgg, synth, dev, stream)
+        calibrate(args, torch, probe, dev)
+        return 0
     pw = synth.WORKLOADS["projection"]
     for mat in pw["matrices"]:
         T, S = synth.workload_matrix(mat, pw["seed"])
@@ -80,6 +91,37 @@ def main() -> int:
                 torch.cuda.synchronize()
                 del packed, wsg
             del T, S, x, xr, y
+    calibrate(args, torch, probe, dev)
+    return 0
+
+
+def decode_layer(args, torch, bgg, synth, dev, stream) -> None:
+    """One layer of the decode step per packing, --reps times (each call
+    of a repetition on its own weight copy, as the step's layers are)."""
+    w = synth.WORKLOADS["decode_step"]
+    layer = synth.decode_stack(1)
+    for fmt in ("PQ2_0", "PTQ1_0"):
+        calls = []
+        for mat in layer:
+            T, S = synth.workload_matrix(mat, w["seed"])
+            d = bgg.bgg_describe(fmt, mat.n, mat.k)
+            host = bgg.bgg_pack_weights(d, T, S)
+            copies = [bgg.upload(host, dev) for _ in range(args.reps)]
+            x = torch.from_numpy(synth.workload_x(w["seed"], 1, mat.k)).to(dev)
+            y = torch.empty((1, mat.n), dtype=torch.float16, device=dev)
+            calls.append((mat.name, d, copies, x, y))
+            del T, S, host
+        ws = bgg.workspace(max(bgg.bgg_gemv_workspace_size(d, 1) for _, d, _, _, _ in calls), dev)
+        for name, d, _, _, _ in calls:
+            print(f"decode layer {fmt} {name} {int(d.N)}x{int(d.K)}: {bgg.bgg_gemv_kernel_name(d, 1)}", flush=True)
+        for r in range(args.reps):
+            for _, d, copies, x, y in calls:
+                bgg.bgg_ternary_gemv(d, copies[r], x, y, 1, bgg.BGG_ROTATE_INPUT, ws, stream)
+        torch.cuda.synchronize()
+        del calls, ws
+
+
+def calibrate(args, torch, probe, dev) -> None:
     cb = torch.empty(args.calib << 20, dtype=torch.uint8, device=dev)
     sink = probe.sink(dev)
     print(f"calibration: probe read and write of {args.calib} MiB", flush=True)
@@ -88,7 +130,6 @@ def main() -> int:
         probe.write(cb)
     torch.cuda.synchronize()
     print("done", flush=True)
-    return 0
 
 
 if __name__ == "__main__":
