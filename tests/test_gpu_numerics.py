@@ -37,8 +37,9 @@ FMTS = ("PQ2_0", "PTQ1_0")
 # (N, K): K cut over workgroups for every token count (few rows), K cut for
 # one token (down projection), K whole for one token (gate/up projection)
 SHAPES = [(300, 5120), (5120, 17408), (17408, 5120)]
-# token counts: one launch / two steps (M = 1), 2..4, 5+ (6 and 13)
-MODES = [("one", 1), ("two", 1), ("one", 3), ("one", 6), ("one", 13)]
+# token counts: one launch / two steps (M = 1), 2 (one launch in both
+# packings), 3 (one launch for PQ2_0, two steps for PTQ1_0), 5+ (6 and 13)
+MODES = [("one", 1), ("two", 1), ("one", 2), ("one", 3), ("one", 6), ("one", 13)]
 F16_MAX = 65504.0
 
 
