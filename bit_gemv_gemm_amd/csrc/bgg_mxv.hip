@@ -685,24 +685,19 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 //     stays zero and serves the lanes of the unused rows (s = 3 or d = 3),
 //     rotated by 2 (rows 0-7 of A) or 1 (rows 8-15) for the same reason;
 //   * row 80: the groups' exponents e (5 ints) and NaN terms (5 floats).
-// The upper halves of table rows 192 .. 223 take the waves' partial rows
-// for the final stores.
 // ---------------------------------------------------------------------------
 constexpr int kPtqMetaRow = 80;
-constexpr int kPtqRedRow = 192;
 constexpr int kPtqMaxTokens = 2;
 
 // LDS byte address of row `row` of token m's operand area.
 __device__ __forceinline__ uint32_t tok_addr(int m, int row) {
   return (uint32_t)(96 * m + row) * kLutRowBytes + 128u;
 }
-__device__ __forceinline__ uint32_t hole_addr(int row) { return (uint32_t)row * kLutRowBytes + 128u; }
 
 template <int NW, int MT>
 __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
   static_assert(NW >= 2 && NW <= 16, "2 to 16 waves");
   static_assert(MT >= 1 && MT <= kPtqMaxTokens, "one or two tokens");
-  static_assert(kPtqRedRow + 2 * MT * NW <= 256, "partial rows fit the table's upper halves");
   constexpr int kEnc = kPeriodGroups * MT;             // blocks to encode
   // encoding: one block per wave ("wide") where the waves take every block
   // in one pass, else one block per 16-lane quarter (fewer, longer passes)
@@ -932,8 +927,10 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
     }
   }
 
-  // 6. the wave's rows: its four lane groups' partials (slots) added, then
-  //    stored through LDS so that every thread of the workgroup stores
+  // 6. the wave's rows: its four lane groups' partials (slots) added, so
+  //    that every lane holds the sums of its column's four row blocks; lane
+  //    (col, kg) stores row 16 kg + col (all of a lane's row-word arrivals
+  //    issued before any is checked)
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -942,29 +939,12 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
       acc[m][b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(acc[m][b])));
       acc[m][b] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(acc[m][b])));
     }
-  if (kg == 0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int b = 0; b < kBlocks; ++b) {
-        const int r = 16 * b + col;
-        *reinterpret_cast<float*>(lds + hole_addr(kPtqRedRow + 2 * (MT * wave + m) + (r >> 5)) + 4 * (r & 31)) =
-            acc[m][b];
-      }
-  }
-  __syncthreads();
-  // thread t stores row t % 64 of tile t / 64 for every token (MT rows; with
-  // K split, all MT row-word arrivals are issued before any is checked)
-  const int t = threadIdx.x >> 6, rl = threadIdx.x & 63;
-  const int64_t ltt = rr * NW + t;
-  const int64_t lrow = ltt * kTile + rl;
+  const int64_t lrow = lt * kTile + 16 * kg + col;
   const int64_t row = a.tile0 * kTile + lrow;
-  if (ltt >= a.NTl || row >= a.N) return;
+  if (lt >= a.NTl || row >= a.N) return;
   float v[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-    v[m] = *reinterpret_cast<const float*>(lds + hole_addr(kPtqRedRow + 2 * (MT * t + m) + (rl >> 5)) +
-                                           4 * (rl & 31));
+  for (int m = 0; m < MT; ++m) v[m] = kg == 0 ? acc[m][0] : kg == 1 ? acc[m][1] : kg == 2 ? acc[m][2] : acc[m][3];
   if (a.P == 1) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) a.y[(int64_t)m * a.N + row] = f2h(v[m]);
