@@ -212,22 +212,37 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t word, uint32_t lane_off) {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Eight consecutive PQ2_0 codes (16 bits of a code word: code i in bits
-// 2i..2i+1) and a scale -> the fp16 MFMA operand (s*t_0, ..., s*t_7).
-// A nibble (c1 << 2 | c0) times 0x4001 puts c0 in bits 0-1 and c1 in bits
-// 16-17; 0x6400 | c is the fp16 1024 + c, and subtracting 1025 gives t = c-1
-// exactly; t * s is exact.
-__device__ __forceinline__ f16x8 decode8_pq2(uint32_t codes16, __half2 s2) {
-  const __half2 bias = __halves2half2(__ushort_as_half(0xE401), __ushort_as_half(0xE401));  // -1025
+// The three values an fp16 scale s gives a PQ2_0 code c = t + 1, as a
+// byte-select table for v_perm_b32: `lo` holds the low byte of the value of
+// code c in byte c, `hi` its high byte in byte c (read as selector c + 4).
+// Code 0 is -s (s with the sign bit flipped), code 1 is 0, code 2 is +s;
+// code 3, which no valid buffer holds, reads 0 like code 1.
+struct Pq2Table {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Pq2Table pq2_table(uint32_t sbits) {
+  const uint32_t l = sbits & 0xFFu, h = (sbits >> 8) & 0xFFu;
+  return {l * 0x00010001u, (h ^ 0x80u) | (h << 16)};
+}
+
+// Eight consecutive PQ2_0 codes (bits `shift` .. `shift` + 15 of a code
+// word: code i in bits 2i..2i+1 of that field) -> the fp16 MFMA operand
+// (s*t_0, ..., s*t_7), bit for bit the value s*t (+-s or 0) -- no
+// arithmetic, only byte moves.  t | t << 14 puts codes 0, 4 in bytes 0, 1
+// and codes 1, 5 in bytes 2, 3 (two-bit fields at the byte starts); shifted
+// down by four the same holds for codes 2, 6, 3, 7.  A first byte permute
+// turns the two codes of one output word into the selector (c_a, c_a + 4,
+// c_b, c_b + 4), a second one reads the table with it.
+__device__ __forceinline__ f16x8 decode8_pq2(uint32_t word, uint32_t shift, Pq2Table tb) {
+  const uint32_t t = __builtin_amdgcn_ubfe(word, shift, 16);
+  const uint32_t z = t | (t << 14);
+  const uint32_t ab = z & 0x03030303u, cd = (z >> 4) & 0x03030303u;
+  const uint32_t ab4 = ab | 0x04040404u, cd4 = cd | 0x04040404u;
   uint32_t out[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t nib = (codes16 >> (4 * j)) & 0xFu;
-    uint32_t p = ((nib * 0x4001u) & 0x00030003u) | 0x64006400u;
-    __half2 h = *reinterpret_cast<__half2*>(&p);
-    h = __hmul2(__hadd2(h, bias), s2);
-    out[j] = *reinterpret_cast<uint32_t*>(&h);
-  }
+  out[0] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(ab4, ab, 0x06020400u));
+  out[1] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(cd4, cd, 0x06020400u));
+  out[2] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(ab4, ab, 0x07030501u));
+  out[3] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(cd4, cd, 0x07030501u));
   f16x8 r;
   __builtin_memcpy(&r, out, sizeof(r));
   return r;

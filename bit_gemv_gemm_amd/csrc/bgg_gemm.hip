@@ -5,23 +5,25 @@
 // is the packing that wins prompt processing; method paragraph: trits with
 // one FP16 scale per 128 weights.  This is the one dense contraction of the
 // path, so it runs on the matrix cores: trit tiles are decoded to fp16 s*t
-// (exact: the value is +-s or 0) straight into LDS and multiplied with fp16
-// x' tiles by v_mfma_f32_32x32x16_f16 with fp32 accumulation.
+// (exact: the value is +-s or 0) in registers and multiplied with fp16 x'
+// tiles by v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //
 // Tiling: a 256-thread workgroup computes a 128 (tokens) x 256 (weight rows)
 // block of Y; each of its four waves owns 64 weight rows (one row tile of
 // the packed layout) and all 128 tokens: 4 x 2 MFMA tiles of 32 x 32, K
-// stepping by 64 (one 16-byte packed chunk per weight row).
-//   * activations: the 128 x 64 fp16 tile of a step is staged in LDS
-//     (double-buffered, shared by the four waves); the loads of step k+1 are
-//     in flight while the matrix cores work on step k;
-//   * weights: every lane loads the packed chunk of its own weight row
-//     straight into registers (2 bits per weight: 1 KiB per wave per step)
+// stepping by 128 (two 16-byte packed chunks per weight row, one scale
+// group).
+//   * activations: the 128 x 128 fp16 tile of a step goes from global memory
+//     straight into LDS (gfx950 global-to-LDS loads, no registers on the
+//     way), double-buffered and shared by the four waves; the loads of step
+//     k+1 are in flight while the matrix cores work on step k;
+//   * weights: every lane loads the packed chunks of its own weight row
+//     straight into registers (2 bits per weight: 2 KiB per wave per step)
 //     and decodes the codes it feeds to the MFMA to fp16 s*t in registers --
 //     exact, since the value is +-s or 0 -- so the weights never touch LDS.
-//     The decode (a few VALU operations per pair of weights) overlaps the
-//     MFMAs of the other waves; the tall wave tile (128 tokens) spreads it
-//     over four MFMA rows.
+//     The decode (two byte permutes per pair of weights, reading a table of
+//     -s, 0, +s built once per scale) overlaps the MFMAs of the other waves;
+//     the tall wave tile (128 tokens) spreads it over four MFMA rows.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -38,29 +40,54 @@ using bgg::ceil_div;
 
 namespace {
 
-constexpr int kBM = 128, kBN = 256, kBK = 64;
-constexpr int kLdsStride = kBK + 8;  // halves per LDS row (+16 bytes against bank conflicts)
+constexpr int kBM = 128, kBN = 256, kBK = 64;  // kBK: one packed chunk
 constexpr int kTileRows = BGG_ROW_TILE;
 
-// K split (gridDim.z == 2): workgroup z runs K steps [0, kmid) or [kmid,
-// steps) and writes fp32 partial sums to P[z][M][N]; k_gemm_sum2 adds the two
-// and rounds to fp16.  gridDim.z == 1: all of K, fp16 y.
+// K split (gridDim.z == 2): workgroup z runs the 64-wide K chunks [0, kmid)
+// or [kmid, K / 64) (kmid even, so both are whole 128-wide steps) and writes
+// fp32 partial sums to P[z][M][N]; k_gemm_sum2 adds the two and rounds to
+// fp16.  gridDim.z == 1: all of K, fp16 y.
+//
+// An LDS activation buffer holds the 128 x 128 tile of a step as 16-byte
+// pieces, piece q (halves 8q..8q+7) of row r at slot r * 16 + (q ^ (r & 15)).
+// A global-to-LDS load writes the 16 bytes of lane l at the wave's LDS base
+// + 16 l, so one load instruction fills four whole rows (each lane fetching
+// the piece its slot holds), and the MFMA reads (sixteen consecutive rows
+// at one q per 16 lanes) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int a_slot(int r, int q) { return r * 16 + (q ^ (r & 15)); }
+
+// Wait for this wave's outstanding loads (global-to-LDS included) and LDS
+// reads, then the workgroup barrier.  Written out because the fence that
+// __syncthreads carries would make the compiler wait for them all before
+// every barrier anyway, while the "memory" clobber keeps it from moving LDS
+// accesses across this point.
+__device__ __forceinline__ void lds_dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __global__ void __launch_bounds__(256, 2)
     k_gemm_pq2(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
                uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
                int64_t NT, int64_t kmid, float* __restrict__ P, uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint4 As0[kBM * 16];
+  __shared__ __attribute__((aligned(16))) uint4 As1[kBM * 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
 
-  // activation loader: row tid/2 of the tile, k half tid%2 (32 values);
-  // rows past M re-read row M-1 (never stored)
-  const int lr = tid >> 1, lh = tid & 1;
-  const int64_t am = m0 + lr < M ? m0 + lr : M - 1;
-  const uint16_t* a_src = X + am * K + lh * 32;
+  // activation loader: load instruction i of this wave fills slots
+  // (8 wave + i) * 64 + lane, i.e. row (8 wave + i) * 4 + lane / 16, piece
+  // (lane % 16) ^ (row & 15); rows past M re-read row M-1 (never stored)
+  const uint16_t* a_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (8 * wave + i) * 4 + (lane >> 4);
+    const int q = (lane & 15) ^ (r & 15);
+    const int64_t am = m0 + r < M ? m0 + r : M - 1;
+    a_src[i] = X + am * K + 8 * q;
+  }
 
   // this wave's weight rows: row tile n0/64 + wave (past the last tile it
   // re-reads the last one and stores nothing); N-subtile j holds rows
@@ -80,78 +107,71 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Software pipeline over K steps of 64: the activation pieces of step
-  // ks+2 and the packed chunks and scales of step ks+1 are loaded while step
-  // ks is multiplied; step ks+1's activations (loaded one iteration earlier)
-  // go to the other LDS buffer at the end of the iteration.  Loads past the
-  // last step re-read the last step (no branch splits the registers), and
-  // the two activation register sets alternate, so the loop is unrolled by
-  // two (K / 64 is even since K is a multiple of 128).
-  // this workgroup's K steps [kb, steps): both ranges have even lengths
-  const int64_t kb = blockIdx.z == 0 ? 0 : kmid;
-  const int64_t steps = gridDim.z == 1 || blockIdx.z == 1 ? K / kBK : kmid;
-  uint4 xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3, b0, b1;
+  // this workgroup's 128-wide K steps [kb, steps).  Step ks multiplies the
+  // buffer filled during step ks-1 while step ks+1's activations stream into
+  // the other buffer and its packed chunks (b2/b3: the second chunk) and
+  // scales into registers (the last step reloads its own activations into
+  // the idle buffer instead); each step ends with every wave's loads landed
+  // and the barrier.  The loop is unrolled by two so that each buffer is its
+  // own LDS object, which lets the compiler see that the loads in flight
+  // never write the buffer being read.
+  const int64_t kb = (blockIdx.z == 0 ? 0 : kmid) / 2;
+  const int64_t steps = (gridDim.z == 1 || blockIdx.z == 1 ? K / kBK : kmid) / 2;
+  uint4 b0, b1, b2, b3;
   uint16_t s0, s1;
-#define BGG_LOAD_A(KS, R0, R1, R2, R3)                                       \
-  do {                                                                       \
-    const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                     \
-    const uint4* ap_ = reinterpret_cast<const uint4*>(a_src + kc_ * kBK);    \
-    R0 = ap_[0], R1 = ap_[1], R2 = ap_[2], R3 = ap_[3];                      \
+#define BGG_LOAD_A(KS, BUF)                                                   \
+  do {                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                             \
+      __builtin_amdgcn_global_load_lds(                                       \
+          a_src[i] + (KS) * 128,                                              \
+          (__attribute__((address_space(3))) void*)&BUF[(8 * wave + i) * 64], \
+          16, 0, 0);                                                          \
   } while (0)
-#define BGG_LOAD_B(KS)                                                       \
-  do {                                                                       \
-    const int64_t kc_ = (KS) < steps ? (KS) : steps - 1;                     \
-    b0 = b_src[kc_ * kTileRows], b1 = b_src[kc_ * kTileRows + 32];           \
+#define BGG_LOAD_B(KS)                                                        \
+  do {                                                                        \
+    const int64_t kc_ = 2 * ((KS) < steps ? (KS) : steps - 1);                \
+    b0 = b_src[kc_ * kTileRows], b1 = b_src[kc_ * kTileRows + 32];            \
+    b2 = b_src[(kc_ + 1) * kTileRows], b3 = b_src[(kc_ + 1) * kTileRows + 32]; \
     s0 = s_src[(kc_ / 2) * kTileRows], s1 = s_src[(kc_ / 2) * kTileRows + 32]; \
   } while (0)
-#define BGG_STORE_A(BUF, R0, R1, R2, R3)                                     \
-  do {                                                                       \
-    uint4* d_ = reinterpret_cast<uint4*>(&As[BUF][lr * kLdsStride + lh * 32]); \
-    d_[0] = R0, d_[1] = R1, d_[2] = R2, d_[3] = R3;                          \
-  } while (0)
-#define BGG_STEP(KS, CUR, L0, L1, L2, L3, S0, S1, S2, S3)                    \
-  do {                                                                       \
-    const uint4 bw[2] = {b0, b1};                                            \
-    __half2 s2[2];                                                           \
-    s2[0] = __halves2half2(__ushort_as_half(s0), __ushort_as_half(s0));      \
-    s2[1] = __halves2half2(__ushort_as_half(s1), __ushort_as_half(s1));      \
-    BGG_LOAD_A((KS) + 2, L0, L1, L2, L3);                                    \
-    BGG_LOAD_B((KS) + 1);                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                       \
-    _Pragma("unroll") for (int kk = 0; kk < kBK / 16; ++kk) {                \
-      f16x8 a[4], b[2];                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) a[i] =                   \
-          *reinterpret_cast<const f16x8*>(                                   \
-              &As[CUR][(i * 32 + li) * kLdsStride + kk * 16 + h * 8]);       \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                        \
-        const uint32_t w_ = kk == 0 ? bw[j].x : kk == 1 ? bw[j].y            \
-                            : kk == 2 ? bw[j].z : bw[j].w;                   \
-        b[j] = decode8_pq2(w_ >> (16 * h), s2[j]);                               \
-      }                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                          \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =           \
+#define BGG_STEP(KS, CUR, NXT)                                                \
+  do {                                                                        \
+    const uint4 bw[2][2] = {{b0, b1}, {b2, b3}};                              \
+    const bgg::Pq2Table tb[2] = {bgg::pq2_table(s0), bgg::pq2_table(s1)};     \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+    BGG_LOAD_A((KS) + 1 < steps ? (KS) + 1 : (KS), NXT);                      \
+    BGG_LOAD_B((KS) + 1);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) {                        \
+      f16x8 a[4], b[2];                                                       \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) a[i] =                    \
+          *reinterpret_cast<const f16x8*>(&CUR[a_slot(i * 32 + li, 2 * kk + h)]); \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                         \
+        const uint4 c_ = bw[kk >> 2][j];                                      \
+        const int k4_ = kk & 3;                                               \
+        const uint32_t w_ = k4_ == 0 ? c_.x : k4_ == 1 ? c_.y : k4_ == 2 ? c_.z : c_.w; \
+        b[j] = decode8_pq2(w_, 16 * h, tb[j]);                                \
+      }                                                                       \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                           \
+          _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =            \
           __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0); \
-    }                                                                        \
-    BGG_STORE_A((CUR) ^ 1, S0, S1, S2, S3);                                  \
-    __syncthreads();                                                         \
+    }                                                                         \
+    lds_dma_barrier();                                                        \
   } while (0)
 
-  BGG_LOAD_A(kb, xa0, xa1, xa2, xa3);
+  BGG_LOAD_A(kb, As0);
   BGG_LOAD_B(kb);
-  BGG_STORE_A(0, xa0, xa1, xa2, xa3);
-  BGG_LOAD_A(kb + 1, ya0, ya1, ya2, ya3);
-  __syncthreads();
-  for (int64_t ks = kb; ks < steps; ks += 2) {
-    BGG_STEP(ks, 0, xa0, xa1, xa2, xa3, ya0, ya1, ya2, ya3);
-    BGG_STEP(ks + 1, 1, ya0, ya1, ya2, ya3, xa0, xa1, xa2, xa3);
+  lds_dma_barrier();
+  int64_t ks = kb;
+  for (; ks + 1 < steps; ks += 2) {
+    BGG_STEP(ks, As0, As1);
+    BGG_STEP(ks + 1, As1, As0);
   }
+  if (ks < steps) BGG_STEP(ks, As0, As1);
 #undef BGG_LOAD_A
 #undef BGG_LOAD_B
-#undef BGG_STORE_A
 #undef BGG_STEP
 
-  // D layout of a 32x32 tile: lane l holds column l%32 (a weight row), rows
-  // (tokens) 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
   if (!w_ok) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -293,10 +313,10 @@ __global__ void __launch_bounds__(256, 2)
 #define BGG_STEP3(KS, CUR, L, S)                                                \
   do {                                                                         \
     const uint4 bw = bown;                                                     \
-    __half2 s2[2][2];                                                          \
+    bgg::Pq2Table tb[2][2];                                                    \
     _Pragma("unroll") for (int e = 0; e < 2; ++e) {                            \
-      s2[0][e] = __halves2half2(__ushort_as_half(s0[e]), __ushort_as_half(s0[e])); \
-      s2[1][e] = __halves2half2(__ushort_as_half(s1[e]), __ushort_as_half(s1[e])); \
+      tb[0][e] = bgg::pq2_table(s0[e]);                                        \
+      tb[1][e] = bgg::pq2_table(s1[e]);                                        \
     }                                                                          \
     /* lane (li, h) turns the chunk of its own row 32 h + li into the 80     \
        codes (five words of sixteen 2-bit codes), keeps the halves its K   \
@@ -347,7 +367,7 @@ __global__ void __launch_bounds__(256, 2)
           *reinterpret_cast<const f16x8*>(                                     \
               &As[CUR][(i * 32 + li) * kLdsStride3 + kk * 16 + h * 8]);        \
       _Pragma("unroll") for (int j = 0; j < 2; ++j)                            \
-          b[j] = decode8_pq2(ch[j][kk / 2] >> (16 * (kk % 2)), sel_ ? s2[j][1] : s2[j][0]); \
+          b[j] = decode8_pq2(ch[j][kk / 2], 16 * (kk % 2), sel_ ? tb[j][1] : tb[j][0]); \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                            \
           _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =             \
           __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0); \

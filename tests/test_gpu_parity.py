@@ -441,6 +441,22 @@ def test_gemm_parity(env, fmt, M, N, K):
     assert np.all(relerr(y2, oracle_y(fmt, T, S, xr, rotate=False)) <= TOL)
 
 
+def test_gemm_pq2_basis_vectors_bit_exact(env):
+    """PQ2_0 GEMM, rotation off, x = e_k for every k of K = 384 (three
+    128-wide K steps, so the last one runs alone): y_n = S[n][k/128] T[n][k]
+    exactly.  Every activation piece position of the LDS layout and every
+    code slot of the weight decode is hit by one token."""
+    bgg, torch = env
+    N, K = 130, 384
+    T, S = gen_matrix(46, 2, N, K)
+    d = Dev(bgg, torch, "PQ2_0", T, S)
+    x = np.eye(K, dtype=np.float16)
+    y = d.gemm(x, rotate=False)
+    want = (np.repeat(S.astype(np.float64), 128, axis=1)[:, :K] * T).astype(np.float16).T
+    bad = np.argwhere(y.view(np.uint16) != want.view(np.uint16))
+    assert bad.size == 0, f"first mismatches (k, n): {bad[:5].tolist()}"
+
+
 def test_gemm_ptq1_basis_vectors_bit_exact(env):
     """PTQ1_0 GEMM, rotation off, x = e_k: y_n = S[n][k/128] T[n][k] exactly
     (one non-zero product per output), at chunk and group edges."""
