@@ -649,7 +649,8 @@ def main() -> int:
             roofline=dict(bound="mfma", achieved=round(tf, 1), peak=F16_MFMA_PEAK_TFLOPS,
                           unit="TFLOP/s", frac=round(tf / F16_MFMA_PEAK_TFLOPS, 4), traffic=None,
                           kernel="k_gemm_pq2 (fp16 MFMA, fp32 accumulate)"),
-            ptq1_0=dict(kernel="k_gemm_ptq1", tflops=round(tf3, 1),
+            ptq1_0=dict(kernel="k_ptq1_to_pq2 (weights rewritten to PQ2_0 once per call) + k_gemm_pq2",
+                        tflops=round(tf3, 1),
                         frac=round(tf3 / F16_MFMA_PEAK_TFLOPS, 4), shapes=ptq1),
             dense_fp16_comparison=dict(kernel="torch.matmul (hipBLASLt) on dequantised fp16 W, run only",
                                        tflops=round(tfd, 1), frac=round(tfd / F16_MFMA_PEAK_TFLOPS, 4),

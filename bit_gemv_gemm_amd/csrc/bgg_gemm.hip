@@ -67,7 +67,8 @@ __device__ __forceinline__ void lds_dma_barrier() {
 
 __global__ void __launch_bounds__(256, 2)
     k_gemm_pq2(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
-               uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
+               const uint16_t* __restrict__ scales, int64_t M, int64_t N, int64_t K, int64_t C,
+               int64_t G,
                int64_t NT, int64_t kmid, float* __restrict__ P, uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint4 As0[kBM * 16];
   __shared__ __attribute__((aligned(16))) uint4 As1[kBM * 16];
@@ -96,8 +97,7 @@ __global__ void __launch_bounds__(256, 2)
   const bool w_ok = tw < NT;
   const int64_t tcl = w_ok ? tw : NT - 1;
   const uint4* b_src = reinterpret_cast<const uint4*>(packed) + tcl * C * kTileRows + li;
-  const uint16_t* s_src =
-      reinterpret_cast<const uint16_t*>(packed + scale_offset) + tcl * G * kTileRows + li;
+  const uint16_t* s_src = scales + tcl * G * kTileRows + li;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -234,7 +234,8 @@ constexpr int kLdsStride3 = kBK3 + 8;  // halves per LDS row (176 bytes)
 
 __global__ void __launch_bounds__(256, 2)
     k_gemm_ptq1(const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
-                uint64_t scale_offset, int64_t M, int64_t N, int64_t K, int64_t C, int64_t G,
+                const uint16_t* __restrict__ scales, int64_t M, int64_t N, int64_t K, int64_t C,
+                int64_t G,
                 int64_t NT, int64_t kmid, float* __restrict__ P, uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride3];
   __shared__ uint32_t lut[256];
@@ -269,8 +270,7 @@ __global__ void __launch_bounds__(256, 2)
   const bool w_ok = tw < NT;
   const int64_t tcl = w_ok ? tw : NT - 1;
   const uint4* b_src = reinterpret_cast<const uint4*>(packed) + tcl * C * kTileRows + li;
-  const uint16_t* s_src =
-      reinterpret_cast<const uint16_t*>(packed + scale_offset) + tcl * G * kTileRows + li;
+  const uint16_t* s_src = scales + tcl * G * kTileRows + li;
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -409,15 +409,84 @@ __global__ void __launch_bounds__(256, 2)
     }
 }
 
+// ---------------------------------------------------------------------------
+// PTQ1_0 -> PQ2_0 row streams of one matrix (wmrh.cn/news/471187, section
+// 关键机制: five trits per byte; allhereai.com/news/1346, packing paragraph:
+// the 2-bit packing is the one that wins prompt processing).  When the
+// workspace has room, the PTQ1_0 GEMM rewrites its weights once per call
+// into the PQ2_0 device layout (same tiles, same scales) and runs k_gemm_pq2: the rewrite streams
+// 1.6 + 2 bits per weight once, where the byte-to-code conversion inside
+// k_gemm_ptq1 runs again for every 128 tokens.  Exact: both layouts hold the
+// same trits.  k_gemm_ptq1 remains for calls without room for the rewrite.
+//
+// One thread per (row tile, 320-trit block, row of the tile): four PTQ1_0
+// chunks (64 bytes, each byte five codes t + 1 low digit first, ten bits from
+// a 256-entry table) in, the 640-bit code string = five PQ2_0 chunks out.
+// Chunks past the end of the row are neither read nor written; bytes past
+// 242 read as zero trits.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+    k_ptq1_to_pq2(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t C3, int64_t C2,
+                  int64_t nblk, int64_t total) {
+  __shared__ uint32_t lut[256];
+  {
+    uint32_t b = threadIdx.x, c = 0;
+    if (b < 243) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        c |= (b % 3u) << (2 * i);
+        b /= 3u;
+      }
+    } else {
+      c = 0x155u;
+    }
+    lut[threadIdx.x] = c;
+  }
+  __syncthreads();
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t li = idx & 63, rest = idx >> 6;
+  const int64_t blk = rest % nblk, t = rest / nblk;
+  uint32_t w[20];
+#pragma unroll
+  for (int i = 0; i < 20; ++i) w[i] = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t c = 4 * blk + j;
+    const uint4 v = c < C3 ? src[(t * C3 + c) * 64 + li] : make_uint4(0, 0, 0, 0);
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t code = lut[(vw[q >> 2] >> (8 * (q & 3))) & 0xFFu];
+      const int pos = 10 * (16 * j + q);  // bit of this byte's first code
+      w[pos >> 5] |= code << (pos & 31);
+      if ((pos & 31) > 22) w[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int64_t c = 5 * blk + j;
+    if (c < C2) dst[(t * C2 + c) * 64 + li] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+  }
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// What one call does beyond the product itself, in workspace order: the
+// rotated x', the PTQ1_0 weights rewritten to PQ2_0, the fp32 K-split
+// partials.
+struct GemmPlan {
+  bool rewrite;  // PTQ1_0 weights rewritten, k_gemm_pq2 runs
+  bool split;    // K split in two, k_gemm_sum2 adds the halves
+  uint64_t rot_bytes, rewrite_bytes, part_bytes;
+};
 
 // K split in two when the output blocks fill the resident workgroup slots
 // (two per CU) much less evenly than twice as many would: the last, partly
 // empty round of workgroups (e.g. 640 blocks on 512 slots for 4096 tokens x
 // 5120 rows) costs as much as a full one.  The fp32 partials cost an extra
 // pass over 2 M N floats, so the split must gain at least 15 %.
-bool gemm_split(const bgg_weights_desc* d, int64_t M) {
-  const int64_t steps = d->format == BGG_FMT_PQ2_0 ? d->K / kBK : d->chunks;
+bool gemm_split(const bgg_weights_desc* d, int64_t M, int64_t steps) {
   if (steps < 8) return false;
   const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
   const double wgs = (double)((d->N + kBN - 1) / kBN) * (double)((mc + kBM - 1) / kBM);
@@ -426,14 +495,35 @@ bool gemm_split(const bgg_weights_desc* d, int64_t M) {
   return eff2 > 1.15 * eff1;
 }
 
-uint64_t gemm_rot_bytes(const bgg_weights_desc* d, int64_t M) {
-  return ((uint64_t)M * d->K * 2 + 255) & ~uint64_t(255);
-}
-
-// fp32 partials of one launch (at most 65535 token blocks)
-uint64_t gemm_part_bytes(const bgg_weights_desc* d, int64_t M) {
-  const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
-  return (uint64_t)2 * mc * d->N * 4;
+// The plan for M tokens given `avail` workspace bytes (UINT64_MAX: as much
+// as the plan wants).  Each optional part runs only if the workspace also
+// holds it; the rotation is not optional (the caller checks it).
+GemmPlan gemm_plan(const bgg_weights_desc* d, int64_t M, bool rotate, uint64_t avail) {
+  GemmPlan p{};
+  p.rot_bytes = rotate ? bgg::align256((uint64_t)M * d->K * 2) : 0;
+  uint64_t used = p.rot_bytes;
+  // PTQ1_0: the rewrite to PQ2_0 costs one pass over 3.85 bits per weight
+  // (5-11 us for the projection shapes), less than what the PQ2_0 kernel
+  // saves at any token count
+  if (d->format == BGG_FMT_PTQ1_0) {
+    const uint64_t b = bgg::align256((uint64_t)d->row_tiles * kTileRows * (uint64_t)d->K / 4);
+    if (avail >= used && avail - used >= b) {
+      p.rewrite = true;
+      p.rewrite_bytes = b;
+      used += b;
+    }
+  }
+  const bool pq2 = d->format == BGG_FMT_PQ2_0 || p.rewrite;
+  if (gemm_split(d, M, pq2 ? d->K / kBK : d->chunks)) {
+    // fp32 partials of one launch (at most 65535 token blocks)
+    const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
+    const uint64_t b = (uint64_t)2 * mc * d->N * 4;
+    if (avail >= used && avail - used >= b) {
+      p.split = true;
+      p.part_bytes = b;
+    }
+  }
+  return p;
 }
 
 }  // namespace
@@ -442,7 +532,8 @@ extern "C" {
 
 size_t bgg_gemm_workspace_size(const bgg_weights_desc* d, int64_t M) {
   if (bgg::check_desc(d) != BGG_OK || M < 1) return 0;
-  return (size_t)(gemm_rot_bytes(d, M) + (gemm_split(d, M) ? gemm_part_bytes(d, M) : 0));
+  const GemmPlan p = gemm_plan(d, M, true, UINT64_MAX);
+  return (size_t)(p.rot_bytes + p.rewrite_bytes + p.part_bytes);
 }
 
 bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, const void* x_dev,
@@ -463,23 +554,31 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
   if (workspace && !aligned16(workspace))
     return fail(BGG_ERR_BUFFER, "bgg_ternary_gemm: misaligned workspace");
   hipStream_t s = (hipStream_t)stream;
+  const bool rotate = (flags & BGG_ROTATE_INPUT) != 0;
+  const GemmPlan p = gemm_plan(d, M, rotate, workspace ? (uint64_t)workspace_bytes : 0);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const void* xr = x_dev;
-  uint64_t used = 0;
-  if (flags & BGG_ROTATE_INPUT) {
-    const uint64_t need = gemm_rot_bytes(d, M);
-    if (!workspace || workspace_bytes < need)
+  if (rotate) {
+    if (!workspace || workspace_bytes < p.rot_bytes)
       return fail(BGG_ERR_BUFFER, "bgg_ternary_gemm: rotation needs a 16-byte aligned workspace "
-                                  "of %llu bytes", (unsigned long long)need);
+                                  "of %llu bytes", (unsigned long long)p.rot_bytes);
     if ((st = bgg_hadamard_rotate(x_dev, workspace, M, d->K, stream))) return st;
     xr = workspace;
-    used = need;
   }
-  // the K split runs only when the workspace also holds its partials
-  float* P = nullptr;
-  if (workspace && gemm_split(d, M) && workspace_bytes >= used + gemm_part_bytes(d, M))
-    P = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + used);
-  const int64_t steps = d->format == BGG_FMT_PQ2_0 ? d->K / kBK : d->chunks;
-  const int64_t kmid = (steps / 2) & ~int64_t(1);  // even: both halves stay even
+  const uint8_t* wts = (const uint8_t*)packed_dev;
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(wts + d->scale_offset);
+  const bool pq2 = d->format == BGG_FMT_PQ2_0 || p.rewrite;
+  const int64_t C = pq2 ? d->K / kBK : d->chunks;  // chunks per row of the kernel's layout
+  if (p.rewrite) {
+    uint8_t* dst = ws + p.rot_bytes;
+    const int64_t nblk = ceil_div(C, 5);
+    const int64_t total = d->row_tiles * nblk * kTileRows;
+    hipLaunchKernelGGL(k_ptq1_to_pq2, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s,
+                       (const uint4*)packed_dev, (uint4*)dst, d->chunks, C, nblk, total);
+    wts = dst;
+  }
+  float* P = p.split ? reinterpret_cast<float*>(ws + p.rot_bytes + p.rewrite_bytes) : nullptr;
+  const int64_t kmid = (C / 2) & ~int64_t(1);  // even: both halves stay even
   // token blocks go on grid.y, which holds at most 65535 blocks: longer
   // prompts run as several launches over consecutive token ranges
   const int64_t max_m = int64_t(65535) * kBM;
@@ -488,10 +587,9 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
     const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM),
                     P ? 2u : 1u);
     uint16_t* y = (uint16_t*)y_dev + m0 * d->N;
-    hipLaunchKernelGGL(d->format == BGG_FMT_PQ2_0 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
-                       (const uint16_t*)xr + m0 * d->K, (const uint8_t*)packed_dev,
-                       d->scale_offset, mc, d->N, d->K, d->chunks, d->groups, d->row_tiles, kmid,
-                       P, y);
+    hipLaunchKernelGGL(pq2 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
+                       (const uint16_t*)xr + m0 * d->K, wts, scales, mc, d->N, d->K, C, d->groups,
+                       d->row_tiles, kmid, P, y);
     if (P) {
       const int64_t mn = mc * d->N;
       hipLaunchKernelGGL(k_gemm_sum2, dim3((unsigned)ceil_div(ceil_div(mn, 4), 256)), dim3(256), 0,

@@ -321,15 +321,21 @@ size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
  * prompt processing, where PQ2_0 is the faster packing].  Trits are decoded
  * to fp16 s*t (exact) in registers and multiplied with fp16 x' tiles staged
  * in LDS on the matrix cores, fp32 accumulation, fp16 y.  PTQ1_0's base-3
- * bytes are first turned into 2-bit codes (an LDS table per byte value).
+ * bytes [C: five trits per byte] are turned into 2-bit codes (an LDS table
+ * per byte value): when the workspace holds them, by rewriting the weights
+ * once per call into the PQ2_0 layout, which the PQ2_0 product then reads;
+ * else inside the product, for every block of 128 tokens.
  *   x_dev      device fp16 [M][K] (model coordinates with BGG_ROTATE_INPUT,
  *              else already rotated); y_dev device fp16 [M][N]
  *   workspace  device, 16-byte aligned, bgg_gemm_workspace_size(desc, M)
- *              bytes: x' when BGG_ROTATE_INPUT is set, then, for shapes whose
- *              output blocks fill the GPU unevenly (few output rows, long K),
- *              the fp32 partial sums of a K split in two.  Smaller (down to
- *              x' only, or NULL without BGG_ROTATE_INPUT) runs without the
- *              split, whose last-bit rounding differs; each choice gives
+ *              bytes: x' when BGG_ROTATE_INPUT is set; then, for PTQ1_0,
+ *              the weights rewritten to PQ2_0 (the PQ2_0 trit bytes of the
+ *              same shape, 256-byte rounded); then, for
+ *              shapes whose output blocks fill the GPU unevenly (few output
+ *              rows, long K), the fp32 partial sums of a K split in two.  A
+ *              smaller workspace (down to x' only, or NULL without
+ *              BGG_ROTATE_INPUT) drops the later parts in that order: the
+ *              results differ in the last-bit rounding; each choice gives
  *              bit-identical y for the same inputs.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (Q1_0, Q2_0_G64),
  * BGG_ERR_SHAPE, BGG_ERR_BUFFER, BGG_ERR_HIP.

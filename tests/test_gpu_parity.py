@@ -457,21 +457,61 @@ def test_gemm_pq2_basis_vectors_bit_exact(env):
     assert bad.size == 0, f"first mismatches (k, n): {bad[:5].tolist()}"
 
 
-def test_gemm_ptq1_basis_vectors_bit_exact(env):
+def test_gemm_ptq1_rewrite_is_the_pq2_layout(env):
+    """With room in the workspace, the PTQ1_0 GEMM rewrites its weights to
+    PQ2_0 and runs the PQ2_0 kernel.  The rewritten
+    trits (at the start of the workspace when nothing is rotated) are the
+    PQ2_0 device layout of the same trits, byte for byte: read back to
+    canonical rows they equal the oracle's PQ2_0 packing (padding rows: zero
+    trits).  K = 1152: 15 PTQ1_0 chunks, 18 PQ2_0 chunks, the last 320-trit
+    block partial."""
+    bgg, torch = env
+    N, K, M = 130, 1152, 256
+    T, S = gen_matrix(47, 2, N, K, fmt="PTQ1_0")
+    d = Dev(bgg, torch, "PTQ1_0", T, S)
+    d2 = bgg.bgg_describe("PQ2_0", N, K)
+    ws = bgg.workspace(bgg.bgg_gemm_workspace_size(d.desc, M))
+    assert ws.numel() >= d2.trit_bytes
+    x = torch.from_numpy(synth.activations_f16(47, 3, M, K)).cuda()
+    y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    bgg.bgg_ternary_gemm(d.desc, d.packed, x, y, M, 0, ws)
+    torch.cuda.synchronize()
+    C2 = K // 64
+    buf = ws[:d2.trit_bytes].cpu().numpy()
+    rows = buf.reshape(d2.row_tiles, C2, 64, 16).transpose(0, 2, 1, 3).reshape(d2.row_tiles * 64, C2 * 16)
+    assert np.array_equal(rows[:N, :d2.row_bytes], oracle.pack("PQ2_0", T))
+    assert np.all(rows[N:] == 0x55)
+    ref = oracle_y("PTQ1_0", T, S, x.cpu().numpy(), rotate=False)
+    assert np.all(relerr(y.cpu().numpy(), ref) <= TOL)
+
+
+@pytest.mark.parametrize("M", [15, 1152])
+def test_gemm_ptq1_basis_vectors_bit_exact(env, M):
     """PTQ1_0 GEMM, rotation off, x = e_k: y_n = S[n][k/128] T[n][k] exactly
-    (one non-zero product per output), at chunk and group edges."""
+    (one non-zero product per output).  M = 15: the byte-table kernel (no
+    workspace), at chunk and group edges; M = 1152: every k, through the
+    weights rewritten to PQ2_0 (a workspace is given)."""
     bgg, torch = env
     N, K = 130, 1152
     T, S = gen_matrix(45, 2, N, K)
     d = Dev(bgg, torch, "PTQ1_0", T, S)
-    ks = [0, 1, 79, 80, 127, 128, 159, 160, 639, 640, 1039, 1040, 1119, 1120, 1151]
+    ks = ([0, 1, 79, 80, 127, 128, 159, 160, 639, 640, 1039, 1040, 1119, 1120, 1151] if M == 15
+          else list(range(K)))
     x = np.zeros((len(ks), K), np.float16)
     for i, k in enumerate(ks):
         x[i, k] = 1.0
-    y = d.gemm(x, rotate=False)
-    for j, k in enumerate(ks):
-        want = (S[:, k // 128].astype(np.float64) * T[:, k]).astype(np.float16)
-        assert np.array_equal(y[j].view(np.uint16), want.view(np.uint16)), f"k={k}"
+    if M == 15:
+        y = d.gemm(x, rotate=False)
+    else:
+        ws = bgg.workspace(bgg.bgg_gemm_workspace_size(d.desc, M))
+        xd = torch.from_numpy(x).cuda()
+        yd = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        bgg.bgg_ternary_gemm(d.desc, d.packed, xd, yd, M, 0, ws)
+        torch.cuda.synchronize()
+        y = yd.cpu().numpy()
+    want = (np.repeat(S.astype(np.float64), 128, axis=1)[:, :K] * T).astype(np.float16).T[ks]
+    bad = np.argwhere(y.view(np.uint16) != want.view(np.uint16))
+    assert bad.size == 0, f"first mismatches (token, n): {bad[:5].tolist()}"
 
 
 @pytest.mark.parametrize("fmt", GEMM_FMTS)
