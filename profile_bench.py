@@ -109,20 +109,25 @@ def traffic(fetch_csv: str, write_csv: str, calib_mib: int, out_json: str, cmd_f
 
 def counters(counter_csv: str, out_md: str, command: str, kernels_wanted) -> None:
     vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)  # kernel -> dispatch id -> duration in us (under the counter run)
     with open(counter_csv) as f:
         for r in csv.DictReader(f):
             name = short_name(r["Kernel_Name"])
             if any(name.startswith(k) for k in kernels_wanted):
                 vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    durs[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     names = sorted({c for v in vals.values() for c in v})
     lines = ["# Counters per dispatch (rocprofv3 --pmc)", "", "Command (run from the repository root, one MI355X):",
              "", "```", command, "```", "",
-             "| kernel | dispatches | " + " | ".join(names) + " |",
-             "|---|---:|" + "---:|" * len(names)]
+             "`us` is the average dispatch duration in the counter run itself.", "",
+             "| kernel | dispatches | us | " + " | ".join(names) + " |",
+             "|---|---:|---:|" + "---:|" * len(names)]
     for k in sorted(vals):
         n = max(len(v) for v in vals[k].values())
+        us = f"{statistics.mean(durs[k].values()):.2f}" if durs.get(k) else ""
         cells = [f"{statistics.mean(vals[k][c]):.4g}" if vals[k].get(c) else "" for c in names]
-        lines.append(f"| `{k}` | {n} | " + " | ".join(cells) + " |")
+        lines.append(f"| `{k}` | {n} | {us} | " + " | ".join(cells) + " |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
