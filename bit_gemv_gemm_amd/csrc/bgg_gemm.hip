@@ -43,10 +43,10 @@ namespace {
 constexpr int kBM = 128, kBN = 256, kBK = 64;  // kBK: one packed chunk
 constexpr int kTileRows = BGG_ROW_TILE;
 
-// K split (gridDim.z == 2): workgroup z runs the 64-wide K chunks [0, kmid)
-// or [kmid, K / 64) (kmid even, so both are whole 128-wide steps) and writes
-// fp32 partial sums to P[z][M][N]; k_gemm_sum2 adds the two and rounds to
-// fp16.  gridDim.z == 1: all of K, fp16 y.
+// K split in S = gridDim.z ranges (S <= K / 128): workgroup z runs the
+// 128-wide K steps [z T / S, (z + 1) T / S) of the T = K / 128 and writes
+// fp32 partial sums to P[z][M][N]; k_gemm_sum adds the S partials in order
+// z = 0, 1, ... and rounds to fp16.  gridDim.z == 1: all of K, fp16 y.
 //
 // An LDS activation buffer holds the 128 x 128 tile of a step as 16-byte
 // pieces, piece q (halves 8q..8q+7) of row r at slot r * 16 + (q ^ (r & 15)).
@@ -115,8 +115,9 @@ __global__ void __launch_bounds__(256, 2)
   // and the barrier.  The loop is unrolled by two so that each buffer is its
   // own LDS object, which lets the compiler see that the loads in flight
   // never write the buffer being read.
-  const int64_t kb = (blockIdx.z == 0 ? 0 : kmid) / 2;
-  const int64_t steps = (gridDim.z == 1 || blockIdx.z == 1 ? K / kBK : kmid) / 2;
+  const int64_t T = K / (2 * kBK);
+  const int64_t kb = (int64_t)blockIdx.z * T / gridDim.z;
+  const int64_t steps = (int64_t)(blockIdx.z + 1) * T / gridDim.z;
   uint4 b0, b1, b2, b3;
   uint16_t s0, s1;
 #define BGG_LOAD_A(KS, BUF)                                                   \
@@ -191,20 +192,23 @@ __global__ void __launch_bounds__(256, 2)
     }
 }
 
-// y = fp16(P[0] + P[1]) over M*N values, four per thread (16-byte loads
-// when M*N is a multiple of 4, so that the second partial is aligned too;
-// else, and for the tail, one by one).
-__global__ void __launch_bounds__(256) k_gemm_sum2(const float* __restrict__ P, int64_t MN,
-                                                   uint16_t* __restrict__ Y) {
+// y = fp16(P[0] + P[1] + ... + P[S-1]) over M*N values (fp32 sums in that
+// order), four per thread (16-byte loads when M*N is a multiple of 4, so
+// that every partial is aligned too; else, and for the tail, one by one).
+__global__ void __launch_bounds__(256) k_gemm_sum(const float* __restrict__ P, int S, int64_t MN,
+                                                  uint16_t* __restrict__ Y) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
   if (i + 4 <= MN && (MN & 3) == 0) {
-    const float4 a = *reinterpret_cast<const float4*>(P + i);
-    const float4 b = *reinterpret_cast<const float4*>(P + MN + i);
-    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(a.x + b.x)) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(a.y + b.y)) << 16);
-    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(a.z + b.z)) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(a.w + b.w)) << 16);
+    float4 a = *reinterpret_cast<const float4*>(P + i);
+    for (int z = 1; z < S; ++z) {
+      const float4 b = *reinterpret_cast<const float4*>(P + z * MN + i);
+      a.x += b.x, a.y += b.y, a.z += b.z, a.w += b.w;
+    }
+    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(a.x)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(a.y)) << 16);
+    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(a.z)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(a.w)) << 16);
     if (((uintptr_t)(Y + i) & 7) == 0) {
       *reinterpret_cast<uint2*>(Y + i) = make_uint2(lo, hi);
     } else {
@@ -213,7 +217,11 @@ __global__ void __launch_bounds__(256) k_gemm_sum2(const float* __restrict__ P, 
     }
   } else {
     const int64_t e = i + 4 < MN ? i + 4 : MN;
-    for (int64_t k = i; k < e; ++k) Y[k] = __half_as_ushort(__float2half_rn(P[k] + P[MN + k]));
+    for (int64_t k = i; k < e; ++k) {
+      float a = P[k];
+      for (int z = 1; z < S; ++z) a += P[z * MN + k];
+      Y[k] = __half_as_ushort(__float2half_rn(a));
+    }
   }
 }
 
@@ -477,22 +485,42 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // partials.
 struct GemmPlan {
   bool rewrite;  // PTQ1_0 weights rewritten, k_gemm_pq2 runs
-  bool split;    // K split in two, k_gemm_sum2 adds the halves
+  int splits;    // K ranges (gridDim.z); from 2 on, k_gemm_sum adds the partials
   uint64_t rot_bytes, rewrite_bytes, part_bytes;
 };
 
-// K split in two when the output blocks fill the resident workgroup slots
-// (two per CU) much less evenly than twice as many would: the last, partly
-// empty round of workgroups (e.g. 640 blocks on 512 slots for 4096 tokens x
-// 5120 rows) costs as much as a full one.  The fp32 partials cost an extra
-// pass over 2 M N floats, so the split must gain at least 15 %.
-bool gemm_split(const bgg_weights_desc* d, int64_t M, int64_t steps) {
-  if (steps < 8) return false;
-  const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
+constexpr int kMaxSplits = 32;
+
+// K ranges for a product of `wgs` output blocks over T 128-wide K steps.
+//  * Output blocks that do not fill the resident workgroup slots (two per
+//    CU; short prompts): S ranges with S * wgs within the slots, S chosen to
+//    minimise T / S steps of about 3.2 us plus the fp32 partials (S M N
+//    floats written and read once more, at about 5 TB/s, and the adding
+//    launch).  A 64-token gate/up product runs 7 ranges, k/v 32.
+//  * Otherwise two ranges when the blocks fill the slots much less evenly
+//    than twice as many would (the last, partly empty round of workgroups,
+//    e.g. 640 blocks on 512 slots for 4096 tokens x 5120 rows, costs nearly
+//    as much as a full one) by at least 15 %, which the extra pass over the
+//    partials must repay.
+// `steps` counts the kernel's own K steps (128-wide; 80-wide chunks for
+// k_gemm_ptq1, which takes at most two ranges).
+int gemm_splits(const bgg_weights_desc* d, int64_t mc, int64_t steps, bool any_split) {
   const double wgs = (double)((d->N + kBN - 1) / kBN) * (double)((mc + kBM - 1) / kBM);
-  const double waves = wgs / (double)(2 * bgg::device_cus());
+  const double slots = (double)(2 * bgg::device_cus());
+  if (any_split && wgs < slots) {
+    const double mn = (double)mc * (double)d->N;
+    int best = 1;
+    double best_t = (double)steps * 3.2e-6;
+    for (int S = 2; S <= kMaxSplits && S <= steps && S * wgs <= slots; ++S) {
+      const double t = (double)steps / S * 3.2e-6 + (double)S * mn * 8.0 / 5e12 + 3e-6;
+      if (t < best_t) best = S, best_t = t;
+    }
+    return best;
+  }
+  if (steps < 4) return 1;
+  const double waves = wgs / slots;
   const double eff1 = waves / std::ceil(waves), eff2 = 2 * waves / std::ceil(2 * waves);
-  return eff2 > 1.15 * eff1;
+  return eff2 > 1.15 * eff1 ? 2 : 1;
 }
 
 // The plan for M tokens given `avail` workspace bytes (UINT64_MAX: as much
@@ -500,9 +528,10 @@ bool gemm_split(const bgg_weights_desc* d, int64_t M, int64_t steps) {
 // holds it; the rotation is not optional (the caller checks it).
 GemmPlan gemm_plan(const bgg_weights_desc* d, int64_t M, bool rotate, uint64_t avail) {
   GemmPlan p{};
+  p.splits = 1;
   p.rot_bytes = rotate ? bgg::align256((uint64_t)M * d->K * 2) : 0;
   uint64_t used = p.rot_bytes;
-  // PTQ1_0: the rewrite to PQ2_0 costs one pass over 3.85 bits per weight
+  // PTQ1_0: the rewrite to PQ2_0 costs one pass over 3.6 bits per weight
   // (5-11 us for the projection shapes), less than what the PQ2_0 kernel
   // saves at any token count
   if (d->format == BGG_FMT_PTQ1_0) {
@@ -514,12 +543,13 @@ GemmPlan gemm_plan(const bgg_weights_desc* d, int64_t M, bool rotate, uint64_t a
     }
   }
   const bool pq2 = d->format == BGG_FMT_PQ2_0 || p.rewrite;
-  if (gemm_split(d, M, pq2 ? d->K / kBK : d->chunks)) {
-    // fp32 partials of one launch (at most 65535 token blocks)
-    const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
-    const uint64_t b = (uint64_t)2 * mc * d->N * 4;
+  // fp32 partials of one launch (at most 65535 token blocks)
+  const int64_t mc = M < int64_t(65535) * kBM ? M : int64_t(65535) * kBM;
+  const int S = gemm_splits(d, mc, pq2 ? d->K / (2 * kBK) : d->chunks, pq2);
+  if (S > 1) {
+    const uint64_t b = (uint64_t)S * mc * d->N * 4;
     if (avail >= used && avail - used >= b) {
-      p.split = true;
+      p.splits = S;
       p.part_bytes = b;
     }
   }
@@ -577,23 +607,23 @@ bgg_status bgg_ternary_gemm(const bgg_weights_desc* d, const void* packed_dev, c
                        (const uint4*)packed_dev, (uint4*)dst, d->chunks, C, nblk, total);
     wts = dst;
   }
-  float* P = p.split ? reinterpret_cast<float*>(ws + p.rot_bytes + p.rewrite_bytes) : nullptr;
-  const int64_t kmid = (C / 2) & ~int64_t(1);  // even: both halves stay even
+  float* P = p.splits > 1 ? reinterpret_cast<float*>(ws + p.rot_bytes + p.rewrite_bytes) : nullptr;
+  const int64_t kmid = (C / 2) & ~int64_t(1);  // k_gemm_ptq1's two ranges (k_gemm_pq2: unused)
   // token blocks go on grid.y, which holds at most 65535 blocks: longer
   // prompts run as several launches over consecutive token ranges
   const int64_t max_m = int64_t(65535) * kBM;
   for (int64_t m0 = 0; m0 < M; m0 += max_m) {
     const int64_t mc = M - m0 < max_m ? M - m0 : max_m;
     const dim3 grid((unsigned)((d->N + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM),
-                    P ? 2u : 1u);
+                    (unsigned)p.splits);
     uint16_t* y = (uint16_t*)y_dev + m0 * d->N;
     hipLaunchKernelGGL(pq2 ? k_gemm_pq2 : k_gemm_ptq1, grid, dim3(256), 0, s,
                        (const uint16_t*)xr + m0 * d->K, wts, scales, mc, d->N, d->K, C, d->groups,
                        d->row_tiles, kmid, P, y);
     if (P) {
       const int64_t mn = mc * d->N;
-      hipLaunchKernelGGL(k_gemm_sum2, dim3((unsigned)ceil_div(ceil_div(mn, 4), 256)), dim3(256), 0,
-                         s, (const float*)P, mn, y);
+      hipLaunchKernelGGL(k_gemm_sum, dim3((unsigned)ceil_div(ceil_div(mn, 4), 256)), dim3(256), 0,
+                         s, (const float*)P, p.splits, mn, y);
     }
   }
   hipError_t e = hipGetLastError();

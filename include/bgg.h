@@ -330,13 +330,13 @@ size_t bgg_gemm_workspace_size(const bgg_weights_desc* desc, int64_t M);
  *   workspace  device, 16-byte aligned, bgg_gemm_workspace_size(desc, M)
  *              bytes: x' when BGG_ROTATE_INPUT is set; then, for PTQ1_0,
  *              the weights rewritten to PQ2_0 (the PQ2_0 trit bytes of the
- *              same shape, 256-byte rounded); then, for
- *              shapes whose output blocks fill the GPU unevenly (few output
- *              rows, long K), the fp32 partial sums of a K split in two.  A
- *              smaller workspace (down to x' only, or NULL without
- *              BGG_ROTATE_INPUT) drops the later parts in that order: the
- *              results differ in the last-bit rounding; each choice gives
- *              bit-identical y for the same inputs.
+ *              same shape, 256-byte rounded); then, for shapes whose output
+ *              blocks fill the GPU unevenly or not at all (few output rows,
+ *              long K, short prompts), the fp32 partial sums of a K split
+ *              into up to 32 ranges.  A smaller workspace (down to x' only,
+ *              or NULL without BGG_ROTATE_INPUT) drops the later parts in
+ *              that order: the results differ in the last-bit rounding;
+ *              each choice gives bit-identical y for the same inputs.
  * Errors: BGG_ERR_NULL, BGG_ERR_DESC, BGG_ERR_FORMAT (Q1_0, Q2_0_G64),
  * BGG_ERR_SHAPE, BGG_ERR_BUFFER, BGG_ERR_HIP.
  */

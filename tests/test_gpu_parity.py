@@ -536,11 +536,46 @@ def test_gemm_prefill_full_size_sampled(env, fmt, name):
 
 
 @pytest.mark.parametrize("fmt", GEMM_FMTS)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_gemm_non_finite_activations(env, fmt, rotate):
+    """NaN, +inf and -inf in one position each of three tokens' x: the prefill
+    GEMM follows IEEE arithmetic (fp16 MFMA products, fp32 sums), so those
+    rows are non-finite exactly where the oracle's fp64 rows are, NaN where
+    it has NaN and the same infinity where it has one; the other tokens keep
+    the bits of a call without the bad values.  With the transform (and its
+    workspace) PTQ1_0 runs on rewritten weights, without it on the byte-table
+    kernel."""
+    bgg, torch = env
+    M, N, K = 6, 300, 1152
+    T, S = gen_matrix(233, 1, N, K, fmt=fmt)
+    d = Dev(bgg, torch, fmt, T, S)
+    x0 = synth.activations_f16(233, 2, M, K)
+    y0 = d.gemm(x0, rotate=rotate)
+    x = x0.copy()
+    bad = {1: np.nan, 3: np.inf, 4: -np.inf}
+    for m, v in bad.items():
+        x[m, 137 * m] = v
+    y = d.gemm(x, rotate=rotate)
+    ref = oracle_y(fmt, T, S, x, rotate=rotate).astype(np.float16)
+    for m in bad:
+        assert not np.isfinite(ref[m]).all(), f"token {m}: the oracle row is finite"
+        yr, rr = y[m], ref[m]
+        assert np.array_equal(np.isnan(yr), np.isnan(rr)), f"token {m}: NaN pattern"
+        inf = np.isinf(rr)
+        assert np.array_equal(yr[inf], rr[inf]) and np.isinf(yr).sum() == inf.sum(), f"token {m}: infinities"
+        fin = np.isfinite(rr)
+        assert np.all(relerr(yr[fin][None], rr[fin][None].astype(np.float64)) <= TOL) if fin.any() else True
+    good = [i for i in range(M) if i not in bad]
+    assert np.array_equal(y[good].view(np.uint16), y0[good].view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 def test_gemm_k_split_deterministic(env, fmt):
-    """The down-shaped product (few output blocks, long K) splits K in two
-    when the workspace holds the partials: the same inputs give the same
-    bits call after call, and the split and unsplit results agree with the
-    oracle and with each other within the bar."""
+    """A product with few output blocks (25 here) splits K into ranges (10
+    here) when the workspace holds the partials: the same inputs give the
+    same bits call after call, and the split and unsplit results agree with
+    the oracle and with each other within the bar.  (The parity shapes above
+    run 1 to 32 ranges with the rotation workspace, none without.)"""
     bgg, torch = env
     M, N, K = 640, 1280, 5248
     say(f"gemm K split {fmt}")
