@@ -74,6 +74,7 @@ struct MxvArgs {
   int64_t NTl;    // tiles of this launch
   int64_t RR;     // row ranges (kWaves tiles each) of this launch
   int GS;         // PQ2_0: groups per slice; PTQ1_0: periods per slice
+  int TW;         // PTQ1_0: row tiles per workgroup (at most its waves)
   int P;          // slices
   int M;          // tokens
   int rotate;
@@ -642,7 +643,8 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 
 // ---------------------------------------------------------------------------
 // PTQ1_0, one or two tokens: k_mxv_ptq1<NW, MT>.  A workgroup of NW waves
-// takes NW 64-row tiles (one per wave) and one period of K (640 trits = 5
+// takes TW <= NW 64-row tiles (one per wave; the waves past them only help
+// with the table and the encoding) and one period of K (640 trits = 5
 // groups = 128 row bytes = 8 chunks).  After issuing its loads every wave
 // writes its share of the byte table, and the lanes of the first waves
 // encode the MT tokens' activations straight into matrix-core operands in
@@ -710,7 +712,12 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kg = lane >> 4;
   const int64_t rr = blockIdx.x % a.RR, sl = blockIdx.x / a.RR;  // row range, period
-  const int64_t lt = rr * NW + wave;
+  // waves from a.TW on take no tile: they build their share of the table
+  // and encode, then leave (the test is uniform over the wave).  Their
+  // loads stay (a branch around them would make the compiler wait for every
+  // load at its end) but read wave 0's tile, one piece per instruction
+  const bool active = wave < a.TW;
+  const int64_t lt = rr * a.TW + (active ? wave : 0);
   const int64_t tile = a.tile0 + (lt < a.NTl ? lt : a.NTl - 1);
 
   // 1. x of the blocks this thread encodes.  Wide form: pass p, block
@@ -751,11 +758,13 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
   // CU has room for them, and its table and encoding work should not wait)
   uint4 w[2][kBlocks];
   const uint4* wsrc[2];
+  // (a helper wave's lanes all read one 16-byte piece per instruction)
+  const int wkg = active ? kg : 0, wcol = active ? col : 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    int64_t c = sl * kPeriodChunks + 4 * h + kg;
+    int64_t c = sl * kPeriodChunks + 4 * h + wkg;
     c = c < a.C ? c : a.C - 1;
-    wsrc[h] = reinterpret_cast<const uint4*>(a.packed) + (tile * a.C + c) * kTile + col;
+    wsrc[h] = reinterpret_cast<const uint4*>(a.packed) + (tile * a.C + c) * kTile + wcol;
   }
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) w[0][b] = ld_stream(wsrc[0] + 16 * b);
@@ -844,6 +853,7 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
     }
   }
   __syncthreads();
+  if (!active) return;
 
   // 5. per half: four chained operations per row block and token, then lane
   //    (col, s < 3) scales its group's sums.  The operands of step k + 1 (the
@@ -987,20 +997,29 @@ K1Split k1_split(int64_t units, int64_t umax, int64_t RR, int64_t min_wgs) {
   return K1Split{ceil_div(units, GW), GW};
 }
 
-// PTQ1_0 kernel: waves (row tiles) per workgroup, the fewest from kPtqMinWaves
-// (5 for one token: the five blocks of a period are encoded in one pass; 3
-// for two) that leave at most one workgroup per CU.  A CU that holds two
-// workgroups takes them in about 1.3x the time of one and so sets the
-// launch's end (measured: gate/up 17408x5120 at one token 9.4 us with 8
-// waves = 272 workgroups on 256 CUs, 8.0 us with 9 waves = 248; at two
-// tokens 16.3 and 11.5 us; q 6144x5120 6.8 us with 4 waves, 6.6 with 5).
+// PTQ1_0 kernel: row tiles per workgroup (tw), the fewest that leave at
+// most one workgroup per CU, and waves per workgroup (nw), one per tile but
+// at least kPtqMinWaves (5 for one token: the five blocks of a period are
+// encoded in one pass; 3 for two), the waves past the tiles only helping
+// with the table and the encoding.  A CU that holds two workgroups takes
+// them in about 1.3x the time of one and so sets the launch's end
+// (measured: gate/up 17408x5120 at one token 9.4 us with 8 tiles = 272
+// workgroups on 256 CUs, 8.0 us with 9 tiles = 248; at two tokens 16.3 and
+// 11.5 us); small projections spread over more CUs with fewer tiles each.
 constexpr int kPtqMaxWaves[3] = {0, 16, 12};  // (two tokens: registers for 3 waves per SIMD)
 constexpr int kPtqMinWaves[3] = {0, 5, 3};
-int ptq1_waves(const bgg_weights_desc* d, int64_t M) {
+struct PtqPlan {
+  int nw, tw;
+};
+PtqPlan ptq1_plan(const bgg_weights_desc* d, int64_t M) {
   const int64_t P = ceil_div(d->groups, kPeriodGroups), cus = device_cus();
-  for (int nw = kPtqMinWaves[M]; nw < kPtqMaxWaves[M]; ++nw)
-    if (ceil_div(d->row_tiles, nw) * P <= cus) return nw;
-  return kPtqMaxWaves[M];
+  int tw = kPtqMaxWaves[M];
+  for (int t = 1; t < kPtqMaxWaves[M]; ++t)
+    if (ceil_div(d->row_tiles, t) * P <= cus) {
+      tw = t;
+      break;
+    }
+  return PtqPlan{std::max(tw, kPtqMinWaves[M]), tw};
 }
 
 template <int NW>
@@ -1036,7 +1055,7 @@ bool mxv_supported(const bgg_weights_desc* d, int64_t M) {
 uint64_t mxv_workspace_bytes() { return 2 * kRowWordBytes; }
 
 int mxv_kernel_name(const bgg_weights_desc* d, int64_t M, char* out, size_t cap) {
-  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv_ptq1<%d, %d>", ptq1_waves(d, M), (int)M);
+  if (d->format == BGG_FMT_PTQ1_0) return snprintf(out, cap, "k_mxv_ptq1<%d, %d>", ptq1_plan(d, M).nw, (int)M);
   if (M == 1) return snprintf(out, cap, "k_mxv1_pq2<5, %d>", mxv1_tpw(d));
   return snprintf(out, cap, "k_mxv_pq2<%d>", kPqGsMax);
 }
@@ -1057,19 +1076,21 @@ bgg_status mxv_launch(const bgg_weights_desc* d, const void* packed, const void*
   a.y = (uint16_t*)y;
   const int64_t NT = d->row_tiles;
   if (d->format == BGG_FMT_PTQ1_0) {
-    // workgroups of nw tiles x one period
-    const int nw = ptq1_waves(d, M);
-    if (nw < kPtqMinWaves[M] || nw > kPtqMaxWaves[M])  // (the rule stays within the instantiated counts)
+    // workgroups of tw tiles x one period, nw waves
+    const PtqPlan pl = ptq1_plan(d, M);
+    const int nw = pl.nw;
+    if (nw < kPtqMinWaves[M] || nw > kPtqMaxWaves[M] || pl.tw < 1 || pl.tw > nw)  // (instantiated counts)
       return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: no kernel for %d waves", nw);
-    const int64_t RRall = ceil_div(NT, nw);
+    a.TW = pl.tw;
+    const int64_t RRall = ceil_div(NT, a.TW);
     a.P = (int)ceil_div(a.G, kPeriodGroups);
     if (a.P > kMaxSlices) return fail(BGG_ERR_SHAPE, "bgg_ternary_gemv: K = %lld is too long", (long long)d->K);
     a.GS = 1;
-    const int64_t rr_per = a.P > 1 ? kRowWordRows / (nw * kTile) : RRall;
+    const int64_t rr_per = a.P > 1 ? kRowWordRows / (a.TW * kTile) : RRall;
     for (int64_t r0 = 0; r0 < RRall; r0 += rr_per) {
       a.RR = std::min(rr_per, RRall - r0);
-      a.tile0 = r0 * nw;
-      a.NTl = std::min<int64_t>(a.RR * nw, NT - a.tile0);
+      a.tile0 = r0 * a.TW;
+      a.NTl = std::min<int64_t>(a.RR * a.TW, NT - a.tile0);
       const dim3 grid((unsigned)(a.RR * a.P));
       launch_ptq1_nw<kPtqMinWaves[2]>(nw, (int)M, grid, st, a);
     }

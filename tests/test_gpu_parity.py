@@ -367,13 +367,16 @@ def test_gemv_matrix_core_every_token_count(env, fmt):
 
 @pytest.mark.parametrize("N,K,M", [(8064 - 37, 6144, 1), (12864, 6144, 1), (16064 - 5, 6144, 1),
                                    (24064 + 64, 6144, 1), (4864 - 1, 6144, 2), (9664 + 3, 6144, 2),
-                                   (17664, 6144, 2), (300, 1408, 2)])
+                                   (17664, 6144, 2), (300, 1408, 2), (1024, 5120, 1), (6144, 5120, 1),
+                                   (5120, 6144, 1), (1000, 5120, 2), (130, 640, 1)])
 def test_gemv_ptq1_waves_per_workgroup(env, N, K, M):
     """The PTQ1_0 one- and two-token kernel takes as many row tiles per
-    workgroup (one per wave) as keep one workgroup per CU, from 5 (one
-    token) or 3 (two) up to 16 or 12: these shapes select counts across that
-    range (ragged last row ranges included).  Rows of the first and the last
-    row range and a random sample match the oracle."""
+    workgroup (one per wave) as keep one workgroup per CU, up to 16 (one
+    token) or 12 (two), with at least 5 or 3 waves (the waves past the tiles
+    only help with the table and the encoding): these shapes select counts
+    across that range, small projections with fewer tiles than waves
+    (ragged last row ranges included).  Rows of the first and the last row
+    range and a random sample match the oracle."""
     bgg, torch = env
     T, S = gen_matrix(141, 2, N, K, fmt="PTQ1_0")
     d = Dev(bgg, torch, "PTQ1_0", T, S)
