@@ -33,6 +33,10 @@ Also in the same JSON line:
                 WRITE_SIZE counters when they were taken on these sources;
   achievable_hbm  a plain streaming read of 2 GiB (this project's probe
                 kernel): the rate HBM delivers to a kernel on this box;
+  launch_floor  a kernel that does no work, launched the way the step
+                launches its calls (a graph of back-to-back launches on one
+                stream): the fixed cost every launch of the step pays, and
+                that cost times the step's launches;
   decode_step   per packing: the step's rate, the kernel breakdown, the
                 shared-transform and grouped-projection variants, and the
                 small-batch sweep M = 2, 4, 8, 16;
@@ -470,6 +474,18 @@ def main() -> int:
         log(f"achievable HBM read: {hbm:.0f} GB/s")
         del big
 
+    # ------------------------------------------- fixed cost of one launch
+    def fn_empty(st):
+        for _ in range(64):
+            probe.empty(160, 512, sink, st)
+    g = capture(fn_empty)
+    floor_us = replay_us(torch, g, 7) / 64
+    del g
+    launch_floor = dict(us=round(floor_us, 3), kernel="k_probe_empty (160 x 512 threads, no work)",
+                        launches_per_step=n_calls, step_ms=round(floor_us * n_calls / 1e3, 3),
+                        share_of_step=round(floor_us * n_calls / 1e3 / ms_per_step, 4))
+    log(f"launch floor: {floor_us:.2f} us per launch, {floor_us * n_calls / 1e3:.2f} ms of the step")
+
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -482,6 +498,7 @@ def main() -> int:
                    "packed_bytes_per_step": step_bytes},
         "roofline": roofline,
         "achievable_hbm": achievable,
+        "launch_floor": launch_floor,
         "cpu_baseline": None,
         "decode_step": per_fmt,
         "context": dict(pages_end_to_end=PAGES_CONTEXT,

@@ -10,6 +10,10 @@
 //                    words) so the loads are not optimised away.
 //   bgg_probe_write  writes `bytes` (a multiple of 16) of zeros with
 //                    16-byte stores.
+//   bgg_probe_empty  launches a kernel of `grid` workgroups of `block`
+//                    threads that does no work: the fixed cost of one launch
+//                    (dispatch, the wait for the previous launch on the
+//                    stream, completion) that every kernel pays.
 // Both return 0, or the HIP error code of the launch; asynchronous on
 // `stream`.
 #include <hip/hip_runtime.h>
@@ -58,6 +62,12 @@ __global__ void __launch_bounds__(kThreads) k_probe_write(u32x4* __restrict__ ds
     __builtin_nontemporal_store(z, dst + i);
 }
 
+// never stores (no thread index reaches kThreads * 1024); the pointer keeps
+// the kernel from being an empty function body the runtime could skip
+__global__ void k_probe_empty(uint32_t* sink) {
+  if (threadIdx.x == kThreads * 1024u) sink[0] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,6 +85,12 @@ int bgg_probe_write(void* dst, size_t bytes, void* stream) {
   if (!dst || bytes % 16) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_probe_write, dim3(kBlocks), dim3(kThreads), 0, (hipStream_t)stream, (u32x4*)dst,
                      (int64_t)(bytes / 16));
+  return (int)hipGetLastError();
+}
+
+int bgg_probe_empty(unsigned grid, unsigned block, void* sink, void* stream) {
+  if (!sink || grid == 0 || block == 0 || block > 1024) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_probe_empty, dim3(grid), dim3(block), 0, (hipStream_t)stream, (uint32_t*)sink);
   return (int)hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 _lib.bgg_probe_sink_words.restype = ctypes.c_size_t
 _lib.bgg_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
 _lib.bgg_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+_lib.bgg_probe_empty.argtypes = [ctypes.c_uint, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
 
 
 def sink(device="cuda"):
@@ -38,3 +39,12 @@ def write(buf: torch.Tensor, stream=None) -> None:
     rc = _lib.bgg_probe_write(buf.data_ptr(), buf.numel() * buf.element_size(), s)
     if rc:
         raise RuntimeError(f"bgg_probe_write: HIP error {rc}")
+
+
+def empty(grid: int, block: int, sink_t: torch.Tensor, stream=None) -> None:
+    """Launch a kernel of grid x block threads that does no work."""
+    assert sink_t.is_cuda
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = _lib.bgg_probe_empty(grid, block, sink_t.data_ptr(), s)
+    if rc:
+        raise RuntimeError(f"bgg_probe_empty: HIP error {rc}")
