@@ -734,6 +734,16 @@ __global__ void __launch_bounds__(64 * W)
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// fp4 B operand of v_mfma_scale_f32_16x16x128_f8f6f4: for fp4 elements the
+// instruction reads only the first four of the eight operand registers (32
+// nibbles per lane), so the other four are left undefined instead of being
+// filled with zeros before every operation.
+__device__ __forceinline__ i32x8 fp4_b(int r0, int r1, int r2, int r3) {
+  const i32x4 v = {r0, r1, r2, r3};
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
 
 constexpr int kMmaSlots = 16;      // token slots of the A operand
 constexpr int kMmaRedStride = 68;  // floats per token row in LDS (64 rows + 4: no bank conflicts)
@@ -771,8 +781,8 @@ __device__ __forceinline__ void mx_group(const i32x8 (&A)[kMxDigits], uint32_t s
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const uint32_t lo = wv[rb].x, hi = wv[rb].y;
-    B[rb] = i32x8{(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                  (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+    B[rb] = fp4_b((int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                  (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u));
     ag[rb] = c0;
   }
 #pragma unroll
@@ -809,8 +819,8 @@ __device__ __forceinline__ void mx_group_q1(const i32x8 (&A)[kMxDigits], uint32_
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const uint32_t w = wv[rb];
-    B[rb] = i32x8{(int)q1_spread8(w & 0xFFu), (int)q1_spread8((w >> 8) & 0xFFu),
-                  (int)q1_spread8((w >> 16) & 0xFFu), (int)q1_spread8(w >> 24), 0, 0, 0, 0};
+    B[rb] = fp4_b((int)q1_spread8(w & 0xFFu), (int)q1_spread8((w >> 8) & 0xFFu),
+                  (int)q1_spread8((w >> 16) & 0xFFu), (int)q1_spread8(w >> 24));
     ag[rb] = c0;
   }
 #pragma unroll
@@ -843,8 +853,8 @@ __device__ __forceinline__ void mx_group_g64(const i32x8 (&A)[kMxDigits], uint32
     for (int rb = 0; rb < 4; ++rb) {
       // (the other half's lanes feed nibble 0, the value 0)
       const uint32_t lo = mine ? wv[rb].x : 0u, hi = mine ? wv[rb].y : 0u;
-      B[rb] = i32x8{(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                    (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
+      B[rb] = fp4_b((int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                  (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u));
       ag[rb] = c0[h];
     }
 #pragma unroll

@@ -60,6 +60,24 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// fp4 B operand of v_mfma_scale_f32_16x16x128_f8f6f4: for fp4 elements the
+// instruction reads only the first four of the eight operand registers (32
+// nibbles per lane), so the other four are left undefined instead of being
+// filled with zeros before every operation.
+__device__ __forceinline__ i32x8 fp4_b(int r0, int r1, int r2, int r3) {
+  const i32x4 v = {r0, r1, r2, r3};
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// A constant in one VGPR for the whole kernel: the block-scale operands of
+// the matrix operations are VGPRs, and a literal there would be moved into
+// a register again before every operation.
+__device__ __forceinline__ int vgpr_const(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
 constexpr int kWaves = 8;       // waves per workgroup, one 64-row tile each
 constexpr int kBlocks = 4;      // 16-row blocks per tile
 constexpr int kPqGsMax = 8;     // PQ2_0: groups per slice (compile-time bound)
@@ -386,6 +404,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
   // 6. one MFMA per group and row block, the four of a group issued together
   float acc[kBlocks] = {0.0f, 0.0f, 0.0f, 0.0f};
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int bsc = vgpr_const(128);  // B scale 2: codes c/2 -> c
 #pragma unroll
   for (int g = 0; g < GSMAX; ++g) {
     if (g < ng) {
@@ -412,9 +431,9 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
         const uint32_t lo = cw[b][0], hi = cw[b][1];
-        const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                         (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
-        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 128);
+        const i32x8 B = fp4_b((int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                               (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u));
+        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, bsc);
       }
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b)
@@ -538,7 +557,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   if (TPW == 1) scales_to_lds();
   wave_lds_sync();
-  // 4. MFMAs: A lanes of rows 0-2 read their digits, the rest are zero.
+  // 4. MFMAs: A lanes of rows 0-2 read their digits.
   //    The second half of the codes is issued in the first iterations, one
   //    group per iteration ahead of that iteration's matrix operations: a
   //    wave that queues loads waits until the CU has room for them, and the
@@ -549,7 +568,8 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) acc[t][b] = 0.0f;
   const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int arow = lane & 15;
+  const int arow3 = (lane & 15) < 3 ? (lane & 15) : 0;
+  const int bsc = vgpr_const(128);  // B scale 2: codes c/2 -> c
 #pragma unroll
   for (int g = 0; g < GPW; ++g) {
     if (kHalf + g < GPW) {
@@ -565,14 +585,11 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (g < ng) {
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-      int sa = 127;
-      if (arow < 3) {
-        const uint4* ap = reinterpret_cast<const uint4*>(sA[wave][g] + arow * 128 + kg * 32);
-        a0 = ap[0];
-        a1 = ap[1];
-        sa = sSc[wave][g][arow];
-      }
+      // (A rows 3-15 feed only output rows that are dropped: their lanes
+      // read digit row 0 again, with no branch and no zero fill)
+      const uint4* ap = reinterpret_cast<const uint4*>(sA[wave][g] + arow3 * 128 + kg * 32);
+      const uint4 a0 = ap[0], a1 = ap[1];
+      const int sa = sSc[wave][g][arow3];
       const i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       const float corr = sCorr[wave][g];
@@ -597,9 +614,9 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv1_pq2(MxvArgs a) {
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
           const uint32_t lo = cw[b][0], hi = cw[b][1];
-          const i32x8 B = {(int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
-                           (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u), 0, 0, 0, 0};
-          D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, 128);
+          const i32x8 B = fp4_b((int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
+                               (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u));
+          D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, bsc);
         }
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
@@ -866,6 +883,7 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) acc[m][b] = 0.0f;
   {
+    const int bsc = vgpr_const(127);  // B scale 1
     const int arow = lane & 15, as = arow >> 2, ad = arow & 3;
     const bool aon = as < 3 && ad < 3;
     const int aq = aon ? 3 * ad + as : 9, rot = aon ? aq : (arow < 8 ? 2 : 1);
@@ -912,11 +930,11 @@ __global__ void __launch_bounds__(64 * NW) k_mxv_ptq1(MxvArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b) {
-        const i32x8 Bv = {B[cur][b][0], B[cur][b][1], B[cur][b][2], B[cur][b][3], 0, 0, 0, 0};
+        const i32x8 Bv = fp4_b(B[cur][b][0], B[cur][b][1], B[cur][b][2], B[cur][b][3]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const f32x4 C = u == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : D[m][b];
-          D[m][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[cur][m], Bv, C, 0, 4, 0, sa[m][h], 0, 127);
+          D[m][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[cur][m], Bv, C, 0, 4, 0, sa[m][h], 0, bsc);
         }
       }
       if (k == 3) {
