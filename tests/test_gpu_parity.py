@@ -539,6 +539,28 @@ def test_gemm_prefill_full_size_sampled(env, fmt, name):
 
 
 @pytest.mark.parametrize("fmt", GEMM_FMTS)
+@pytest.mark.parametrize("K", [1024, 1152])
+def test_gemm_two_k_ranges(env, fmt, K):
+    """520 output blocks (M = 13312, N = 1280) fill the 512 workgroup slots
+    unevenly, so K is cut in two ranges over two workgroups with fp32
+    partials in the workspace, for an even (K = 1024) and an odd (K = 1152)
+    number of 128-wide K steps.  Sampled token rows match the oracle over
+    all N outputs, and a second call gives the same bits."""
+    bgg, torch = env
+    M, N = 13312, 1280
+    say(f"gemm two K ranges {fmt} M={M} N={N} K={K}")
+    T, S = gen_matrix(131, 4, N, K)
+    d = Dev(bgg, torch, fmt, T, S)
+    x = synth.activations_f16(131, 5, M, K)
+    y = d.gemm(x)
+    assert not np.isnan(y).any()
+    assert np.array_equal(d.gemm(x).view(np.uint16), y.view(np.uint16))
+    rows = np.array([0, 1, 127, 128, 4095, 4096, 6655, 6656, 9000, 13183, 13184, 13311])
+    ref = oracle.matvec(T, S, oracle.rotate(x[rows]))
+    assert np.all(relerr(y[rows], ref) <= TOL)
+
+
+@pytest.mark.parametrize("fmt", GEMM_FMTS)
 @pytest.mark.parametrize("rotate", [True, False])
 def test_gemm_non_finite_activations(env, fmt, rotate):
     """NaN, +inf and -inf in one position each of three tokens' x: the prefill
