@@ -214,7 +214,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // The three values an fp16 scale s gives a PQ2_0 code c = t + 1, as a
 // byte-select table for v_perm_b32: `lo` holds the low byte of the value of
-// code c in byte c, `hi` its high byte in byte c (read as selector c + 4).
+// code c in byte c, `hi` its high byte in byte c.
 // Code 0 is -s (s with the sign bit flipped), code 1 is 0, code 2 is +s;
 // code 3, which no valid buffer holds, reads 0 like code 1.
 struct Pq2Table {
@@ -230,19 +230,21 @@ __device__ __forceinline__ Pq2Table pq2_table(uint32_t sbits) {
 // (s*t_0, ..., s*t_7), bit for bit the value s*t (+-s or 0) -- no
 // arithmetic, only byte moves.  t | t << 14 puts codes 0, 4 in bytes 0, 1
 // and codes 1, 5 in bytes 2, 3 (two-bit fields at the byte starts); shifted
-// down by four the same holds for codes 2, 6, 3, 7.  A first byte permute
-// turns the two codes of one output word into the selector (c_a, c_a + 4,
-// c_b, c_b + 4), a second one reads the table with it.
+// down by four the same holds for codes 2, 6, 3, 7.  Those four codes, used
+// as byte selectors as they are, read the low bytes of their values from
+// the table's `lo` word and the high bytes from its `hi` word (one byte
+// permute each); a third permute pairs each low byte with its high byte.
 __device__ __forceinline__ f16x8 decode8_pq2(uint32_t word, uint32_t shift, Pq2Table tb) {
   const uint32_t t = __builtin_amdgcn_ubfe(word, shift, 16);
   const uint32_t z = t | (t << 14);
-  const uint32_t ab = z & 0x03030303u, cd = (z >> 4) & 0x03030303u;
-  const uint32_t ab4 = ab | 0x04040404u, cd4 = cd | 0x04040404u;
+  const uint32_t ab = z & 0x03030303u, cd = (z >> 4) & 0x03030303u;  // codes (0, 4, 1, 5), (2, 6, 3, 7)
+  const uint32_t lab = __builtin_amdgcn_perm(0u, tb.lo, ab), hab = __builtin_amdgcn_perm(0u, tb.hi, ab);
+  const uint32_t lcd = __builtin_amdgcn_perm(0u, tb.lo, cd), hcd = __builtin_amdgcn_perm(0u, tb.hi, cd);
   uint32_t out[4];
-  out[0] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(ab4, ab, 0x06020400u));
-  out[1] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(cd4, cd, 0x06020400u));
-  out[2] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(ab4, ab, 0x07030501u));
-  out[3] = __builtin_amdgcn_perm(tb.hi, tb.lo, __builtin_amdgcn_perm(cd4, cd, 0x07030501u));
+  out[0] = __builtin_amdgcn_perm(hab, lab, 0x06020400u);  // values of codes 0, 1
+  out[1] = __builtin_amdgcn_perm(hcd, lcd, 0x06020400u);  // 2, 3
+  out[2] = __builtin_amdgcn_perm(hab, lab, 0x07030501u);  // 4, 5
+  out[3] = __builtin_amdgcn_perm(hcd, lcd, 0x07030501u);  // 6, 7
   f16x8 r;
   __builtin_memcpy(&r, out, sizeof(r));
   return r;
