@@ -236,7 +236,8 @@ __device__ __forceinline__ Pq2Table pq2_table(uint32_t sbits) {
 // permute each); a third permute pairs each low byte with its high byte.
 __device__ __forceinline__ f16x8 decode8_pq2(uint32_t word, uint32_t shift, Pq2Table tb) {
   const uint32_t t = __builtin_amdgcn_ubfe(word, shift, 16);
-  const uint32_t z = t | (t << 14);
+  uint32_t z;  // t | t << 14 in one instruction
+  asm("v_lshl_or_b32 %0, %1, 14, %1" : "=v"(z) : "v"(t));
   const uint32_t ab = z & 0x03030303u, cd = (z >> 4) & 0x03030303u;  // codes (0, 4, 1, 5), (2, 6, 3, 7)
   const uint32_t lab = __builtin_amdgcn_perm(0u, tb.lo, ab), hab = __builtin_amdgcn_perm(0u, tb.hi, ab);
   const uint32_t lcd = __builtin_amdgcn_perm(0u, tb.lo, cd), hcd = __builtin_amdgcn_perm(0u, tb.hi, cd);

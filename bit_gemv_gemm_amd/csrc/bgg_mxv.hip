@@ -403,7 +403,6 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
 
   // 6. one MFMA per group and row block, the four of a group issued together
   float acc[kBlocks] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const int bsc = vgpr_const(128);  // B scale 2: codes c/2 -> c
 #pragma unroll
   for (int g = 0; g < GSMAX; ++g) {
@@ -413,7 +412,9 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
       const i32x8 A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       const int sa = sSc[g][lane];
-      const float corr = sCorr[g][kg];
+      // digit row 2 of the lane's token starts at -2^(e-14) sum q (an exact
+      // integer multiple of 2^(e-14), as every partial sum is)
+      const f32x4 cz = {0.0f, 0.0f, -sCorr[g][kg], 0.0f};
       // block 2 p: bytes 0-7 of the chunk on lanes kg = 0, 2, bytes 8-15 on
       // kg = 1, 3; block 2 p + 1 likewise (v_permlane16_swap: odd 16-lane
       // rows of the first operand with even rows of the second)
@@ -433,11 +434,11 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
         const uint32_t lo = cw[b][0], hi = cw[b][1];
         const i32x8 B = fp4_b((int)(lo & 0x33333333u), (int)((lo >> 2) & 0x33333333u),
                                (int)(hi & 0x33333333u), (int)((hi >> 2) & 0x33333333u));
-        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, zero, 0, 4, 0, sa, 0, bsc);
+        D[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, cz, 0, 4, 0, sa, 0, bsc);
       }
 #pragma unroll
       for (int b = 0; b < kBlocks; ++b)
-        acc[b] = fmaf(h2f(sS[wave][g * kTile + 16 * b + col]), (D[b][0] + D[b][1]) + (D[b][2] - corr), acc[b]);
+        acc[b] = fmaf(h2f(sS[wave][g * kTile + 16 * b + col]), (D[b][0] + D[b][1]) + D[b][2], acc[b]);
     }
   }
 
