@@ -34,7 +34,9 @@
 //     an exact e4m3 value;
 //   * one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 weight rows and group:
 //     A (fp8, 16 rows) = four row quads, each quad (d0, d1, d2, 0) of one
-//     token, with A's E8M0 block scale 2^(e-14+10-5k) on digit k; B (fp4, 16
+//     token (rows whose outputs are dropped may hold anything: the
+//     one-token kernel repeats digit row 0 there), with A's E8M0 block
+//     scale 2^(e-14+10-5k) on digit k; B (fp4, 16
 //     columns) = the codes c = t + 1 of 16 weight rows as nibbles (value
 //     c/2, B scale 2);
 //   * output lane (quad G, row j) adds its quad's three digit rows: every
@@ -453,7 +455,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_mxv_pq2(MxvArgs a) {
 // K range of GW groups; its 8 waves split that range (GPW groups each) and
 // cover all TPW tiles, so no wave shares activations with another: wave w
 // encodes its own groups (four per pass, 16 lanes each; only A rows 0-2,
-// the three digits, are non-zero, so its LDS keeps just those) in the middle
+// the three digits, feed kept outputs, so its LDS keeps just those) in the middle
 // of issuing its weight loads, and the waves meet only for the final
 // fixed-order reduction in LDS.  With one K range per row range there is no
 // row word at all; else the ranges are added through the row words.
